@@ -1,0 +1,163 @@
+"""CPU oracle for GGUF Q8_0 / Q4_K dequant, matvec and small matmul.
+
+TEST INFRASTRUCTURE ONLY. This package defines the values the GPU library
+must reproduce. Only the test-suite, the smoke check and the CPU-baseline leg
+of ``bench.py`` may import it; the product path never does. It shares no
+code with ``gguf_block_quant_gq_amd``.
+
+The arithmetic lives in ``gq_oracle.c`` (plain C, ``-O2 -ffp-contract=off``):
+hand-decoded fp16, block unpack, fp32 dequant ``(d*sc)*q - dmin*m`` (Q4_K) or
+``d*q`` (Q8_0), and f64-accumulated sums. The page and section each step
+follows are cited in that file.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gq_oracle.c")
+_LIB = os.path.join(_HERE, "libgq_oracle.so")
+
+TYPE_Q8_0 = 8
+TYPE_Q4_K = 12
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC,
+           "-lm", "-lpthread"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.gqo_row_bytes.argtypes = [i32, i64]
+    lib.gqo_row_bytes.restype = i64
+    lib.gqo_f16_to_f32_n.argtypes = [vp, i64, vp]
+    lib.gqo_f16_to_f32_n.restype = None
+    lib.gqo_f32_to_f16_rne.argtypes = [ctypes.c_float]
+    lib.gqo_f32_to_f16_rne.restype = ctypes.c_uint16
+    lib.gqo_q4_k_unpack_scales.argtypes = [vp, vp, vp]
+    lib.gqo_q4_k_unpack_scales.restype = None
+    lib.gqo_dequant.argtypes = [i32, vp, i64, i64, vp]
+    lib.gqo_dequant.restype = i32
+    lib.gqo_matvec.argtypes = [i32, vp, i64, i64, vp, vp, vp, i32]
+    lib.gqo_matvec.restype = i32
+    lib.gqo_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp, i32]
+    lib.gqo_matmul.restype = i32
+    lib.gqo_quantize_q8_0.argtypes = [vp, i64, i64, vp]
+    lib.gqo_quantize_q8_0.restype = i32
+    lib.gqo_quantize_q4_k.argtypes = [vp, i64, i64, vp]
+    lib.gqo_quantize_q4_k.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise ValueError(f"oracle {what} failed with status {status}")
+
+
+def _as_bytes(W) -> np.ndarray:
+    W = np.ascontiguousarray(W)
+    if W.dtype != np.uint8:
+        W = W.view(np.uint8)
+    return W.reshape(-1)
+
+
+def row_bytes(fmt: int, cols: int) -> int:
+    return int(_load().gqo_row_bytes(fmt, cols))
+
+
+def f16_to_f32(h) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16).reshape(-1)
+    out = np.empty(h.shape, np.float32)
+    _load().gqo_f16_to_f32_n(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+def f32_to_f16_rne(f: float) -> int:
+    return int(_load().gqo_f32_to_f16_rne(float(f)))
+
+
+def q4_k_unpack_scales(s12) -> tuple[np.ndarray, np.ndarray]:
+    s = np.ascontiguousarray(s12, dtype=np.uint8).reshape(12)
+    sc = np.empty(8, np.uint8)
+    m = np.empty(8, np.uint8)
+    _load().gqo_q4_k_unpack_scales(_ptr(s), _ptr(sc), _ptr(m))
+    return sc, m
+
+
+def dequant(fmt: int, W, rows: int, cols: int) -> np.ndarray:
+    Wb = _as_bytes(W)
+    if Wb.size < rows * row_bytes(fmt, cols):
+        raise ValueError("W holds fewer bytes than rows * row_bytes")
+    out = np.empty((rows, cols), np.float32)
+    _check(_load().gqo_dequant(fmt, _ptr(Wb), rows, cols, _ptr(out)), "dequant")
+    return out
+
+
+def matmul(fmt: int, W, rows: int, cols: int, X, nthreads: int = 1):
+    """Y[m, r] = sum_c w(r,c) X[m,c] in f64, and S[m, r] = sum_c |w X|."""
+    Wb = _as_bytes(W)
+    if Wb.size < rows * row_bytes(fmt, cols):
+        raise ValueError("W holds fewer bytes than rows * row_bytes")
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    X2 = X.reshape(-1, cols)
+    M = X2.shape[0]
+    Y = np.empty((M, rows), np.float64)
+    S = np.empty((M, rows), np.float64)
+    _check(_load().gqo_matmul(fmt, _ptr(Wb), rows, cols, _ptr(X2), M,
+                              _ptr(Y), _ptr(S), int(nthreads)), "matmul")
+    return Y, S
+
+
+def matvec(fmt: int, W, rows: int, cols: int, x, nthreads: int = 1):
+    """y[r] = sum_c w(r,c) x[c] in f64, and S[r] = sum_c |w x|."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(cols)
+    Y, S = matmul(fmt, W, rows, cols, x.reshape(1, cols), nthreads)
+    return Y[0], S[0]
+
+
+def select_rows(fmt: int, W, cols: int, row_idx) -> np.ndarray:
+    """The packed bytes of the given rows, as a new contiguous matrix."""
+    Wb = _as_bytes(W)
+    rb = row_bytes(fmt, cols)
+    idx = np.asarray(row_idx, dtype=np.int64)
+    return Wb.reshape(-1, rb)[idx].reshape(-1) if Wb.size % rb == 0 else \
+        np.concatenate([Wb[i * rb:(i + 1) * rb] for i in idx])
+
+
+def quantize(fmt: int, w) -> np.ndarray:
+    """Test-only reference quantiser: fp32 [rows, cols] -> packed bytes."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim == 1:
+        w = w.reshape(1, -1)
+    rows, cols = w.shape
+    out = np.zeros(rows * row_bytes(fmt, cols), np.uint8)
+    fn = _load().gqo_quantize_q8_0 if fmt == TYPE_Q8_0 else _load().gqo_quantize_q4_k
+    if fmt not in (TYPE_Q8_0, TYPE_Q4_K):
+        raise ValueError(f"unknown type {fmt}")
+    _check(fn(_ptr(w), rows, cols, _ptr(out)), "quantize")
+    return out
