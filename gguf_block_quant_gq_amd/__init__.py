@@ -1,0 +1,163 @@
+"""Python binding of libgq, the MI355X (gfx950) block-quantised GEMV/GEMM library.
+
+The functions mirror the C ABI in ``include/gq.h`` one for one and only
+marshal arguments: torch tensors are used for device memory and streams, and
+every step of the computation runs in the HIP kernels of ``libgq.so``. There
+is no CPU fallback: if the library is not built, loading raises.
+
+    gq_dequant(fmt, W, rows, cols, out=None)           -> out [rows, cols] fp32
+    gq_matvec(fmt, W, rows, cols, x, y=None)           -> y [rows] fp32
+    gq_matmul(fmt, W, rows, cols, X, Y=None)           -> Y [M, rows] fp32
+
+W is a uint8 CUDA tensor holding rows * gq_row_bytes(fmt, cols) bytes of
+GGUF blocks; fmt is FMT_Q8_0 (8) or FMT_Q4_K (12).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgq.so")
+
+FMT_Q8_0 = 8
+FMT_Q4_K = 12
+
+GQ_OK = 0
+GQ_ERR_NULL = 1
+GQ_ERR_FMT = 2
+GQ_ERR_SHAPE = 3
+GQ_ERR_ALIGN = 4
+GQ_ERR_DEVICE = 5
+GQ_ERR_OVERLAP = 6
+
+EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matmul")
+
+_lib = None
+
+
+class GQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+
+
+def load_library():
+    """Load libgq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(or python gguf_block_quant_gq_amd/_build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.gq_row_bytes.argtypes = [i32, i64]
+    lib.gq_row_bytes.restype = i64
+    lib.gq_status_str.argtypes = [i32]
+    lib.gq_status_str.restype = ctypes.c_char_p
+    lib.gq_dequant.argtypes = [i32, vp, i64, i64, vp]
+    lib.gq_dequant.restype = i32
+    lib.gq_matvec.argtypes = [i32, vp, i64, i64, vp, vp, vp]
+    lib.gq_matvec.restype = i32
+    lib.gq_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
+    lib.gq_matmul.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().gq_status_str(int(status)).decode()
+
+
+def gq_row_bytes(fmt: int, cols: int) -> int:
+    return int(load_library().gq_row_bytes(int(fmt), int(cols)))
+
+
+# ------------------------------------------------------------ marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr())
+
+
+def _check_dev(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _check_w(fmt, W, rows, cols):
+    _check_dev(W, "W")
+    need = rows * gq_row_bytes(fmt, cols) if gq_row_bytes(fmt, cols) >= 0 else 0
+    if W.numel() * W.element_size() < need:
+        raise ValueError(f"W holds {W.numel() * W.element_size()} bytes, needs {need}")
+
+
+def _stream_handle(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def gq_dequant(fmt: int, W, rows: int, cols: int, out=None):
+    """Bit-exact fp32 expansion of W (blocks until done, null stream)."""
+    torch = _torch()
+    _check_w(fmt, W, rows, cols)
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=W.device)
+    _check_dev(out, "out", torch.float32)
+    if out.numel() < rows * cols:
+        raise ValueError("out is too small")
+    st = load_library().gq_dequant(int(fmt), _ptr(W), int(rows), int(cols), _ptr(out))
+    if st != GQ_OK:
+        raise GQError(st, "gq_dequant")
+    return out
+
+
+def gq_matvec(fmt: int, W, rows: int, cols: int, x, y=None, stream=None):
+    """y = W x on `stream` (default: torch's current stream), asynchronous."""
+    torch = _torch()
+    _check_w(fmt, W, rows, cols)
+    _check_dev(x, "x", torch.float32)
+    if x.numel() < cols:
+        raise ValueError("x is too small")
+    if y is None:
+        y = torch.empty(rows, dtype=torch.float32, device=W.device)
+    _check_dev(y, "y", torch.float32)
+    if y.numel() < rows:
+        raise ValueError("y is too small")
+    st = load_library().gq_matvec(int(fmt), _ptr(W), int(rows), int(cols), _ptr(x), _ptr(y),
+                                  _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_matvec")
+    return y
+
+
+def gq_matmul(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):
+    """Y[M, rows] = X[M, cols] W^T on `stream`, asynchronous."""
+    torch = _torch()
+    _check_w(fmt, W, rows, cols)
+    _check_dev(X, "X", torch.float32)
+    if X.numel() % cols != 0:
+        raise ValueError("X must hold M * cols floats")
+    M = X.numel() // cols
+    if Y is None:
+        Y = torch.empty((M, rows), dtype=torch.float32, device=W.device)
+    _check_dev(Y, "Y", torch.float32)
+    if Y.numel() < M * rows:
+        raise ValueError("Y is too small")
+    st = load_library().gq_matmul(int(fmt), _ptr(W), int(rows), int(cols), _ptr(X), int(M),
+                                  _ptr(Y), _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_matmul")
+    return Y

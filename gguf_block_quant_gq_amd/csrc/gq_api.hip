@@ -1,0 +1,143 @@
+// gq_api.hip -- the extern "C" entry points of libgq (declared in gq.h):
+// argument validation on the host, kernel choice, launch.
+//
+// The dispatch mirrors the quantised matvec dispatch of "nurllama 0.18.1
+// API" (kernels.nu section): the ggml tensor type picks the kernel, and a
+// type without a kernel is reported to the caller (GQ_ERR_FMT) so that it
+// can fall back. Every check runs before the first HIP call.
+#include <atomic>
+#include <climits>
+#include <cstdint>
+
+#include "../../include/gq.h"
+#include "gq_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // 0 = not yet queried
+
+// Compute units of the current device (cached per device).
+int current_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev >= kMaxDevices) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    return n;
+  }
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return -1;
+  g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+int units_per_row(int fmt, int64_t cols) {
+  if (fmt == gq::kFmtQ8_0) return (int)((cols + 31) / 32);
+  return (int)(8 * ((cols + 255) / 256));
+}
+
+// Shape and format checks shared by every entry point. On success *rb is
+// the row stride in bytes and *wbytes the size of W.
+int check_shape(int fmt, int64_t rows, int64_t cols, int64_t M, int64_t* rb, int64_t* wbytes) {
+  if (fmt != GQ_FMT_Q8_0 && fmt != GQ_FMT_Q4_K) return GQ_ERR_FMT;
+  if (rows < 0 || cols <= 0 || M < 0) return GQ_ERR_SHAPE;
+  if (rows > INT_MAX || cols > INT_MAX || M > INT_MAX) return GQ_ERR_SHAPE;
+  *rb = gq_row_bytes(fmt, cols);
+  if (*rb <= 0) return GQ_ERR_SHAPE;
+  if (rows > 0 && *rb > INT64_MAX / rows) return GQ_ERR_SHAPE;
+  *wbytes = rows * *rb;
+  return GQ_OK;
+}
+
+int check_align(int fmt, const void* W) {
+  uintptr_t need = fmt == GQ_FMT_Q8_0 ? 2 : 4;
+  return ((uintptr_t)W % need) ? GQ_ERR_ALIGN : GQ_OK;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" int64_t gq_row_bytes(int fmt, int64_t cols) {
+  if (cols < 0 || cols > INT64_MAX - 256) return -1;
+  if (fmt == GQ_FMT_Q8_0) return ((cols + 31) / 32) * 34;
+  if (fmt == GQ_FMT_Q4_K) return ((cols + 255) / 256) * 144;
+  return -1;
+}
+
+extern "C" const char* gq_status_str(int status) {
+  switch (status) {
+    case GQ_OK: return "GQ_OK";
+    case GQ_ERR_NULL: return "GQ_ERR_NULL: a required pointer is NULL";
+    case GQ_ERR_FMT: return "GQ_ERR_FMT: unsupported block format";
+    case GQ_ERR_SHAPE: return "GQ_ERR_SHAPE: bad or overflowing rows/cols/M";
+    case GQ_ERR_ALIGN: return "GQ_ERR_ALIGN: misaligned pointer";
+    case GQ_ERR_DEVICE: return "GQ_ERR_DEVICE: HIP runtime error";
+    case GQ_ERR_OVERLAP: return "GQ_ERR_OVERLAP: output overlaps an input";
+    default: return "unknown gq status";
+  }
+}
+
+extern "C" int gq_dequant(int fmt, const void* W, int64_t rows, int64_t cols, float* out) {
+  int64_t rb = 0, wbytes = 0;
+  int st = check_shape(fmt, rows, cols, 0, &rb, &wbytes);
+  if (st != GQ_OK) return st;
+  if (rows > INT64_MAX / 4 / cols) return GQ_ERR_SHAPE;
+  if (rows == 0) return GQ_OK;
+  if (!W || !out) return GQ_ERR_NULL;
+  if ((st = check_align(fmt, W)) != GQ_OK) return st;
+  if ((uintptr_t)out % 4) return GQ_ERR_ALIGN;
+  if (overlaps(out, rows * cols * 4, W, wbytes)) return GQ_ERR_OVERLAP;
+
+  (void)hipGetLastError();  // start from a clean error state
+  gq::DequantArgs a{(const uint8_t*)W, out, rb, rows, (int)cols, units_per_row(fmt, cols)};
+  hipError_t e = gq::launch_dequant(fmt, a, 0);
+  if (e != hipSuccess) return GQ_ERR_DEVICE;
+  return finish(hipStreamSynchronize(0));
+}
+
+extern "C" int gq_matvec(int fmt, const void* W, int64_t rows, int64_t cols, const float* x,
+                         float* y, void* stream) {
+  int64_t rb = 0, wbytes = 0;
+  int st = check_shape(fmt, rows, cols, 1, &rb, &wbytes);
+  if (st != GQ_OK) return st;
+  if (rows == 0) return GQ_OK;
+  if (!W || !x || !y) return GQ_ERR_NULL;
+  if ((st = check_align(fmt, W)) != GQ_OK) return st;
+  if ((uintptr_t)x % 4 || (uintptr_t)y % 4) return GQ_ERR_ALIGN;
+  if (overlaps(y, rows * 4, W, wbytes) || overlaps(y, rows * 4, x, cols * 4)) return GQ_ERR_OVERLAP;
+
+  const int cus = current_cus();
+  if (cus <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  gq::GemvArgs a{(const uint8_t*)W, x, y, rb, (int)rows, (int)cols, units_per_row(fmt, cols)};
+  return finish(gq::launch_gemv(fmt, a, cus * 8, (hipStream_t)stream));
+}
+
+extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,
+                         int64_t M, float* Y, void* stream) {
+  int64_t rb = 0, wbytes = 0;
+  int st = check_shape(fmt, rows, cols, M, &rb, &wbytes);
+  if (st != GQ_OK) return st;
+  if (M > 0 && (rows > INT64_MAX / 4 / M || cols > INT64_MAX / 4 / M)) return GQ_ERR_SHAPE;
+  if (rows == 0 || M == 0) return GQ_OK;
+  if (!W || !X || !Y) return GQ_ERR_NULL;
+  if ((st = check_align(fmt, W)) != GQ_OK) return st;
+  if ((uintptr_t)X % 4 || (uintptr_t)Y % 4) return GQ_ERR_ALIGN;
+  if (overlaps(Y, M * rows * 4, W, wbytes) || overlaps(Y, M * rows * 4, X, M * cols * 4))
+    return GQ_ERR_OVERLAP;
+
+  const int cus = current_cus();
+  if (cus <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, (int)M, units_per_row(fmt, cols)};
+  return finish(gq::launch_gemm_small(fmt, a, cus * 8, (hipStream_t)stream));
+}

@@ -1,0 +1,49 @@
+// gq_internal.h -- host-side launch interface between the C ABI (gq_api.hip)
+// and the kernel files. Not installed; the public interface is include/gq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gq {
+
+constexpr int kFmtQ8_0 = 8;
+constexpr int kFmtQ4_K = 12;
+
+struct GemvArgs {
+  const uint8_t* W;
+  const float* x;
+  float* y;
+  int64_t row_bytes;
+  int rows;
+  int cols;
+  int units;  // per row: Q8_0 blocks, or Q4_K 16-byte code chunks (8 per block)
+};
+
+struct DequantArgs {
+  const uint8_t* W;
+  float* out;
+  int64_t row_bytes;
+  int64_t rows;
+  int cols;
+  int units;  // as in GemvArgs
+};
+
+struct GemmArgs {
+  const uint8_t* W;
+  const float* X;
+  float* Y;
+  int64_t row_bytes;
+  int rows;
+  int cols;
+  int M;
+  int units;
+};
+
+// All launchers enqueue on `s` and return the launch status.
+hipError_t launch_dequant(int fmt, const DequantArgs& a, hipStream_t s);
+hipError_t launch_gemv(int fmt, const GemvArgs& a, int max_blocks, hipStream_t s);
+hipError_t launch_gemm_small(int fmt, const GemmArgs& a, int max_blocks, hipStream_t s);
+hipError_t launch_gemm_mfma(int fmt, const GemmArgs& a, int num_cus, hipStream_t s);
+
+}  // namespace gq

@@ -1,0 +1,118 @@
+/*
+ * gq.h -- C ABI of libgq: block-quantised (GGUF Q8_0 / Q4_K) weight matrices
+ * times fp32 activations on an AMD MI355X (gfx950), dequantised on the fly.
+ *
+ * The operation: a weight matrix W[out, in] stored row-major as GGUF blocks,
+ * each row a whole number of blocks, multiplied by fp32 activations
+ * ("nurllama 0.18.1 API", kernels.nu section, layout contract
+ * y[r] = sum_c W[r*in + c] * x[c]; model.nu section: weights stay quantised
+ * on the device and each block is decoded inside the matmul; the prompt is
+ * processed in chunks so each weight is read once per chunk).
+ *
+ * Shapes and layout
+ *   rows = output features, cols = input features.
+ *   A row holds ceil(cols / QK) blocks: gq_row_bytes(fmt, cols) bytes.
+ *   W holds rows * gq_row_bytes(fmt, cols) bytes in GGUF block order, exactly
+ *   as found in the file. Codes at columns >= cols in a row's last block are
+ *   ignored (GGUF itself only stores whole blocks, so this only matters for
+ *   cols that are not a multiple of QK).
+ *   Q8_0 (fmt 8):  34 B per 32 weights: fp16 d, then 32 int8 q; w = d*q.
+ *   Q4_K (fmt 12): 144 B per 256 weights: fp16 d, fp16 dmin, 12 bytes of
+ *     packed 6-bit scale/min codes (sc_j, m_j, j < 8), 128 bytes of 4-bit
+ *     codes; weight 64g+32h+l takes nibble h of code byte 32g+l and belongs
+ *     to sub-block j = 2g+h; w = (d*sc_j)*code - dmin*m_j.
+ *
+ * Ownership and threading
+ *   All pointers are device pointers owned by the caller. The library never
+ *   allocates, frees or keeps a pointer and needs no workspace. Its only
+ *   global state is a per-device cache of device properties, filled once.
+ *   Calls on different streams may run concurrently.
+ *
+ * Alignment
+ *   Q8_0 W: 2-byte aligned (a row range of a Q8_0 tensor starts on any
+ *   34-byte block boundary). Q4_K W: 4-byte aligned. x, y, X, Y, out: 4-byte
+ *   aligned. An output that overlaps an input is rejected (GQ_ERR_OVERLAP).
+ *
+ * Errors
+ *   Every entry point returns a gq_status. Arguments are validated on the
+ *   host before any HIP call, so a bad argument never reaches the GPU.
+ *   rows == 0 (or M == 0) is an empty product: GQ_OK, nothing is written.
+ *   An unsupported fmt returns GQ_ERR_FMT so that a caller can fall back to
+ *   another path ("nurllama 0.18.1 API", kernels.nu section: the quantised
+ *   matvec dispatch reports a type it has no kernel for).
+ *   An asynchronous kernel fault surfaces at the caller's next synchronise.
+ *   No C++ exception crosses this interface.
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ggml tensor type ids ("nurllama 0.18.1 API", convert.nu section, gives
+ * Q8_0 = 8; Q4_K = 12 is GGUF's id for the K-quant). */
+enum gq_fmt {
+    GQ_FMT_Q8_0 = 8,
+    GQ_FMT_Q4_K = 12,
+};
+
+enum gq_status {
+    GQ_OK = 0,
+    GQ_ERR_NULL = 1,   /* a required pointer is NULL */
+    GQ_ERR_FMT = 2,    /* fmt is not Q8_0 or Q4_K */
+    GQ_ERR_SHAPE = 3,  /* rows or M < 0, cols <= 0, or a size that overflows */
+    GQ_ERR_ALIGN = 4,  /* a pointer breaks the alignment rules above */
+    GQ_ERR_DEVICE = 5, /* the HIP runtime reported an error */
+    GQ_ERR_OVERLAP = 6, /* the output range overlaps an input range */
+};
+
+/* Bytes of one row of `cols` input features: ceil(cols/QK) * block bytes.
+ * Returns a negative value for an unknown fmt or cols < 0. Host only. */
+int64_t gq_row_bytes(int fmt, int64_t cols);
+
+/* A static, human-readable name for a status code. */
+const char* gq_status_str(int status);
+
+/*
+ * out[r*cols + c] = w(r, c) as fp32, for r < rows, c < cols.
+ * Bit-exact: Q8_0 w = d*q and Q4_K w = (d*sc)*code - dmin*m, where every
+ * product is exact in fp32 and the Q4_K subtraction rounds once to nearest
+ * even; fp16 subnormal scales are decoded exactly. This is the device
+ * counterpart of the host dequant fallback ("nurllama 0.18.1 API", model.nu
+ * section). Runs on the null stream and returns after it has finished.
+ * out: rows*cols floats.
+ */
+int gq_dequant(int fmt, const void* W, int64_t rows, int64_t cols, float* out);
+
+/*
+ * y[r] = sum_{c < cols} w(r, c) * x[c] for r < rows; y is overwritten.
+ * The decode-step matrix-vector product ("nurllama" README, "What it runs":
+ * the matvec kernels decode GGUF blocks inside the matmul). x: cols floats,
+ * y: rows floats. Accumulation is fp32 with exact per-block products; the
+ * result is within 2e-4 * sum_c |w*x| of the exact sum, and repeated calls
+ * give bit-identical results. Enqueued asynchronously on `stream` (a
+ * hipStream_t; NULL = the null stream).
+ */
+int gq_matvec(int fmt, const void* W, int64_t rows, int64_t cols,
+              const float* x, float* y, void* stream);
+
+/*
+ * Y[m*rows + r] = sum_{c < cols} w(r, c) * X[m*cols + c], for m < M, r < rows;
+ * Y is overwritten. X: [M, cols] row-major fp32; Y: [M, rows] row-major fp32.
+ * The batched form used for prompt chunks ("nurllama 0.18.1 API", model.nu
+ * section: the matmuls run over up to 64 positions at once, each weight read
+ * once per chunk). M < 16 streams W once with fp32 arithmetic; M >= 16 uses
+ * the matrix cores. Same accuracy bound as gq_matvec. Asynchronous on
+ * `stream`.
+ */
+int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
+              const float* X, int64_t M, float* Y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQ_H */

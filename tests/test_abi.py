@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports what include/gq.h declares, and rejects
+bad arguments on the host before any HIP call (so these run without a GPU).
+No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gguf_block_quant_gq_amd as gq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(gq_\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gq.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) >= {"gq_dequant", "gq_matvec", "gq_matmul", "gq_row_bytes", "gq_status_str"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(gq.EXPORTS) == set(names)
+
+
+def test_row_bytes(lib):
+    assert gq.gq_row_bytes(8, 32) == 34
+    assert gq.gq_row_bytes(8, 896) == 28 * 34
+    assert gq.gq_row_bytes(8, 33) == 68
+    assert gq.gq_row_bytes(12, 256) == 144
+    assert gq.gq_row_bytes(12, 896) == 4 * 144
+    assert gq.gq_row_bytes(12, 14336) == 56 * 144
+    assert gq.gq_row_bytes(7, 256) < 0
+    assert gq.gq_row_bytes(8, -1) < 0
+
+
+def test_row_bytes_matches_oracle(oracle):
+    for fmt in (8, 12):
+        for cols in (1, 31, 32, 33, 255, 256, 257, 896, 4096, 4864, 14336):
+            assert gq.gq_row_bytes(fmt, cols) == oracle.row_bytes(fmt, cols)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert gq.status_str(s).startswith("GQ_")
+    assert "unknown" in gq.status_str(99)
+
+
+W_OK = 0x10000        # fake, never dereferenced: validation fails first
+X_OK = 0x20000
+Y_OK = 0x30000
+
+
+def _mv(lib, fmt=12, W=W_OK, rows=4, cols=256, x=X_OK, y=Y_OK):
+    return lib.gq_matvec(fmt, W, rows, cols, x, y, None)
+
+
+def _mm(lib, fmt=12, W=W_OK, rows=4, cols=256, X=X_OK, M=2, Y=Y_OK):
+    return lib.gq_matmul(fmt, W, rows, cols, X, M, Y, None)
+
+
+def _dq(lib, fmt=12, W=W_OK, rows=4, cols=256, out=Y_OK):
+    return lib.gq_dequant(fmt, W, rows, cols, out)
+
+
+@pytest.mark.parametrize("call", [_mv, _mm, _dq])
+def test_validation_before_any_device_call(lib, call):
+    assert call(lib, fmt=0) == gq.GQ_ERR_FMT
+    assert call(lib, fmt=14) == gq.GQ_ERR_FMT
+    assert call(lib, rows=-1) == gq.GQ_ERR_SHAPE
+    assert call(lib, cols=0) == gq.GQ_ERR_SHAPE
+    assert call(lib, cols=-5) == gq.GQ_ERR_SHAPE
+    assert call(lib, rows=1 << 40) == gq.GQ_ERR_SHAPE
+    assert call(lib, W=None) == gq.GQ_ERR_NULL
+    assert call(lib, W=W_OK + 2) == gq.GQ_ERR_ALIGN        # Q4_K needs 4-byte W
+    assert call(lib, fmt=8, W=W_OK + 1) == gq.GQ_ERR_ALIGN  # Q8_0 needs 2-byte W
+    # empty products succeed without touching anything
+    assert call(lib, rows=0, W=None) == gq.GQ_OK
+
+
+def test_validation_vectors(lib):
+    assert _mv(lib, x=None) == gq.GQ_ERR_NULL
+    assert _mv(lib, y=None) == gq.GQ_ERR_NULL
+    assert _mv(lib, x=X_OK + 2) == gq.GQ_ERR_ALIGN
+    assert _mv(lib, y=Y_OK + 1) == gq.GQ_ERR_ALIGN
+    assert _mv(lib, y=W_OK) == gq.GQ_ERR_OVERLAP
+    assert _mv(lib, y=X_OK + 4) == gq.GQ_ERR_OVERLAP
+    assert _mm(lib, M=-1) == gq.GQ_ERR_SHAPE
+    assert _mm(lib, M=0, X=None) == gq.GQ_OK
+    assert _mm(lib, X=None) == gq.GQ_ERR_NULL
+    assert _mm(lib, Y=None) == gq.GQ_ERR_NULL
+    assert _mm(lib, Y=X_OK) == gq.GQ_ERR_OVERLAP
+    assert _dq(lib, out=None) == gq.GQ_ERR_NULL
+    assert _dq(lib, out=W_OK) == gq.GQ_ERR_OVERLAP
+    assert _dq(lib, out=Y_OK + 2) == gq.GQ_ERR_ALIGN
+    # a Q8_0 row range may start on any 34-byte block, i.e. a 2-byte boundary
+    # (the alignment check passes, the overlap check after it fires)
+    assert _mv(lib, fmt=8, W=W_OK + 34, y=W_OK + 40) == gq.GQ_ERR_OVERLAP
