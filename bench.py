@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of libgq on one MI355X.
+
+The timed step is one Llama-3-8B-shaped Q4_K decode step: the q, k, v, o,
+gate, up and down projections of 32 distinct layers (224 gq_matvec calls,
+3.93 GB of packed weights, so every call streams cold weights from HBM),
+enqueued back-to-back on one stream. The step is captured once in a HIP
+graph and replayed (host launch cost would otherwise exceed the GPU time of
+the small projections); the eager rate is reported beside it.
+
+value = algorithmic bytes per step (packed W + x + y of every call) / time,
+in GB/s. The JSON line also carries:
+  roofline      the dominant kernel (the Q4_K GEMV instance of the K = 4096
+                projections) timed alone with HIP events on its stream;
+  cpu_baseline  the C oracle on the host cores over a bounded sample;
+  workloads     the other shapes: Q8_0 lm_head (cold), the Qwen2.5-0.5B and
+                SmolLM-135M decode shapes, the prefill GEMM TFLOP/s at
+                M = 16/64/512 and gq_dequant.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream, which is where libgq launches."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time(self, fn, iters: int, warmup: int = 1) -> float:
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / iters  # ms per fn()
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm: first launches outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def gemv_bytes(fmt_row_bytes: int, rows: int, cols: int) -> int:
+    return rows * fmt_row_bytes + 4 * cols + 4 * rows
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the block-quantised GEMV path runs on a single "
+              f"MI355X (no collectives); --gpus {args.gpus} is not supported.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gguf_block_quant_gq_amd as gq
+    import synth
+
+    torch.cuda.set_device(0)
+    lib = gq.load_library()
+    timer = Timer(torch)
+    stream_ptr = lambda: int(torch.cuda.current_stream().cuda_stream)  # noqa: E731
+
+    # ------------------------------------------------ decode step workload
+    t0 = time.time()
+    mats = []
+    total_bytes = 0
+    for layer in range(synth.LLAMA3_8B_LAYERS):
+        for proj in range(7):
+            name, rows, cols, _, _ = synth.llama3_8b_matrix(layer, proj)
+            W, x = synth.llama3_8b_weight_and_x(layer, proj)
+            Wd = torch.from_numpy(W).cuda()
+            xd = torch.from_numpy(x).cuda()
+            yd = torch.empty(rows, dtype=torch.float32, device="cuda")
+            rb = gq.gq_row_bytes(gq.FMT_Q4_K, cols)
+            nbytes = gemv_bytes(rb, rows, cols)
+            total_bytes += nbytes
+            mats.append(dict(name=name, rows=rows, cols=cols, W=Wd, x=xd, y=yd, bytes=nbytes,
+                             args=(gq.FMT_Q4_K, Wd.data_ptr(), rows, cols, xd.data_ptr(),
+                                   yd.data_ptr())))
+    torch.cuda.synchronize()
+    log(f"generated and uploaded 224 Q4_K matrices ({total_bytes / 1e9:.3f} GB) in "
+        f"{time.time() - t0:.1f}s")
+
+    def step(subset=None):
+        sp = stream_ptr()
+        for m in (mats if subset is None else subset):
+            st = lib.gq_matvec(*m["args"], sp)
+            if st != 0:
+                raise gq.GQError(st, "gq_matvec")
+
+    graph = capture(torch, step)
+    ms_graph = timer.time(graph.replay, args.steps, warmup=args.warmup)
+    ms_eager = timer.time(step, max(5, args.steps // 5), warmup=2)
+    value = total_bytes / (ms_graph * 1e-3) / 1e9
+    log(f"decode step: {ms_graph * 1e3:.1f} us (graph), {ms_eager * 1e3:.1f} us (eager); "
+        f"{value:.0f} GB/s = {100 * value / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+
+    # per-projection rates (graph of the 32 launches of one projection)
+    per_proj = {}
+    for proj in range(7):
+        sub = [m for m in mats if m["name"] == synth.LLAMA3_8B_LAYER[proj][0]]
+        g = capture(torch, lambda sub=sub: step(sub))
+        ms = timer.time(g.replay, max(5, args.steps // 5), warmup=2)
+        b = sum(m["bytes"] for m in sub)
+        per_proj[sub[0]["name"]] = dict(us_per_call=round(ms * 1e3 / len(sub), 3),
+                                        GBps=round(b / (ms * 1e-3) / 1e9, 1),
+                                        pct_hbm=round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1))
+    log(f"per projection: {per_proj}")
+
+    # --------------------------------- roofline: the dominant GEMV kernel
+    # The K = 4096 projections (q, k, v, o, gate, up: 192 launches of one
+    # kernel instance, 73% of the step's bytes) timed alone.
+    dom = [m for m in mats if m["cols"] == 4096]
+    gdom = capture(torch, lambda: step(dom))
+    ms_dom = timer.time(gdom.replay, max(5, args.steps // 5), warmup=2)
+    dom_bytes = sum(m["bytes"] for m in dom) / len(dom)
+    dom_us = ms_dom * 1e3 / len(dom)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="gemv_kernel<Q4KUnit,64,*,1> (Q4_K, K=4096: q, k, v, o, gate, up)",
+                    launches=len(dom), bytes_per_launch=round(dom_bytes),
+                    avg_launch_us=round(dom_us, 3))
+    log(f"roofline: {roofline}")
+
+    extras = {}
+    if not args.no_extras:
+        extras = run_extras(torch, gq, lib, synth, timer, stream_ptr, args)
+        del graph, gdom
+
+    # ------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(synth, args.cpu_seconds)
+        log(f"cpu baseline: {cpu}")
+
+    line = {
+        "metric": "Q4_K/Q8_0 GEMV weight GB/s & % of 8 TB/s HBM peak; prefill GEMM TFLOP/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_graph, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3_8b_decode_step_q4_k",
+            "calls_per_step": len(mats),
+            "layers": synth.LLAMA3_8B_LAYERS,
+            "projections": [p[0] for p in synth.LLAMA3_8B_LAYER],
+            "weight_bytes_per_step": int(sum(m["rows"] * gq.gq_row_bytes(12, m["cols"])
+                                              for m in mats)),
+            "bytes_per_step": int(total_bytes),
+            "launch": "hipGraph replay of 224 gq_matvec launches on one stream",
+            "eager_ms_per_step": round(ms_eager, 4),
+            "eager_GBps": round(total_bytes / (ms_eager * 1e-3) / 1e9, 1),
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "per_projection": per_proj,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "workloads": extras,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
+    out = {}
+    iters = max(10, args.steps)
+
+    # Q8_0 lm_head, cold: rotate 4 copies (580 MB > 2 x 256 MB Infinity Cache)
+    fmt, rows, cols = synth.QWEN05_LM_HEAD
+    W, x = synth.matrix_and_x(fmt, rows, cols, 2, 0)
+    copies = [torch.from_numpy(W).cuda() for _ in range(4)]
+    xd = torch.from_numpy(x).cuda()
+    yd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rb = gq.gq_row_bytes(fmt, cols)
+    nbytes = gemv_bytes(rb, rows, cols)
+
+    def lm(cs):
+        sp = stream_ptr()
+        for c in cs:
+            lib.gq_matvec(fmt, c.data_ptr(), rows, cols, xd.data_ptr(), yd.data_ptr(), sp)
+
+    ms_cold = timer.time(lambda: lm(copies), iters, warmup=2) / len(copies)
+    ms_warm = timer.time(lambda: lm(copies[:1] * 4), iters, warmup=2) / 4
+    out["qwen05b_lm_head_q8_0"] = dict(
+        shape=[rows, cols], us_per_call=round(ms_cold * 1e3, 2),
+        GBps=round(nbytes / (ms_cold * 1e-3) / 1e9, 1),
+        pct_hbm=round(100 * nbytes / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+        warm_us_per_call=round(ms_warm * 1e3, 2))
+    log(f"lm_head: {out['qwen05b_lm_head_q8_0']}")
+
+    # gq_dequant of the lm_head (bit-exact expansion, 545 MB written)
+    dq = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+
+    def dequant():
+        st = lib.gq_dequant(fmt, copies[0].data_ptr(), rows, cols, dq.data_ptr())
+        assert st == 0
+
+    ms = timer.time(dequant, 5, warmup=1)
+    dbytes = rows * rb + 4 * rows * cols
+    out["dequant_lm_head_q8_0"] = dict(us_per_call=round(ms * 1e3, 1),
+                                       GBps=round(dbytes / (ms * 1e-3) / 1e9, 1),
+                                       pct_hbm=round(100 * dbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1))
+    del dq, copies
+
+    # small decode shapes (latency-bound), graph-replayed, warm
+    small = [("smollm135m_ffn_up_q8_0", synth.SMOLLM_FFN_UP, 0, 0)]
+    small += [(f"qwen05b_{r}x{c}_q4_k", (f, r, c), 1, i)
+              for i, (f, r, c) in enumerate(synth.QWEN05_DECODE)]
+    for name, (f, r, c), seed, mid in small:
+        W, x = synth.matrix_and_x(f, r, c, seed, mid)
+        Wd, xd2 = torch.from_numpy(W).cuda(), torch.from_numpy(x).cuda()
+        y2 = torch.empty(r, dtype=torch.float32, device="cuda")
+        b = gemv_bytes(gq.gq_row_bytes(f, c), r, c)
+
+        def call(f=f, r=r, c=c, Wd=Wd, xd2=xd2, y2=y2):
+            sp = stream_ptr()
+            for _ in range(20):
+                lib.gq_matvec(f, Wd.data_ptr(), r, c, xd2.data_ptr(), y2.data_ptr(), sp)
+
+        g = capture(torch, call)
+        ms = timer.time(g.replay, 10, warmup=2) / 20
+        out[name] = dict(us_per_call=round(ms * 1e3, 2),
+                         GBps=round(b / (ms * 1e-3) / 1e9, 1))
+    log(f"small shapes: { {k: v for k, v in out.items() if 'q4_k' in k or 'smollm' in k} }")
+
+    # prefill GEMM at the Llama-3-8B shapes
+    for which in ("gate", "down"):
+        for M in synth.PREFILL_M:
+            W, X, rows, cols = synth.prefill_inputs(which, M)
+            Wd, Xd = torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda()
+            Yd = torch.empty((M, rows), dtype=torch.float32, device="cuda")
+
+            def mm(Wd=Wd, Xd=Xd, Yd=Yd, rows=rows, cols=cols, M=M):
+                st = lib.gq_matmul(12, Wd.data_ptr(), rows, cols, Xd.data_ptr(), M,
+                                   Yd.data_ptr(), stream_ptr())
+                assert st == 0
+
+            ms = timer.time(mm, 10 if M < 512 else 5, warmup=1)
+            flops = 2.0 * M * rows * cols
+            wb = rows * gq.gq_row_bytes(12, cols) + 4 * M * (rows + cols)
+            tf = flops / (ms * 1e-3) / 1e12
+            out[f"prefill_{which}_M{M}"] = dict(
+                us_per_call=round(ms * 1e3, 1), TFLOPs=round(tf, 2),
+                pct_mfma_f16_peak=round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2),
+                GBps=round(wb / (ms * 1e-3) / 1e9, 1))
+            log(f"prefill {which} M={M}: {out[f'prefill_{which}_M{M}']}")
+    return out
+
+
+def cpu_baseline(synth, seconds: float):
+    """The C oracle (dequant + f64 dot) on the host cores over the q, k, v,
+    o, gate, up, down matrices of layer 0 of the same decode step, repeated
+    until about `seconds` of wall time; reported as weight GB/s."""
+    import oracle
+
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    mats = []
+    for proj in range(7):
+        name, rows, cols, _, _ = synth.llama3_8b_matrix(0, proj)
+        W, x = synth.llama3_8b_weight_and_x(0, proj)
+        mats.append((rows, cols, W, x))
+    per_pass = sum(r * oracle.row_bytes(12, c) + 4 * (r + c) for r, c, _, _ in mats)
+    done = 0
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        for rows, cols, W, x in mats:
+            oracle.matvec(12, W, rows, cols, x, nthreads=threads)
+        passes += 1
+        done += per_pass
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) over layer 0's 7 Q4_K projections "
+                      f"({per_pass / 1e6:.1f} MB per pass) of the decode step, "
+                      f"f64 accumulation, {dt:.1f}s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -102,7 +102,8 @@ __global__ __launch_bounds__(kThreads) void dequant_q4_k_kernel(DequantArgs a) {
 
 }  // namespace
 
-hipError_t launch_dequant(int fmt, const DequantArgs& a, hipStream_t s) {
+hipError_t launch_dequant(int fmt, DequantArgs a, hipStream_t s) {
+  a.units = fmt == kFmtQ8_0 ? (a.cols + 31) / 32 : 8 * ((a.cols + 255) / 256);
   const int64_t total = a.rows * (int64_t)a.units;
   int64_t blocks = (total + kThreads - 1) / kThreads;
   if (blocks > 16384) blocks = 16384;

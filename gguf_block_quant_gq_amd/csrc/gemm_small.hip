@@ -24,7 +24,7 @@ constexpr int kMaxM = 15;
 
 template <class F, int G, int U, int RB>
 __global__ __launch_bounds__(kThreads) void gemm_small_kernel(GemmArgs a) {
-  static_assert(G >= 8 && G <= kThreads && (G & (G - 1)) == 0, "G");
+  static_assert(G >= 4 && G <= kThreads && (G & (G - 1)) == 0, "G");
   constexpr int kGroups = kThreads / G;
   constexpr int kWavesPerGroup = G > 64 ? G / 64 : 1;
   constexpr int kSeg = G * U;
@@ -74,6 +74,7 @@ __global__ __launch_bounds__(kThreads) void gemm_small_kernel(GemmArgs a) {
               typename F::X xr;
               if (F::valid(unit, a.units, a.cols)) F::load_x(xr, xm, unit, a.cols);
               else F::zero_x(xr);
+              F::finish_x(xr);
 #pragma unroll
               for (int i = 0; i < RB; ++i) acc[i][m] += F::dot_dec(dec[i][u], xr);
             }
@@ -87,15 +88,15 @@ __global__ __launch_bounds__(kThreads) void gemm_small_kernel(GemmArgs a) {
           if constexpr (G <= 64) {
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
-              const float v = group_sum<G>(acc[i][m]);
+              const float v = group_sum_last<G>(acc[i][m]);
               const int row = rbase + i;
-              if (gl == 0 && row < a.rows) a.Y[(int64_t)(m0 + m) * a.rows + row] = v;
+              if (gl == G - 1 && row < a.rows) a.Y[(int64_t)(m0 + m) * a.rows + row] = v;
             }
           } else {
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
-              const float v = group_sum<64>(acc[i][m]);
-              if ((tid & 63) == 0) red[tid >> 6][i][m] = v;
+              const float v = group_sum_last<64>(acc[i][m]);
+              if ((tid & 63) == 63) red[tid >> 6][i][m] = v;
             }
           }
         }
@@ -128,23 +129,27 @@ hipError_t launch_one(const GemmArgs& a, int max_blocks, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class F>
+template <class F, int RB>
 hipError_t dispatch(const GemmArgs& a, int max_blocks, hipStream_t s) {
   const int n = a.units;
-  if (n <= 8) return launch_one<F, 8, 1, 2>(a, max_blocks, s);
-  if (n <= 16) return launch_one<F, 16, 1, 2>(a, max_blocks, s);
-  if (n <= 32) return launch_one<F, 32, 1, 2>(a, max_blocks, s);
-  if (n <= 64) return launch_one<F, 64, 1, 2>(a, max_blocks, s);
-  if (n <= 128) return launch_one<F, 64, 2, 2>(a, max_blocks, s);
-  if (n <= 256) return launch_one<F, 128, 2, 2>(a, max_blocks, s);
-  return launch_one<F, 256, 2, 2>(a, max_blocks, s);
+  if (n <= 8) return launch_one<F, 8, 1, RB>(a, max_blocks, s);
+  if (n <= 16) return launch_one<F, 16, 1, RB>(a, max_blocks, s);
+  if (n <= 32) return launch_one<F, 32, 1, RB>(a, max_blocks, s);
+  if (n <= 64) return launch_one<F, 64, 1, RB>(a, max_blocks, s);
+  if (n <= 128) return launch_one<F, 128, 1, RB>(a, max_blocks, s);
+  return launch_one<F, 256, 1, RB>(a, max_blocks, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_small(int fmt, const GemmArgs& a, int max_blocks, hipStream_t s) {
-  if (fmt == kFmtQ8_0) return dispatch<Q8Unit>(a, max_blocks, s);
-  return dispatch<Q4KUnit>(a, max_blocks, s);
+hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s) {
+  const int max_blocks = cus * 4;
+  if (fmt == kFmtQ8_0) {
+    a.units = (a.cols + 31) / 32;
+    return dispatch<Q8Unit, 2>(a, max_blocks, s);
+  }
+  a.units = 4 * ((a.cols + 255) / 256);
+  return dispatch<Q4KUnit, 1>(a, max_blocks, s);
 }
 
 }  // namespace gq

@@ -2,21 +2,26 @@
 //
 // The decode-step matrix-vector product is bound by the bytes of W
 // (nx_f32_llm_v4 source, model binder: decode is memory-bandwidth bound, so
-// bytes moved is the runtime). The kernels stream each packed block once,
-// straight from HBM, and decode it in registers.
+// bytes moved is the runtime). The kernel streams each packed block once,
+// straight from HBM, and decodes it in registers.
 //
 // Work decomposition ("row groups"): the 256 threads of a workgroup form
-// 256/G groups of G lanes (G a power of two, 8..256). A group owns one row at
-// a time; its lanes split the row into units -- a Q8_0 block (32 weights,
-// 34 B) or a 16-byte Q4_K code chunk (32 weights) -- lane l owning units
-// l, l + G, ..., l + (U-1)G. Because a lane always owns the same units, the
-// x values of those units are loaded once into registers and reused for every
-// row the group visits; nothing else is staged. Consecutive lanes own
-// consecutive units, so each load instruction of a wave reads one contiguous
-// span of the row. Each group keeps RB rows in flight, then folds its lanes'
-// partial sums with a fixed butterfly (and, for G > 64, through LDS), so the
-// result is deterministic. Rows wider than G*U units are walked in segments,
-// reloading x per segment.
+// 256/G groups of G lanes (G a power of two, 4..256). A group owns RB rows at
+// a time; its lanes split each row into units -- a Q8_0 block (32 weights,
+// 34 B) or the 32 code bytes of one Q4_K sub-block pair (64 weights) -- lane
+// l owning unit l. Because a lane always owns the same unit, that unit's x
+// values are loaded once into registers and reused for every row the group
+// visits. Consecutive lanes own consecutive units, so each load instruction
+// of a wave reads one contiguous span of a row.
+//
+// Workgroups loop over row batches (grid-stride); the bytes of the next batch
+// are requested before the current one is decoded, so HBM latency overlaps
+// the arithmetic. Loads are never predicated: a row index past the end is
+// clamped to the last row (its result is discarded) and a lane whose unit
+// lies past the row's last column reads a real unit of the row with zero x.
+// Partial sums are folded with a fixed DPP/shuffle butterfly (and for
+// G > 64 through LDS), so results are deterministic. Rows wider than G units
+// are walked in segments, reloading x per segment.
 //
 // Prior art: the one-warp-per-row matvec of the "nurllama" README ("What it
 // runs": the warp walks the row's blocks, lanes split each block, a shuffle
@@ -31,133 +36,275 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// ------------------------------------------------------------ the kernel
-template <class F, int G, int U, int RB>
+// Launch-shape constants (compile-time; the defaults are the measured best
+// on MI355X): resident workgroups per CU for RB = 1 and RB > 1 kernels, and
+// the rows below which a group takes one row per iteration.
+#ifndef GQ_GEMV_WG_PER_CU_RB1
+#define GQ_GEMV_WG_PER_CU_RB1 4
+#endif
+#ifndef GQ_GEMV_WG_PER_CU_RBN
+#define GQ_GEMV_WG_PER_CU_RBN 2
+#endif
+#ifndef GQ_GEMV_RBN
+#define GQ_GEMV_RBN 2
+#endif
+#ifndef GQ_GEMV_RB1_WAVES_PER_CU
+#define GQ_GEMV_RB1_WAVES_PER_CU 8
+#endif
+#ifndef GQ_GEMV_NB
+#define GQ_GEMV_NB 1
+#endif
+
+template <class F, int RB>
+__device__ __forceinline__ void load_rows(typename F::Raw (&raw)[RB], const GemvArgs& a,
+                                          int rbase, int unit_ld) {
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    int row = rbase + i;
+    row = row < a.rows ? row : a.rows - 1;
+    F::load(raw[i], a.W + (int64_t)row * a.row_bytes, unit_ld);
+  }
+}
+
+template <int G, int RB>
+__device__ __forceinline__ void reduce_store(float (&acc)[RB], const GemvArgs& a, int rbase,
+                                             int gl, int grp, float (*red)[RB]) {
+  if constexpr (G <= 64) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) acc[i] = group_sum_last<G>(acc[i]);
+    if (gl == G - 1) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        if (rbase + i < a.rows) a.y[rbase + i] = acc[i];
+    }
+  } else {
+    constexpr int kWavesPerGroup = G / 64;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) acc[i] = group_sum_last<64>(acc[i]);
+    const int tid = threadIdx.x;
+    if ((tid & 63) == 63) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) red[tid >> 6][i] = acc[i];
+    }
+    __syncthreads();
+    if (gl < RB) {
+      const int w0 = grp * kWavesPerGroup;
+      float v = red[w0][gl];
+#pragma unroll
+      for (int w = 1; w < kWavesPerGroup; ++w) v += red[w0 + w][gl];
+      const int row = rbase + gl;
+      if (row < a.rows) a.y[row] = v;
+    }
+    __syncthreads();
+  }
+}
+
+// Stage the G*kChunks 16-byte chunks of x that the group's lanes own into
+// LDS with coalesced loads (each wave instruction reads 1 KB of consecutive
+// columns), zero past `cols`, then give every lane its own chunks. The
+// chunks of unit u are stored rotated by u / (16 / kChunks) so that the 16
+// lanes served together by a ds_read_b128 hit 16 different bank quads.
+template <class F, int G>
+__device__ __forceinline__ int x_slot(int q) {
+  constexpr int C = F::kChunks;
+  const int u = q / C, k = q % C;
+  return C * u + ((k + u / (16 / C)) % C);
+}
+
+// Staging is split in two so that the x loads can be issued before the
+// first W batch: issue_x puts the thread's share of x chunks into registers
+// (no wait), commit_x writes them to LDS once they have arrived.
+template <class F, int G>
+struct XStage {
+  static constexpr int kPerThread = (G * F::kChunks + kThreads - 1) / kThreads;
+  f32x4 v[kPerThread];
+};
+
+template <class F, int G>
+__device__ __forceinline__ void issue_x(XStage<F, G>& st, const float* x, int cols, int ubase) {
+  constexpr int C = F::kChunks;
+  const int c0 = ubase * F::kPerUnitCols;
+#pragma unroll
+  for (int j = 0; j < XStage<F, G>::kPerThread; ++j) {
+    const int q = threadIdx.x + j * kThreads;
+    const int col = c0 + 4 * q;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (q < G * C) {
+      if (col + 4 <= cols) {
+        v = load_f32x4(x + col);
+      } else {
+        v.x = col < cols ? x[col] : 0.f;
+        v.y = col + 1 < cols ? x[col + 1] : 0.f;
+        v.z = col + 2 < cols ? x[col + 2] : 0.f;
+        v.w = col + 3 < cols ? x[col + 3] : 0.f;
+      }
+    }
+    st.v[j] = v;
+  }
+}
+
+template <class F, int G>
+__device__ __forceinline__ void commit_x(f32x4* xs, const XStage<F, G>& st) {
+  constexpr int C = F::kChunks;
+#pragma unroll
+  for (int j = 0; j < XStage<F, G>::kPerThread; ++j) {
+    const int q = threadIdx.x + j * kThreads;
+    if (q < G * C) xs[x_slot<F, G>(q)] = st.v[j];
+  }
+}
+
+template <class F, int G>
+__device__ __forceinline__ void fetch_x(typename F::X& xr, const f32x4* xs, int gl) {
+  constexpr int C = F::kChunks;
+  f32x4 c[C];
+#pragma unroll
+  for (int k = 0; k < C; ++k) c[k] = xs[x_slot<F, G>(C * gl + k)];
+  F::set_x(xr, c);
+  F::finish_x(xr);
+}
+
+// Rows fit in one segment: x stays in registers for the whole kernel.
+// The workgroup's row batches flow through a ring of NB register buffers:
+// batch it sits in buffer (k mod NB) and its loads were issued NB-1 batches
+// earlier, so NB-1 batches are always in flight while one is decoded.
+// Prefetches are unconditional (past the last batch they re-read the last
+// row, which is cached and discarded), so no branch surrounds a load and each
+// wait covers only the oldest buffer.
+template <class F, int G, int RB, int NB>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
-  static_assert(G >= 8 && G <= kThreads && (G & (G - 1)) == 0, "G");
+  static_assert(G >= 4 && G <= kThreads && (G & (G - 1)) == 0, "G");
+  static_assert(NB >= 1 && NB <= 8, "NB");
   constexpr int kGroups = kThreads / G;
-  constexpr int kWavesPerGroup = G > 64 ? G / 64 : 1;
-  constexpr int kSeg = G * U;  // units per segment
+  constexpr int kRowsPerIter = kGroups * RB;
+  __shared__ float red[kThreads / 64][RB];
 
   const int tid = threadIdx.x;
   const int grp = tid / G;
   const int gl = tid % G;
   const typename F::Lane ln = F::lane(gl);
+  const int unit = gl;
+  const int unit_ld = unit < a.units ? unit : a.units - 1;
 
-  __shared__ float red[kThreads / 64][RB];
+  const int iters = (a.rows + kRowsPerIter - 1) / kRowsPerIter;
+  int it = blockIdx.x;
+  if (it >= iters) return;  // uniform per workgroup
+  const int stride = gridDim.x;
+  auto batch_row = [&](int b) {
+    return (b < iters ? b : iters - 1) * kRowsPerIter + grp * RB;
+  };
 
-  typename F::X xr[U];
-  const int nseg = (a.units + kSeg - 1) / kSeg;
-  if (nseg == 1) {
+  // x is requested first, then the first NB W batches; x is committed to
+  // LDS while the W batches are still in flight.
+  __shared__ f32x4 xs[G * F::kChunks];
+  XStage<F, G> st;
+  issue_x<F, G>(st, a.x, a.cols, 0);
+  typename F::Raw buf[NB][RB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int unit = u * G + gl;
-      if (F::valid(unit, a.units, a.cols)) F::load_x(xr[u], a.x, unit, a.cols);
-      else F::zero_x(xr[u]);
+  for (int s = 0; s < NB; ++s) load_rows<F, RB>(buf[s], a, batch_row(it + s * stride), unit_ld);
+  commit_x<F, G>(xs, st);
+  __syncthreads();
+  typename F::X xr;
+  fetch_x<F, G>(xr, xs, gl);
+
+  bool done = false;
+  while (!done) {
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      if (!done) {
+        float acc[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) acc[i] = F::dot(buf[s][i], xr, ln);
+        reduce_store<G, RB>(acc, a, it * kRowsPerIter + grp * RB, gl, grp, red);
+        it += stride;
+        if (it >= iters) done = true;
+        else load_rows<F, RB>(buf[s], a, batch_row(it + (NB - 1) * stride), unit_ld);
+      }
     }
   }
+}
 
-  const int rows_per_iter = kGroups * RB;
-  for (int r0 = blockIdx.x * rows_per_iter; r0 < a.rows; r0 += gridDim.x * rows_per_iter) {
-    const int rbase = r0 + grp * RB;
+// Rows wider than G units: each row batch walks the row in segments of G
+// units, reloading the lane's x values per segment.
+template <class F, int G, int RB>
+__global__ __launch_bounds__(kThreads) void gemv_seg_kernel(GemvArgs a) {
+  constexpr int kGroups = kThreads / G;
+  constexpr int kRowsPerIter = kGroups * RB;
+  __shared__ float red[kThreads / 64][RB];
+
+  const int tid = threadIdx.x;
+  const int grp = tid / G;
+  const int gl = tid % G;
+  const typename F::Lane ln = F::lane(gl);
+  const int nseg = (a.units + G - 1) / G;
+  const int iters = (a.rows + kRowsPerIter - 1) / kRowsPerIter;
+
+  for (int it = blockIdx.x; it < iters; it += gridDim.x) {
+    const int rbase = it * kRowsPerIter + grp * RB;
     float acc[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) acc[i] = 0.f;
-
     for (int seg = 0; seg < nseg; ++seg) {
-      const int ubase = seg * kSeg;
-      if (nseg > 1) {
+      const int unit = seg * G + gl;
+      const int unit_ld = unit < a.units ? unit : a.units - 1;
+      typename F::Raw raw[RB];
+      load_rows<F, RB>(raw, a, rbase, unit_ld);
+      typename F::X xr;
+      if (F::valid(unit, a.units, a.cols)) F::load_x(xr, a.x, unit, a.cols);
+      else F::zero_x(xr);
+      F::finish_x(xr);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          int unit = ubase + u * G + gl;
-          if (F::valid(unit, a.units, a.cols)) F::load_x(xr[u], a.x, unit, a.cols);
-          else F::zero_x(xr[u]);
-        }
-      }
-      typename F::Raw raw[RB][U];
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int row = rbase + i;
-        const uint8_t* rp = a.W + (int64_t)row * a.row_bytes;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          int unit = ubase + u * G + gl;
-          if (row < a.rows && F::valid(unit, a.units, a.cols)) F::load(raw[i][u], rp, unit);
-          else F::zero(raw[i][u]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[i] += F::dot(raw[i][u], xr[u], ln);
-      }
+      for (int i = 0; i < RB; ++i) acc[i] += F::dot(raw[i], xr, ln);
     }
-
-    if constexpr (G <= 64) {
-#pragma unroll
-      for (int i = 0; i < RB; ++i) acc[i] = group_sum<G>(acc[i]);
-      if (gl < RB) {
-        float v = acc[0];
-#pragma unroll
-        for (int i = 1; i < RB; ++i)
-          if (gl == i) v = acc[i];
-        const int row = rbase + gl;
-        if (row < a.rows) a.y[row] = v;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < RB; ++i) acc[i] = group_sum<64>(acc[i]);
-      const int wave = tid >> 6;
-      if ((tid & 63) == 0) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i) red[wave][i] = acc[i];
-      }
-      __syncthreads();
-      if (gl < RB) {
-        const int w0 = grp * kWavesPerGroup;
-        float v = red[w0][gl];
-#pragma unroll
-        for (int w = 1; w < kWavesPerGroup; ++w) v += red[w0 + w][gl];
-        const int row = rbase + gl;
-        if (row < a.rows) a.y[row] = v;
-      }
-      __syncthreads();
-    }
+    reduce_store<G, RB>(acc, a, rbase, gl, grp, red);
   }
 }
 
-template <class F, int G, int U, int RB>
-hipError_t launch_one(const GemvArgs& a, int max_blocks, hipStream_t s) {
-  constexpr int kGroups = kThreads / G;
-  int64_t tiles = ((int64_t)a.rows + kGroups * RB - 1) / (kGroups * RB);
-  int blocks = (int)(tiles < max_blocks ? tiles : max_blocks);
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL((gemv_kernel<F, G, U, RB>), dim3(blocks), dim3(kThreads), 0, s, a);
+template <class F, int G, int RB>
+hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s) {
+  constexpr int kRowsPerIter = (kThreads / G) * RB;
+  const int64_t iters = ((int64_t)a.rows + kRowsPerIter - 1) / kRowsPerIter;
+  // As many workgroups as can be resident at once (4 per CU at <= 128
+  // VGPRs, else 2); each loops over row batches.
+  const int64_t cap = (int64_t)cus * (RB == 1 ? GQ_GEMV_WG_PER_CU_RB1 : GQ_GEMV_WG_PER_CU_RBN);
+  const int blocks = (int)(iters < cap ? iters : cap);
+  if (a.units <= G)
+    hipLaunchKernelGGL((gemv_kernel<F, G, RB, GQ_GEMV_NB>), dim3(blocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemv_seg_kernel<F, G, RB>), dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-// Pick (G, U): the smallest G*U that covers the row's units (at most 4 units
-// per lane), preferring fewer idle lanes; wide rows use G = 256, U = 4 and
-// segments.
+// G: the smallest power of two >= the row's units (max 256; wider rows use
+// segments). RB: rows per group per iteration -- 1 when the matrix is too
+// short to give every CU a few groups, else 2.
+template <class F, int G>
+hipError_t with_g(const GemvArgs& a, int cus, hipStream_t s) {
+  const int64_t groups_needed = (int64_t)cus * GQ_GEMV_RB1_WAVES_PER_CU * (G >= 64 ? 1 : 64 / G);
+  if ((int64_t)a.rows < 2 * groups_needed) return launch_one<F, G, 1>(a, cus, s);
+  return launch_one<F, G, GQ_GEMV_RBN>(a, cus, s);
+}
+
 template <class F>
-hipError_t dispatch(const GemvArgs& a, int max_blocks, hipStream_t s) {
+hipError_t dispatch(const GemvArgs& a, int cus, hipStream_t s) {
   const int n = a.units;
-  if (n <= 8) return launch_one<F, 8, 1, 4>(a, max_blocks, s);
-  if (n <= 16) return launch_one<F, 16, 1, 4>(a, max_blocks, s);
-  if (n <= 32) return launch_one<F, 32, 1, 4>(a, max_blocks, s);
-  if (n <= 64) return launch_one<F, 64, 1, 4>(a, max_blocks, s);
-  if (n <= 128) return launch_one<F, 64, 2, 4>(a, max_blocks, s);
-  if (n <= 192) return launch_one<F, 64, 3, 2>(a, max_blocks, s);
-  if (n <= 256) return launch_one<F, 64, 4, 2>(a, max_blocks, s);
-  if (n <= 512) return launch_one<F, 256, 2, 4>(a, max_blocks, s);
-  return launch_one<F, 256, 4, 2>(a, max_blocks, s);
+  if (n <= 4) return with_g<F, 4>(a, cus, s);
+  if (n <= 8) return with_g<F, 8>(a, cus, s);
+  if (n <= 16) return with_g<F, 16>(a, cus, s);
+  if (n <= 32) return with_g<F, 32>(a, cus, s);
+  if (n <= 64) return with_g<F, 64>(a, cus, s);
+  if (n <= 128) return with_g<F, 128>(a, cus, s);
+  return with_g<F, 256>(a, cus, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemv(int fmt, const GemvArgs& a, int max_blocks, hipStream_t s) {
-  if (fmt == kFmtQ8_0) return dispatch<Q8Unit>(a, max_blocks, s);
-  return dispatch<Q4KUnit>(a, max_blocks, s);
+hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s) {
+  if (fmt == kFmtQ8_0) {
+    a.units = (a.cols + 31) / 32;
+    return dispatch<Q8Unit>(a, cus, s);
+  }
+  a.units = 4 * ((a.cols + 255) / 256);
+  return dispatch<Q4KUnit>(a, cus, s);
 }
 
 }  // namespace gq

@@ -39,11 +39,6 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
 }
 
-int units_per_row(int fmt, int64_t cols) {
-  if (fmt == gq::kFmtQ8_0) return (int)((cols + 31) / 32);
-  return (int)(8 * ((cols + 255) / 256));
-}
-
 // Shape and format checks shared by every entry point. On success *rb is
 // the row stride in bytes and *wbytes the size of W.
 int check_shape(int fmt, int64_t rows, int64_t cols, int64_t M, int64_t* rb, int64_t* wbytes) {
@@ -98,7 +93,7 @@ extern "C" int gq_dequant(int fmt, const void* W, int64_t rows, int64_t cols, fl
   if (overlaps(out, rows * cols * 4, W, wbytes)) return GQ_ERR_OVERLAP;
 
   (void)hipGetLastError();  // start from a clean error state
-  gq::DequantArgs a{(const uint8_t*)W, out, rb, rows, (int)cols, units_per_row(fmt, cols)};
+  gq::DequantArgs a{(const uint8_t*)W, out, rb, rows, (int)cols, 0};
   hipError_t e = gq::launch_dequant(fmt, a, 0);
   if (e != hipSuccess) return GQ_ERR_DEVICE;
   return finish(hipStreamSynchronize(0));
@@ -118,8 +113,8 @@ extern "C" int gq_matvec(int fmt, const void* W, int64_t rows, int64_t cols, con
   const int cus = current_cus();
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
-  gq::GemvArgs a{(const uint8_t*)W, x, y, rb, (int)rows, (int)cols, units_per_row(fmt, cols)};
-  return finish(gq::launch_gemv(fmt, a, cus * 8, (hipStream_t)stream));
+  gq::GemvArgs a{(const uint8_t*)W, x, y, rb, (int)rows, (int)cols, 0};
+  return finish(gq::launch_gemv(fmt, a, cus, (hipStream_t)stream));
 }
 
 extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,
@@ -138,6 +133,6 @@ extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, con
   const int cus = current_cus();
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
-  gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, (int)M, units_per_row(fmt, cols)};
-  return finish(gq::launch_gemm_small(fmt, a, cus * 8, (hipStream_t)stream));
+  gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
+  return finish(gq::launch_gemm_small(fmt, a, cus, (hipStream_t)stream));
 }

@@ -189,12 +189,28 @@ __device__ __forceinline__ void q4k_chunk_codes(u32x4 v, float lo[16], float hi[
 }
 
 // ------------------------------------------------------------ reductions --
-// Butterfly sum over aligned groups of G lanes (G a power of two <= 64).
-// Every lane of the group ends with the same total; the order is fixed.
+// Sum over aligned groups of G lanes (G a power of two <= 64) with DPP only
+// (no LDS traffic). Within a 16-lane DPP row the butterfly quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror leaves the row
+// total in every lane of the row; row_bcast:15 then adds row 0's total into
+// row 1 and row 2's into row 3, and row_bcast:31 adds lane 31 into rows 2-3.
+// The group total ends up in the group's LAST lane (lane G-1 of the group);
+// the association order is fixed, so results are deterministic.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
 template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+__device__ __forceinline__ float group_sum_last(float v) {
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "G");
+  if constexpr (G >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  if constexpr (G >= 16) v += dpp_f32<0x140>(v); // row_mirror
+  if constexpr (G >= 32) v += dpp_f32<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  if constexpr (G >= 64) v += dpp_f32<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
   return v;
 }
 

@@ -17,7 +17,7 @@ struct GemvArgs {
   int64_t row_bytes;
   int rows;
   int cols;
-  int units;  // per row: Q8_0 blocks, or Q4_K 16-byte code chunks (8 per block)
+  int units;  // units per row (set by the launcher)
 };
 
 struct DequantArgs {
@@ -26,7 +26,7 @@ struct DequantArgs {
   int64_t row_bytes;
   int64_t rows;
   int cols;
-  int units;  // as in GemvArgs
+  int units;  // per row: Q8_0 blocks or Q4_K 16-byte chunks (set by the launcher)
 };
 
 struct GemmArgs {
@@ -41,9 +41,10 @@ struct GemmArgs {
 };
 
 // All launchers enqueue on `s` and return the launch status.
-hipError_t launch_dequant(int fmt, const DequantArgs& a, hipStream_t s);
-hipError_t launch_gemv(int fmt, const GemvArgs& a, int max_blocks, hipStream_t s);
-hipError_t launch_gemm_small(int fmt, const GemmArgs& a, int max_blocks, hipStream_t s);
-hipError_t launch_gemm_mfma(int fmt, const GemmArgs& a, int num_cus, hipStream_t s);
+// `units` is filled in by the launcher; `cus` is the device's CU count.
+hipError_t launch_dequant(int fmt, DequantArgs a, hipStream_t s);
+hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s);
+hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
+hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s);
 
 }  // namespace gq
