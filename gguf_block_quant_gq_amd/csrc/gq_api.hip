@@ -134,5 +134,8 @@ extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, con
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
   gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
+  // M >= 16 is a dense contraction: Q4_K runs on the matrix cores.
+  if (M >= 16 && fmt == GQ_FMT_Q4_K)
+    return finish(gq::launch_gemm_mfma(fmt, a, cus, (hipStream_t)stream));
   return finish(gq::launch_gemm_small(fmt, a, cus, (hipStream_t)stream));
 }
