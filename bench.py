@@ -78,6 +78,35 @@ def gemv_bytes(fmt_row_bytes: int, rows: int, cols: int) -> int:
     return rows * fmt_row_bytes + 4 * cols + 4 * rows
 
 
+DOMINANT_KERNEL = "gemv_kernel<Q4KUnit, 64, 2, 1>"
+# HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE
+# and WRITE_SIZE (bench.py --traffic-probe), each scaled by the same counter
+# on a 256 MiB plain copy (FETCH x 2.000, WRITE x 1.000); set to None whenever
+# the kernel changes until it is measured again.
+TRAFFIC_BYTES_PER_LAUNCH = 21491488
+
+
+def dominant_launches(mats):
+    return [m for m in mats if m["cols"] == 4096 and m["rows"] >= 4096]
+
+
+def traffic_probe(torch, gq, lib, mats, stream_ptr):
+    """One plain device copy of 256 MiB (the counter calibration), then one
+    pass over the dominant kernel's launches; for rocprofv3 --pmc runs."""
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    sp = stream_ptr()
+    for m in dominant_launches(mats):
+        lib.gq_matvec(*m["args"], sp)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel(),
+                      "dominant_bytes_per_launch": sum(m["bytes"] for m in dominant_launches(mats))
+                      / len(dominant_launches(mats))}), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,6 +115,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run a 256 MiB copy and one pass of the dominant kernel, then exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -124,6 +155,10 @@ def main() -> int:
     log(f"generated and uploaded 224 Q4_K matrices ({total_bytes / 1e9:.3f} GB) in "
         f"{time.time() - t0:.1f}s")
 
+    if args.traffic_probe:
+        traffic_probe(torch, gq, lib, mats, stream_ptr)
+        return 0
+
     def step(subset=None):
         sp = stream_ptr()
         for m in (mats if subset is None else subset):
@@ -151,19 +186,20 @@ def main() -> int:
     log(f"per projection: {per_proj}")
 
     # --------------------------------- roofline: the dominant GEMV kernel
-    # The K = 4096 projections (q, k, v, o, gate, up: 192 launches of one
-    # kernel instance, 73% of the step's bytes) timed alone.
-    dom = [m for m in mats if m["cols"] == 4096]
+    # The launches of one kernel instance, gemv_kernel<Q4KUnit, 64, 2, 1>:
+    # the K = 4096 projections with >= 4096 rows (q, o, gate, up; 128 of the
+    # 224 launches, 69% of the step's bytes), timed alone (graph replay, HIP
+    # events on the launch stream).
+    dom = dominant_launches(mats)
     gdom = capture(torch, lambda: step(dom))
     ms_dom = timer.time(gdom.replay, max(5, args.steps // 5), warmup=2)
     dom_bytes = sum(m["bytes"] for m in dom) / len(dom)
     dom_us = ms_dom * 1e3 / len(dom)
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="gemv_kernel<Q4KUnit,64,*,1> (Q4_K, K=4096: q, k, v, o, gate, up)",
-                    launches=len(dom), bytes_per_launch=round(dom_bytes),
-                    avg_launch_us=round(dom_us, 3))
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=TRAFFIC_BYTES_PER_LAUNCH,
+                    kernel=DOMINANT_KERNEL, launches_per_step=len(dom),
+                    bytes_per_launch=round(dom_bytes), avg_launch_us=round(dom_us, 3))
     log(f"roofline: {roofline}")
 
     extras = {}
