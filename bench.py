@@ -78,12 +78,12 @@ def gemv_bytes(fmt_row_bytes: int, rows: int, cols: int) -> int:
     return rows * fmt_row_bytes + 4 * cols + 4 * rows
 
 
-DOMINANT_KERNEL = "gemv_kernel<Q4KUnit, 64, 2, 1>"
+DOMINANT_KERNEL = "gemv_kernel<Q4KUnit, 64, 2>"
 # HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE
 # and WRITE_SIZE (bench.py --traffic-probe), each scaled by the same counter
 # on a 256 MiB plain copy (FETCH x 2.000, WRITE x 1.000); set to None whenever
 # the kernel changes until it is measured again.
-TRAFFIC_BYTES_PER_LAUNCH = 21491488
+TRAFFIC_BYTES_PER_LAUNCH = 21619395
 
 
 def dominant_launches(mats):

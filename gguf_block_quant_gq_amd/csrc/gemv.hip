@@ -26,6 +26,8 @@
 // Prior art: the one-warp-per-row matvec of the "nurllama" README ("What it
 // runs": the warp walks the row's blocks, lanes split each block, a shuffle
 // reduction folds the partials), re-shaped for 64-wide wavefronts.
+#include <type_traits>
+
 #include "gq_device.h"
 #include "gq_internal.h"
 #include "gq_units.h"
@@ -48,11 +50,14 @@ constexpr int kThreads = 256;
 #ifndef GQ_GEMV_RBN
 #define GQ_GEMV_RBN 2
 #endif
+#ifndef GQ_GEMV_Q8_WG_PER_CU
+#define GQ_GEMV_Q8_WG_PER_CU GQ_GEMV_WG_PER_CU_RBN
+#endif
+#ifndef GQ_GEMV_Q8_RBN
+#define GQ_GEMV_Q8_RBN GQ_GEMV_RBN
+#endif
 #ifndef GQ_GEMV_RB1_WAVES_PER_CU
 #define GQ_GEMV_RB1_WAVES_PER_CU 8
-#endif
-#ifndef GQ_GEMV_NB
-#define GQ_GEMV_NB 1
 #endif
 
 template <class F, int RB>
@@ -164,19 +169,19 @@ __device__ __forceinline__ void fetch_x(typename F::X& xr, const f32x4* xs, int 
 }
 
 // Rows fit in one segment: x stays in registers for the whole kernel.
-// The workgroup's row batches flow through a ring of NB register buffers:
-// batch it sits in buffer (k mod NB) and its loads were issued NB-1 batches
-// earlier, so NB-1 batches are always in flight while one is decoded.
-// Prefetches are unconditional (past the last batch they re-read the last
-// row, which is cached and discarded), so no branch surrounds a load and each
-// wait covers only the oldest buffer.
-template <class F, int G, int RB, int NB>
+// Row groups wider than a wave (G > 64) would need a barrier per batch to add
+// the waves' partial sums; instead each wave parks its partials in an LDS
+// ring of kSlots batches and the ring is folded (and y stored) once per
+// kSlots batches, so the waves run unsynchronised in between.
+template <class F, int G, int RB>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   static_assert(G >= 4 && G <= kThreads && (G & (G - 1)) == 0, "G");
-  static_assert(NB >= 1 && NB <= 8, "NB");
   constexpr int kGroups = kThreads / G;
   constexpr int kRowsPerIter = kGroups * RB;
-  __shared__ float red[kThreads / 64][RB];
+  constexpr int kWavesPerGroup = G > 64 ? G / 64 : 1;
+  constexpr int kSlots = 8;
+  constexpr bool kQ8 = std::is_same<typename F::Base, Q8Unit>::value;
+  __shared__ float ring[G > 64 ? kSlots : 1][kThreads / 64][RB];
 
   const int tid = threadIdx.x;
   const int grp = tid / G;
@@ -186,40 +191,73 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   const int unit_ld = unit < a.units ? unit : a.units - 1;
 
   const int iters = (a.rows + kRowsPerIter - 1) / kRowsPerIter;
-  int it = blockIdx.x;
-  if (it >= iters) return;  // uniform per workgroup
+  const int it0 = blockIdx.x;
+  if (it0 >= iters) return;  // uniform per workgroup
   const int stride = gridDim.x;
-  auto batch_row = [&](int b) {
-    return (b < iters ? b : iters - 1) * kRowsPerIter + grp * RB;
-  };
 
-  // x is requested first, then the first NB W batches; x is committed to
-  // LDS while the W batches are still in flight.
+  // x is requested first, then the first W batch; x is committed to LDS
+  // while the W batch is still in flight.
   __shared__ f32x4 xs[G * F::kChunks];
   XStage<F, G> st;
   issue_x<F, G>(st, a.x, a.cols, 0);
-  typename F::Raw buf[NB][RB];
-#pragma unroll
-  for (int s = 0; s < NB; ++s) load_rows<F, RB>(buf[s], a, batch_row(it + s * stride), unit_ld);
+  typename F::Raw buf[RB];
+  load_rows<F, RB>(buf, a, it0 * kRowsPerIter + grp * RB, unit_ld);
   commit_x<F, G>(xs, st);
   __syncthreads();
   typename F::X xr;
   fetch_x<F, G>(xr, xs, gl);
 
-  bool done = false;
-  while (!done) {
+  // fold the ring: slot s holds batch it0 + (n0 + s) * stride
+  auto flush = [&](int n0, int used) {
+    __syncthreads();
+    if (gl < used * RB) {
+      const int s = gl / RB, i = gl % RB;
+      const int w0 = grp * kWavesPerGroup;
+      float v = ring[s][w0][i];
 #pragma unroll
-    for (int s = 0; s < NB; ++s) {
-      if (!done) {
-        float acc[RB];
-#pragma unroll
-        for (int i = 0; i < RB; ++i) acc[i] = F::dot(buf[s][i], xr, ln);
-        reduce_store<G, RB>(acc, a, it * kRowsPerIter + grp * RB, gl, grp, red);
-        it += stride;
-        if (it >= iters) done = true;
-        else load_rows<F, RB>(buf[s], a, batch_row(it + (NB - 1) * stride), unit_ld);
-      }
+      for (int w = 1; w < kWavesPerGroup; ++w) v += ring[s][w0 + w][i];
+      const int row = (it0 + (n0 + s) * stride) * kRowsPerIter + grp * RB + i;
+      if (row < a.rows) a.y[row] = v;
     }
+    __syncthreads();
+  };
+
+  int n = 0;  // batches done by this workgroup
+  for (int it = it0; it < iters; it += stride, ++n) {
+    float acc[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) acc[i] = F::dot(buf[i], xr, ln);
+    // The next batch's loads are unconditional: past the last batch they
+    // re-read the last batch (cached, discarded), so no branch surrounds them.
+    // Q4_K issues them before the reduction, Q8_0 (whose short rows make
+    // more, smaller batches) after it: each order measured faster for its
+    // format.
+    const int nx = it + stride < iters ? it + stride : iters - 1;
+    if constexpr (!kQ8) load_rows<F, RB>(buf, a, nx * kRowsPerIter + grp * RB, unit_ld);
+    if constexpr (G <= 64) {
+      const int rbase = it * kRowsPerIter + grp * RB;
+#pragma unroll
+      for (int i = 0; i < RB; ++i) acc[i] = group_sum_last<G>(acc[i]);
+      if (gl == G - 1) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+          if (rbase + i < a.rows) a.y[rbase + i] = acc[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) acc[i] = group_sum_last<64>(acc[i]);
+      const int slot = n % kSlots;
+      if ((tid & 63) == 63) {
+#pragma unroll
+        for (int i = 0; i < RB; ++i) ring[slot][tid >> 6][i] = acc[i];
+      }
+      if (slot == kSlots - 1) flush(n - (kSlots - 1), kSlots);
+    }
+    if constexpr (kQ8) load_rows<F, RB>(buf, a, nx * kRowsPerIter + grp * RB, unit_ld);
+  }
+  if constexpr (G > 64) {
+    const int used = n % kSlots;
+    if (used) flush(n - used, used);
   }
 }
 
@@ -265,12 +303,13 @@ hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s) {
   const int64_t iters = ((int64_t)a.rows + kRowsPerIter - 1) / kRowsPerIter;
   // As many workgroups as can be resident at once (4 per CU at <= 128
   // VGPRs, else 2); each loops over row batches.
-  const int64_t cap = (int64_t)cus * (RB == 1 ? GQ_GEMV_WG_PER_CU_RB1 : GQ_GEMV_WG_PER_CU_RBN);
+  constexpr bool kQ8 = std::is_same<typename F::Base, Q8Unit>::value;
+  const int64_t cap = (int64_t)cus * (RB == 1 ? GQ_GEMV_WG_PER_CU_RB1 : kQ8 ? GQ_GEMV_Q8_WG_PER_CU : GQ_GEMV_WG_PER_CU_RBN);
   const int blocks = (int)(iters < cap ? iters : cap);
   if (a.units <= G)
-    hipLaunchKernelGGL((gemv_kernel<F, G, RB, GQ_GEMV_NB>), dim3(blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<F, G, RB>), dim3(blocks), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((gemv_seg_kernel<F, G, RB>), dim3(blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemv_seg_kernel<typename F::Base, G, RB>), dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -281,7 +320,8 @@ template <class F, int G>
 hipError_t with_g(const GemvArgs& a, int cus, hipStream_t s) {
   const int64_t groups_needed = (int64_t)cus * GQ_GEMV_RB1_WAVES_PER_CU * (G >= 64 ? 1 : 64 / G);
   if ((int64_t)a.rows < 2 * groups_needed) return launch_one<F, G, 1>(a, cus, s);
-  return launch_one<F, G, GQ_GEMV_RBN>(a, cus, s);
+  constexpr bool kQ8 = std::is_same<typename F::Base, Q8Unit>::value;
+  return launch_one<F, G, kQ8 ? GQ_GEMV_Q8_RBN : GQ_GEMV_RBN>(a, cus, s);
 }
 
 template <class F>

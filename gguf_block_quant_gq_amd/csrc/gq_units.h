@@ -11,6 +11,7 @@ namespace gq {
 
 // ------------------------------------------------------------- Q8_0 unit
 struct Q8Unit {
+  using Base = Q8Unit;
   static constexpr int kWeights = kQ8Weights;
   static constexpr int kPerUnitCols = 32;  // x columns per unit
   struct X {
@@ -101,6 +102,7 @@ struct Q8Unit {
 // where x_a, x_b are the unit's two 32-column x slices and X_a, X_b their
 // sums (kept per lane, next to the x values).
 struct Q4KUnit {
+  using Base = Q4KUnit;
   static constexpr int kPerBlock = 4;  // units per super-block
   static constexpr int kPerUnitCols = 64;  // x columns per unit
   struct X {
