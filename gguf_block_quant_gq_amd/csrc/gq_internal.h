@@ -47,4 +47,9 @@ hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s);
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
 hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s);
 
+// Stream-ordered scratch from a per-device pool (workspace.hip): the block is
+// usable by work enqueued on `s` after ws_alloc and before ws_free.
+hipError_t ws_alloc(size_t bytes, hipStream_t s, void** p);
+hipError_t ws_free(void* p, hipStream_t s);
+
 }  // namespace gq

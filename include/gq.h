@@ -23,10 +23,18 @@
  *     to sub-block j = 2g+h; w = (d*sc_j)*code - dmin*m_j.
  *
  * Ownership and threading
- *   All pointers are device pointers owned by the caller. The library never
- *   allocates, frees or keeps a pointer and needs no workspace. Its only
- *   global state is a per-device cache of device properties, filled once.
- *   Calls on different streams may run concurrently.
+ *   All pointers are device pointers owned by the caller; the library never
+ *   frees or keeps them. gq_dequant and gq_matvec use no memory beyond their
+ *   arguments. gq_matmul on the matrix cores (Q4_K, M >= 16) takes a
+ *   stream-ordered workspace from a library-owned HIP memory pool (one per
+ *   device, created on first use, memory kept until the process ends):
+ *   17472 * ceil(M/16) * ceil(cols/256) bytes of prepared activations,
+ *   plus 4 * M * rows bytes per extra split when the K range is split over
+ *   workgroups. It is allocated and released on the caller's stream, so the
+ *   call stays asynchronous and calls on different streams never share it;
+ *   an allocation failure returns GQ_ERR_DEVICE. Global state: that pool and
+ *   a per-device cache of device properties, each filled once. Calls on
+ *   different streams may run concurrently.
  *
  * Alignment
  *   Q8_0 W: 2-byte aligned (a row range of a Q8_0 tensor starts on any
@@ -105,8 +113,9 @@ int gq_matvec(int fmt, const void* W, int64_t rows, int64_t cols,
  * The batched form used for prompt chunks ("nurllama 0.18.1 API", model.nu
  * section: the matmuls run over up to 64 positions at once, each weight read
  * once per chunk). M < 16 streams W once with fp32 arithmetic; M >= 16 uses
- * the matrix cores. Same accuracy bound as gq_matvec. Asynchronous on
- * `stream`.
+ * the matrix cores for Q4_K (with the workspace described above) and the
+ * fp32 path for Q8_0. Same accuracy bound as gq_matvec; repeated calls give
+ * bit-identical results. Asynchronous on `stream`.
  */
 int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
               const float* X, int64_t M, float* Y, void* stream);
