@@ -251,22 +251,6 @@ __device__ __forceinline__ RowHead decode_head(u32x4 hd, int q) {
   return h;
 }
 
-// One 16-byte-per-lane direct load from a buffer into LDS: lane l's bytes
-// land at lds + 16 l (lds is wave-uniform). The LDS address-space cast only
-// exists for the GPU; the host pass of a kernel template never runs it.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
-#if __HIP_DEVICE_COMPILE__
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
-#endif
-}
-
-// s_waitcnt with only the vector-memory counter limited to n.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // Vector-memory operations a wave has issued after requesting the chunk
 // that step s (0..8) of a super-block reads, by the issue order of a step:
 // [s == 0: WR header loads] [U chunk loads, for 8 steps ahead] compute
@@ -295,13 +279,6 @@ __device__ __forceinline__ void wait_for_chunk(int s) {
 static_assert(after_chunk(0, 2, 4) == 30 && after_chunk(1, 2, 4) == 30 && after_chunk(2, 2, 4) == 34 &&
               after_chunk(8, 2, 4) == 30, "after_chunk");
 
-// A workgroup barrier that orders the compiler's memory accesses but adds
-// no wait of its own (the waits before it are explicit).
-__device__ __forceinline__ void bare_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
-
-// Keeps the compiler from moving memory operations across this point: the
-// explicit wait counts rely on the vector-memory issue order of the source.
-__device__ __forceinline__ void issue_fence() { __asm__ volatile("" ::: "memory"); }
 
 // The prepared x of one super-block arrives in 9 chunks: parts 0..7 the hi
 // and lo fragments of sub-block `part` for the WM m-tiles, part 8 their

@@ -60,6 +60,11 @@ constexpr int kThreads = 256;
 #define GQ_GEMV_RB1_WAVES_PER_CU 8
 #endif
 
+template <class F>
+constexpr bool is_q8() {
+  return std::is_same<typename F::Base, Q8Unit>::value || std::is_same<typename F::Base, Q8PairUnit>::value;
+}
+
 template <class F, int RB>
 __device__ __forceinline__ void load_rows(typename F::Raw (&raw)[RB], const GemvArgs& a,
                                           int rbase, int unit_ld) {
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   constexpr int kRowsPerIter = kGroups * RB;
   constexpr int kWavesPerGroup = G > 64 ? G / 64 : 1;
   constexpr int kSlots = 8;
-  constexpr bool kQ8 = std::is_same<typename F::Base, Q8Unit>::value;
+  constexpr bool kQ8 = is_q8<F>();
   __shared__ float ring[G > 64 ? kSlots : 1][kThreads / 64][RB];
 
   const int tid = threadIdx.x;
@@ -303,8 +308,8 @@ hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s) {
   const int64_t iters = ((int64_t)a.rows + kRowsPerIter - 1) / kRowsPerIter;
   // As many workgroups as can be resident at once (4 per CU at <= 128
   // VGPRs, else 2); each loops over row batches.
-  constexpr bool kQ8 = std::is_same<typename F::Base, Q8Unit>::value;
-  const int64_t cap = (int64_t)cus * (RB == 1 ? GQ_GEMV_WG_PER_CU_RB1 : kQ8 ? GQ_GEMV_Q8_WG_PER_CU : GQ_GEMV_WG_PER_CU_RBN);
+  constexpr bool kQ8 = is_q8<F>();
+  const int64_t cap = (int64_t)cus * (kQ8 ? GQ_GEMV_Q8_WG_PER_CU : RB == 1 ? GQ_GEMV_WG_PER_CU_RB1 : GQ_GEMV_WG_PER_CU_RBN);
   const int blocks = (int)(iters < cap ? iters : cap);
   if (a.units <= G)
     hipLaunchKernelGGL((gemv_kernel<F, G, RB>), dim3(blocks), dim3(kThreads), 0, s, a);
@@ -320,7 +325,7 @@ template <class F, int G>
 hipError_t with_g(const GemvArgs& a, int cus, hipStream_t s) {
   const int64_t groups_needed = (int64_t)cus * GQ_GEMV_RB1_WAVES_PER_CU * (G >= 64 ? 1 : 64 / G);
   if ((int64_t)a.rows < 2 * groups_needed) return launch_one<F, G, 1>(a, cus, s);
-  constexpr bool kQ8 = std::is_same<typename F::Base, Q8Unit>::value;
+  constexpr bool kQ8 = is_q8<F>();
   return launch_one<F, G, kQ8 ? GQ_GEMV_Q8_RBN : GQ_GEMV_RBN>(a, cus, s);
 }
 
@@ -340,7 +345,13 @@ hipError_t dispatch(const GemvArgs& a, int cus, hipStream_t s) {
 
 hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s) {
   if (fmt == kFmtQ8_0) {
-    a.units = (a.cols + 31) / 32;
+    const int blocks = (a.cols + 31) / 32;
+    // an even block count keeps every row 4-byte aligned: pairs of blocks
+    if (blocks % 2 == 0 && (uintptr_t)a.W % 4 == 0) {
+      a.units = blocks / 2;
+      return dispatch<Q8PairUnit>(a, cus, s);
+    }
+    a.units = blocks;
     return dispatch<Q8Unit>(a, cus, s);
   }
   a.units = 4 * ((a.cols + 255) / 256);

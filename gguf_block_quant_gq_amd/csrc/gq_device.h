@@ -214,4 +214,34 @@ __device__ __forceinline__ float group_sum_last(float v) {
   return v;
 }
 
+// ------------------------------------------- direct global-to-LDS loads --
+// The streaming kernels move data straight from a buffer into LDS and wait
+// for it with explicit vector-memory counts: that counter retires in order,
+// so a wave waits for a given load with vmcnt(N), N = the number of vector
+// memory operations it issued after that load.
+
+// One 16-byte-per-lane direct load from a buffer into LDS: lane l's bytes
+// land at lds + 16 l (lds is wave-uniform). The LDS address-space cast only
+// exists for the GPU; the host pass of a kernel template never runs it.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
+// s_waitcnt with only the vector-memory counter limited to n.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A workgroup barrier that orders the compiler's memory accesses but adds
+// no wait of its own (the waits before it are explicit).
+__device__ __forceinline__ void bare_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
+
+// Keeps the compiler from moving memory operations across this point: the
+// explicit wait counts rely on the vector-memory issue order of the source.
+__device__ __forceinline__ void issue_fence() { __asm__ volatile("" ::: "memory"); }
+
 }  // namespace gq

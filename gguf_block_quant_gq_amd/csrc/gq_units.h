@@ -92,6 +92,86 @@ struct Q8Unit {
   }
 };
 
+// -------------------------------------------------------- Q8_0 pair unit
+// Two consecutive Q8_0 blocks (68 bytes = 17 dwords), used when every row
+// starts on a 4-byte boundary (even block count, 4-byte aligned W): the lane
+// loads them with four 16-byte loads and one 4-byte load, both scales
+// included (first block: d in bytes 0-1, codes in 2..33; second block: d in
+// bytes 34-35, codes in 36..67, dword aligned). Columns 64 u .. 64 u + 63.
+struct Q8PairUnit {
+  using Base = Q8PairUnit;
+  static constexpr int kPerUnitCols = 64;
+  struct X {
+    float v[64];
+  };
+  struct Raw {
+    uint32_t w[17];
+  };
+  struct Lane {};
+
+  __device__ static Lane lane(int) { return Lane{}; }
+
+  __device__ static bool valid(int unit, int units, int) { return unit < units; }
+
+  __device__ static void load_x(X& x, const float* xv, int unit, int cols) {
+    const int c0 = unit * 64;
+    if (c0 + 64 <= cols) {
+#pragma unroll
+      for (int i = 0; i < 64; i += 4) {
+        const f32x4 t = load_f32x4(xv + c0 + i);
+        x.v[i] = t.x; x.v[i + 1] = t.y; x.v[i + 2] = t.z; x.v[i + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) x.v[i] = (c0 + i < cols) ? xv[c0 + i] : 0.f;
+    }
+  }
+
+  __device__ static void zero_x(X& x) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x.v[i] = 0.f;
+  }
+
+  __device__ static void finish_x(X&) {}
+
+  static constexpr int kChunks = 16;
+  __device__ static void set_x(X& x, const f32x4 (&c)[kChunks]) {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      x.v[4 * k] = c[k].x; x.v[4 * k + 1] = c[k].y; x.v[4 * k + 2] = c[k].z; x.v[4 * k + 3] = c[k].w;
+    }
+  }
+
+  __device__ static void load(Raw& raw, const uint8_t* row, int unit) {
+    const uint8_t* p = row + (int64_t)unit * (2 * kQ8Bytes);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const u32x4 v = load_u32x4(p + 16 * k);
+      raw.w[4 * k] = v.x; raw.w[4 * k + 1] = v.y; raw.w[4 * k + 2] = v.z; raw.w[4 * k + 3] = v.w;
+    }
+    raw.w[16] = load_u32(p + 64);
+  }
+
+  __device__ static void zero(Raw& raw) {
+#pragma unroll
+    for (int k = 0; k < 17; ++k) raw.w[k] = 0u;
+  }
+
+  __device__ static float dot(const Raw& raw, const X& x, const Lane&) {
+    uint32_t q0[8], q1[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      q0[k] = __builtin_amdgcn_alignbyte(raw.w[k + 1], raw.w[k], 2);
+      q1[k] = raw.w[9 + k];
+    }
+    const float s0 = q8_block_dot(q0, x.v);
+    const float s1 = q8_block_dot(q1, x.v + 32);
+    const float d0 = half_bits_to_float(raw.w[0] & 0xFFFFu);
+    const float d1 = half_bits_to_float(raw.w[8] >> 16);
+    return __builtin_fmaf(d1, s1, d0 * s0);
+  }
+};
+
 // ------------------------------------------------------------- Q4_K unit
 // Unit = the 32 code bytes of group g (0..3) of super-block sb: byte l holds
 // the code of weight 64g + l in its low nibble (sub-block 2g) and of weight

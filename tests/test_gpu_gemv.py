@@ -68,6 +68,19 @@ def test_edge_shapes(gq, oracle, fmt, rows, cols):
     _check(gq, oracle, fmt, W, rows, cols, x, "edge")
 
 
+@pytest.mark.parametrize("rows,cols", [
+    (8193, 64), (8200, 250), (9001, 576), (8197, 1004), (8200, 2048), (8197, 4096), (9000, 96),
+])
+def test_q8_0_tall_matrices(gq, oracle, rows, cols):
+    """Tall Q8_0 matrices: an even number of blocks per row runs on block
+    pairs (row group widths 4..64 lanes), an odd one (96 columns) on single
+    blocks. Ragged rows and columns."""
+    rng = synth.rng_for(210, rows * 100000 + cols)
+    W = synth.weights(8, rows, cols, rng)
+    x = synth.activations(cols, rng)
+    _check(gq, oracle, 8, W, rows, cols, x, "tall q8_0")
+
+
 def test_q8_0_row_range_at_two_byte_offset(gq, oracle):
     rows, cols = 50, 160                       # 5 blocks per row: odd
     W = synth.weights(8, rows + 1, cols, synth.rng_for(9, 9))
