@@ -9,8 +9,11 @@
 // whatever the compiler contracts. fp16 scales are converted with the
 // hardware conversion, which keeps fp16 subnormals.
 //
-// One thread per unit (a Q8_0 block or a 16-byte Q4_K code chunk); the
-// kernel is bound by the fp32 writes (4 B out per <= 1.07 B in).
+// One wave per 256 consecutive outputs of a row (a Q4_K super-block, or
+// eight Q8_0 blocks): lane l produces outputs 4l..4l+3, so every wave store
+// writes one contiguous kilobyte, with non-temporal stores (the kernel is
+// bound by the fp32 writes, 4 B out per <= 1.07 B in), and the wave's loads
+// stay inside one 144- or 272-byte span of the row.
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -19,94 +22,86 @@ namespace gq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 
-__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d, bool vec) {
-  if (vec) {
-    f32x4 v = {a, b, c, d};
-    *(f32x4*)p = v;
+// Store the lane's 4 outputs at o (column c0 of a row of `cols`).
+template <bool VEC>
+__device__ __forceinline__ void store_quad(float* o, int c0, int cols, float a, float b, float c, float d) {
+  if (VEC && c0 + 4 <= cols) {
+    const f32x4 v = {a, b, c, d};
+    __builtin_nontemporal_store(v, (f32x4*)o);  // streamed out, never re-read here
   } else {
-    p[0] = a; p[1] = b; p[2] = c; p[3] = d;
+    if (c0 < cols) o[0] = a;
+    if (c0 + 1 < cols) o[1] = b;
+    if (c0 + 2 < cols) o[2] = c;
+    if (c0 + 3 < cols) o[3] = d;
   }
 }
 
+// Wave item = (row, 8-block group). Lane l: block 8 gi + (l >> 3), codes
+// 4 (l & 7) .. +3 of it, i.e. bytes 2 + 4 (l & 7) .. +3 of the block.
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void dequant_q8_0_kernel(DequantArgs a) {
-  const int64_t total = a.rows * (int64_t)a.units;
-  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < total;
-       u += (int64_t)gridDim.x * kThreads) {
-    const int64_t row = u / a.units;
-    const int j = (int)(u - row * a.units);
-    Q8Raw raw;
-    q8_load(a.W + row * a.row_bytes + (int64_t)j * kQ8Bytes, raw);
-    uint32_t q[8];
-    q8_codes(raw, q);
-    const float d = half_bits_to_float(raw.d16);
-    const int c0 = j * kQ8Weights;
+  const int lane = threadIdx.x & 63;
+  const int groups = (a.units + 7) / 8;
+  const int64_t items = a.rows * (int64_t)groups;
+  for (int64_t it = blockIdx.x * (int64_t)kWaves + (threadIdx.x >> 6); it < items;
+       it += (int64_t)gridDim.x * kWaves) {
+    const int64_t row = it / groups;
+    const int gi = (int)(it - row * groups);
+    const int blk = 8 * gi + (lane >> 3);
+    const int c0 = blk * kQ8Weights + 4 * (lane & 7);
+    if (c0 >= a.cols) continue;
+    const uint8_t* p = a.W + row * a.row_bytes + (int64_t)blk * kQ8Bytes;
+    const float d = half_bits_to_float(load_u16(p));
+    const uint8_t* cp = p + 2 + 4 * (lane & 7);  // 2-byte aligned
+    const uint32_t q = load_u16(cp) | (load_u16(cp + 2) << 16);
     float* o = a.out + row * a.cols + c0;
-    if (c0 + kQ8Weights <= a.cols) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        store4(o + 4 * k, d * i8_at(q[k], 0), d * i8_at(q[k], 1), d * i8_at(q[k], 2),
-               d * i8_at(q[k], 3), VEC);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kQ8Weights; ++i)
-        if (c0 + i < a.cols) o[i] = d * i8_at(q[i >> 2], i & 3);
-    }
+    store_quad<VEC>(o, c0, a.cols, d * i8_at(q, 0), d * i8_at(q, 1), d * i8_at(q, 2), d * i8_at(q, 3));
   }
 }
 
+// Wave item = (row, super-block). Lane l: sub-block j = l >> 3, outputs
+// 32 j + 4 (l & 7) .. +3, whose codes are the low (j even) or high (j odd)
+// nibbles of code bytes 32 (j >> 1) + 4 (l & 7) .. +3: one dword.
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void dequant_q4_k_kernel(DequantArgs a) {
-  const int64_t total = a.rows * (int64_t)a.units;
-  for (int64_t u = blockIdx.x * (int64_t)kThreads + threadIdx.x; u < total;
-       u += (int64_t)gridDim.x * kThreads) {
-    const int64_t row = u / a.units;
-    const int k = (int)(u - row * a.units);
-    const int sb = k >> 3, c = k & 7, g = c >> 1, t = c & 1;
-    const int c0 = sb * kQ4KWeights + 64 * g + 16 * t;
+  const int lane = threadIdx.x & 63;
+  const int nsb = a.units;
+  const int64_t items = a.rows * (int64_t)nsb;
+  const int j = lane >> 3, g = j >> 1, h = j & 1;
+  for (int64_t it = blockIdx.x * (int64_t)kWaves + (threadIdx.x >> 6); it < items;
+       it += (int64_t)gridDim.x * kWaves) {
+    const int64_t row = it / nsb;
+    const int sb = (int)(it - row * nsb);
+    const int c0 = sb * kQ4KWeights + 4 * lane;
     if (c0 >= a.cols) continue;
     const uint8_t* blk = a.W + row * a.row_bytes + (int64_t)sb * kQ4KBytes;
-    const u32x4 h = load_u32x4(blk);
-    const u32x4 v = load_u32x4(blk + 16 + 16 * c);
+    const u32x4 hd = load_u32x4(blk);
+    const uint32_t w = load_u32(blk + 16 + 32 * g + 4 * (lane & 7));
     uint32_t sc[2], m[2];
-    q4k_scales(q4k_scale_sel(g), h.y, h.z, h.w, sc, m);
-    const float d = half_bits_to_float(h.x & 0xFFFFu);
-    const float dmin = half_bits_to_float(h.x >> 16);
-    const float A0 = d * (float)sc[0], A1 = d * (float)sc[1];      // exact
-    const float B0 = dmin * (float)m[0], B1 = dmin * (float)m[1];  // exact
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float lo[16], hi[16];
+    q4k_scales(q4k_scale_sel(g), hd.y, hd.z, hd.w, sc, m);
+    const float d = half_bits_to_float(hd.x & 0xFFFFu);
+    const float dmin = half_bits_to_float(hd.x >> 16);
+    const float A = d * (float)sc[h];     // exact
+    const float B = dmin * (float)m[h];   // exact
+    const uint32_t n = (h ? w >> 4 : w) & 0x0F0F0F0Fu;
+    float v[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t byte = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-      lo[i] = A0 * (float)(byte & 15u) - B0;
-      hi[i] = A1 * (float)(byte >> 4) - B1;
-    }
+    for (int e = 0; e < 4; ++e) v[e] = A * (float)((n >> (8 * e)) & 0xFFu) - B;
     float* o = a.out + row * a.cols + c0;
-    if (c0 + 48 <= a.cols) {
-#pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        store4(o + i, lo[i], lo[i + 1], lo[i + 2], lo[i + 3], VEC);
-        store4(o + 32 + i, hi[i], hi[i + 1], hi[i + 2], hi[i + 3], VEC);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (c0 + i < a.cols) o[i] = lo[i];
-        if (c0 + 32 + i < a.cols) o[32 + i] = hi[i];
-      }
-    }
+    store_quad<VEC>(o, c0, a.cols, v[0], v[1], v[2], v[3]);
   }
 }
 
 }  // namespace
 
 hipError_t launch_dequant(int fmt, DequantArgs a, hipStream_t s) {
-  a.units = fmt == kFmtQ8_0 ? (a.cols + 31) / 32 : 8 * ((a.cols + 255) / 256);
-  const int64_t total = a.rows * (int64_t)a.units;
-  int64_t blocks = (total + kThreads - 1) / kThreads;
-  if (blocks > 16384) blocks = 16384;
+  // units per row: Q8_0 blocks, or Q4_K super-blocks
+  a.units = fmt == kFmtQ8_0 ? (a.cols + 31) / 32 : (a.cols + 255) / 256;
+  const int64_t items = a.rows * (int64_t)(fmt == kFmtQ8_0 ? (a.units + 7) / 8 : a.units);
+  int64_t blocks = (items + kWaves - 1) / kWaves;
+  if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   const bool vec = (a.cols % 4 == 0) && (((uintptr_t)a.out & 15) == 0);
   dim3 grid((unsigned)blocks), block(kThreads);

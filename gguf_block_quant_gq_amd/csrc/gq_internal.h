@@ -26,7 +26,7 @@ struct DequantArgs {
   int64_t row_bytes;
   int64_t rows;
   int cols;
-  int units;  // per row: Q8_0 blocks or Q4_K 16-byte chunks (set by the launcher)
+  int units;  // per row: Q8_0 blocks or Q4_K super-blocks (set by the launcher)
 };
 
 struct GemmArgs {
