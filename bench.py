@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+SMALL_M = (4, 8)               # few activation rows (padded to 16 on the matrix cores)
 
 
 def log(msg: str) -> None:
@@ -310,9 +311,10 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
                          GBps=round(b / (ms * 1e-3) / 1e9, 1))
     log(f"small shapes: { {k: v for k, v in out.items() if 'q4_k' in k or 'smollm' in k} }")
 
-    # prefill GEMM at the Llama-3-8B shapes
+    # Q4_K products with a few (M = 4, 8) and many activation rows at the
+    # Llama-3-8B prefill shapes (matrix cores)
     for which in ("gate", "down"):
-        for M in synth.PREFILL_M:
+        for M in SMALL_M + synth.PREFILL_M:
             W, X, rows, cols = synth.prefill_inputs(which, M)
             Wd, Xd = torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda()
             Yd = torch.empty((M, rows), dtype=torch.float32, device="cuda")
@@ -326,11 +328,13 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
             flops = 2.0 * M * rows * cols
             wb = rows * gq.gq_row_bytes(12, cols) + 4 * M * (rows + cols)
             tf = flops / (ms * 1e-3) / 1e12
-            out[f"prefill_{which}_M{M}"] = dict(
+            key = f"matmul_{which}_M{M}"
+            out[key] = dict(
                 us_per_call=round(ms * 1e3, 1), TFLOPs=round(tf, 2),
                 pct_mfma_f16_peak=round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2),
-                GBps=round(wb / (ms * 1e-3) / 1e9, 1))
-            log(f"prefill {which} M={M}: {out[f'prefill_{which}_M{M}']}")
+                GBps=round(wb / (ms * 1e-3) / 1e9, 1),
+                pct_hbm=round(100 * wb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2))
+            log(f"matmul {which} M={M}: {out[key]}")
     return out
 
 

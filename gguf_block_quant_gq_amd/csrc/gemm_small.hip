@@ -1,4 +1,4 @@
-// gemm_small.hip -- Y = X W^T for a handful of activation rows (M < 16).
+// gemm_small.hip -- Y = X W^T for Q8_0 weights and several activation rows.
 //
 // The prompt-chunk form of the product ("nurllama 0.18.1 API", model.nu
 // section: the matmuls run over several positions at once so each weight is
@@ -9,8 +9,10 @@
 // L2: M * cols * 4 bytes). Accumulators are kept per (row, m) and folded
 // across the group at the end, in a fixed order.
 //
-// W is streamed from HBM once per tile of kMaxM activation rows, so for
-// M < 16 exactly once.
+// W is streamed from HBM once per tile of kMaxM activation rows. (Q4_K
+// products with M >= 2 run on the matrix cores instead, which was measured
+// faster: this kernel re-reads every activation row for each batch of weight
+// rows, from L2.)
 #include "gq_device.h"
 #include "gq_internal.h"
 #include "gq_units.h"
@@ -143,13 +145,11 @@ hipError_t dispatch(const GemmArgs& a, int max_blocks, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s) {
-  const int max_blocks = cus * 4;
-  if (fmt == kFmtQ8_0) {
-    a.units = (a.cols + 31) / 32;
-    return dispatch<Q8Unit, 2>(a, max_blocks, s);
-  }
-  a.units = 4 * ((a.cols + 255) / 256);
-  return dispatch<Q4KUnit, 1>(a, max_blocks, s);
+  // Q8_0 only: Q4_K products with several activation rows run on the
+  // matrix cores (gemm_mfma.hip).
+  if (fmt != kFmtQ8_0) return hipErrorInvalidValue;
+  a.units = (a.cols + 31) / 32;
+  return dispatch<Q8Unit, 2>(a, cus * 4, s);
 }
 
 }  // namespace gq

@@ -133,9 +133,16 @@ extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, con
   const int cus = current_cus();
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
+  // One activation row is the matvec (same rounding, its kernel). Q4_K with
+  // two or more rows runs on the matrix cores: padded to 16 rows it was
+  // measured faster than the fp32 few-row kernel from M = 2 on (the latter
+  // re-reads each activation row per weight-row batch). Q8_0 keeps the fp32
+  // kernel for M >= 2.
+  if (M == 1) {
+    gq::GemvArgs v{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
+    return finish(gq::launch_gemv(fmt, v, cus, (hipStream_t)stream));
+  }
   gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
-  // M >= 16 is a dense contraction: Q4_K runs on the matrix cores.
-  if (M >= 16 && fmt == GQ_FMT_Q4_K)
-    return finish(gq::launch_gemm_mfma(fmt, a, cus, (hipStream_t)stream));
+  if (fmt == GQ_FMT_Q4_K) return finish(gq::launch_gemm_mfma(fmt, a, cus, (hipStream_t)stream));
   return finish(gq::launch_gemm_small(fmt, a, cus, (hipStream_t)stream));
 }

@@ -336,50 +336,6 @@ struct Q4KUnit {
     const float ms = __builtin_fmaf(m[1], x.sb, m[0] * x.sa);
     return __builtin_fmaf(d, qs, -dmin * ms);
   }
-
-  // Decoded form, reused across several activation vectors: the unit's
-  // dequantised weights, w = (d*sc)*code - dmin*m rounded once (the codes
-  // are code * 2^-9 and the scale carries the 2^9, so every product is exact).
-  struct Dec {
-    float a[32], b[32];  // sub-block 2g, sub-block 2g + 1
-  };
-
-  __device__ static void decode(Dec& dec, const Raw& raw, const Lane& ln) {
-    float sc[2], m[2];
-    scales(raw, ln, sc, m);
-    const float d = half_bits_to_float(raw.h.x & 0xFFFFu) * kFp8CodeScale;
-    const float dmin = half_bits_to_float(raw.h.x >> 16);
-    const float fa = d * sc[0], fb = d * sc[1], ga = dmin * m[0], gb = dmin * m[1];
-    const uint32_t w[8] = {raw.q0.x, raw.q0.y, raw.q0.z, raw.q0.w,
-                           raw.q1.x, raw.q1.y, raw.q1.z, raw.q1.w};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t l4 = w[k] & 0x0F0F0F0Fu;
-      const uint32_t h4 = (w[k] >> 4) & 0x0F0F0F0Fu;
-      const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(l4, false);
-      const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(l4, true);
-      const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(h4, false);
-      const f32x2 e = __builtin_amdgcn_cvt_pk_f32_fp8(h4, true);
-      dec.a[4 * k] = __builtin_fmaf(fa, a.x, -ga);
-      dec.a[4 * k + 1] = __builtin_fmaf(fa, a.y, -ga);
-      dec.a[4 * k + 2] = __builtin_fmaf(fa, b.x, -ga);
-      dec.a[4 * k + 3] = __builtin_fmaf(fa, b.y, -ga);
-      dec.b[4 * k] = __builtin_fmaf(fb, c.x, -gb);
-      dec.b[4 * k + 1] = __builtin_fmaf(fb, c.y, -gb);
-      dec.b[4 * k + 2] = __builtin_fmaf(fb, e.x, -gb);
-      dec.b[4 * k + 3] = __builtin_fmaf(fb, e.y, -gb);
-    }
-  }
-
-  __device__ static float dot_dec(const Dec& dec, const X& x) {
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      s0 = __builtin_fmaf(dec.a[i], x.a[i], s0);
-      s1 = __builtin_fmaf(dec.b[i], x.b[i], s1);
-    }
-    return s0 + s1;
-  }
 };
 
 }  // namespace gq

@@ -25,7 +25,7 @@
  * Ownership and threading
  *   All pointers are device pointers owned by the caller; the library never
  *   frees or keeps them. gq_dequant and gq_matvec use no memory beyond their
- *   arguments. gq_matmul on the matrix cores (Q4_K, M >= 16) takes a
+ *   arguments. gq_matmul on the matrix cores (Q4_K, M >= 2) takes a
  *   stream-ordered workspace from a library-owned HIP memory pool (one per
  *   device, created on first use, memory kept until the process ends):
  *   17472 * ceil(M/16) * ceil(cols/256) bytes of prepared activations,
@@ -112,10 +112,11 @@ int gq_matvec(int fmt, const void* W, int64_t rows, int64_t cols,
  * Y is overwritten. X: [M, cols] row-major fp32; Y: [M, rows] row-major fp32.
  * The batched form used for prompt chunks ("nurllama 0.18.1 API", model.nu
  * section: the matmuls run over up to 64 positions at once, each weight read
- * once per chunk). M < 16 streams W once with fp32 arithmetic; M >= 16 uses
- * the matrix cores for Q4_K (with the workspace described above) and the
- * fp32 path for Q8_0. Same accuracy bound as gq_matvec; repeated calls give
- * bit-identical results. Asynchronous on `stream`.
+ * once per chunk). M == 1 runs the gq_matvec kernel. Q4_K with M >= 2 runs
+ * on the matrix cores (with the workspace described above); Q8_0 with
+ * M >= 2 streams W once per 15 activation rows with fp32 arithmetic. Same
+ * accuracy bound as gq_matvec; repeated calls give bit-identical results.
+ * Asynchronous on `stream`.
  */
 int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
               const float* X, int64_t M, float* Y, void* stream);

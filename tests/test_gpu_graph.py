@@ -1,0 +1,60 @@
+"""gq_matvec inside a captured HIP graph (the form the decode-step
+benchmark times): the graph is replayed several times with new activations
+written eagerly between replays, and every replay must equal an eager call
+on the same inputs bit for bit (and the f64 oracle within tolerance)."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import assert_within_tolerance, oracle_threads, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+# (fmt, rows, cols): a Q4_K matrix with wide rows, a Q4_K one with short
+# ragged rows, the Q8_0 block-pair path and the single-block Q8_0 path
+SHAPES = [(12, 1024, 4096), (12, 300, 896), (8, 2000, 896), (8, 500, 96)]
+
+
+def test_graph_replays_match_eager(gq, oracle):
+    import torch
+
+    mats, xs, ys = [], [], []
+    for k, (fmt, rows, cols) in enumerate(SHAPES):
+        rng = synth.rng_for(800, k)
+        mats.append(to_dev(synth.weights(fmt, rows, cols, rng)))
+        xs.append(torch.empty(cols, dtype=torch.float32, device="cuda"))
+        ys.append(torch.empty(rows, dtype=torch.float32, device="cuda"))
+
+    def step():
+        for (fmt, rows, cols), W, x, y in zip(SHAPES, mats, xs, ys):
+            gq.gq_matvec(fmt, W, rows, cols, x, y=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for x in xs:
+            x.zero_()
+        step()  # warm up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+
+    for rep in range(3):
+        host_x = [synth.activations(cols, synth.rng_for(801 + rep, k))
+                  for k, (_, _, cols) in enumerate(SHAPES)]
+        for x, hx in zip(xs, host_x):
+            x.copy_(torch.from_numpy(hx))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [to_host(y).copy() for y in ys]
+        step()  # the same calls, eagerly
+        eager = [to_host(y) for y in ys]
+        print(f"[graph] replay {rep}", flush=True)
+        for k, (fmt, rows, cols) in enumerate(SHAPES):
+            assert np.array_equal(got[k].view(np.uint32), eager[k].view(np.uint32)), (rep, k)
+            Wh = to_host(mats[k])
+            ref, S = oracle.matvec(fmt, Wh, rows, cols, host_x[k], nthreads=oracle_threads())
+            assert_within_tolerance(got[k], ref, S, f"graph replay {rep} fmt={fmt} {rows}x{cols}")
