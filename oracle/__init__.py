@@ -1,4 +1,5 @@
-"""CPU oracle for GGUF Q8_0 / Q4_K dequant, matvec and small matmul.
+"""CPU oracle for GGUF Q8_0 / Q4_K / Q5_0 / Q5_K / Q6_K dequant, matvec and
+small matmul.
 
 TEST INFRASTRUCTURE ONLY. This package defines the values the GPU library
 must reproduce. Only the test-suite, the smoke check and the CPU-baseline leg
@@ -6,8 +7,9 @@ of ``bench.py`` may import it; the product path never does. It shares no
 code with ``gguf_block_quant_gq_amd``.
 
 The arithmetic lives in ``gq_oracle.c`` (plain C, ``-O2 -ffp-contract=off``):
-hand-decoded fp16, block unpack, fp32 dequant ``(d*sc)*q - dmin*m`` (Q4_K) or
-``d*q`` (Q8_0), and f64-accumulated sums. The page and section each step
+hand-decoded fp16, block unpack, fp32 dequant ``(d*sc)*q - dmin*m`` (Q4_K,
+Q5_K), ``(d*scale)*(q - 32)`` (Q6_K), ``d*(q - 16)`` (Q5_0) or ``d*q``
+(Q8_0), and f64-accumulated sums. The page and section each step
 follows are cited in that file.
 """
 from __future__ import annotations
@@ -24,6 +26,9 @@ _LIB = os.path.join(_HERE, "libgq_oracle.so")
 
 TYPE_Q8_0 = 8
 TYPE_Q4_K = 12
+TYPE_Q5_0 = 6
+TYPE_Q5_K = 13
+TYPE_Q6_K = 14
 
 _lib = None
 

@@ -23,6 +23,25 @@
  *        Weight i = 64g + 32h + l (g<4, h<2, l<32) is in sub-block j = 2g+h;
  *        its code is the low nibble of qs[32g+l] when h = 0, the high nibble
  *        when h = 1. w_i = (d*sc_j)*code - dmin*m_j.
+ *      Q5_0, 22 bytes per 32 weights: bytes 0-1 = d (fp16), 2-5 = a 32-bit
+ *        little-endian word qh holding bit 4 of every code (bit i for weight
+ *        i), 6..21 = sixteen bytes of low nibbles: weight i < 16 takes the
+ *        low nibble of byte i, weight 16 + i the high nibble of byte i.
+ *        code_i in 0..31, w_i = d * (code_i - 16).
+ *      Q5_K, 176 bytes per 256 weights: d, dmin and the twelve 6-bit scale
+ *        bytes exactly as in Q4_K (bytes 0..15), then 32 bytes qh (16..47),
+ *        then 128 bytes of low nibbles (48..175) placed as in Q4_K. Weight
+ *        i = 64g + 32h + l takes bit 2g + h of qh[l] as bit 4 of its code.
+ *        w_i = (d*sc_j)*code - dmin*m_j with code in 0..31.
+ *      Q6_K, 210 bytes per 256 weights: bytes 0..127 = low nibbles ql,
+ *        128..191 = high bit pairs qh, 192..207 = sixteen int8 scales (one per
+ *        16 consecutive weights), 208-209 = d (fp16). Weight
+ *        i = 128n + 32k + l (n<2, k<4, l<32): low four bits = nibble k>>1 of
+ *        ql[64n + 32(k&1) + l], high two bits = bits 2k..2k+1 of qh[32n + l];
+ *        code in 0..63, w_i = (d*scale_{i/16})*(code - 32).
+ *    Formats other than these are not decoded (the pages list Q5_K, Q6_K and
+ *    Q5_0 next to Q4_K: "nurllama" README, "What it runs"; "nurllama 0.18.1
+ *    API", kernels.nu section, its per-format kernel list).
  *  - Columns >= cols in a row's last block are ignored (a reading: GGUF
  *    itself only stores whole blocks per row).
  */
@@ -39,17 +58,34 @@ enum {
     O_Q8_0_BYTES = 34,
     O_Q4_K_WEIGHTS = 256,
     O_Q4_K_BYTES = 144,
+    O_Q5_0_WEIGHTS = 32,
+    O_Q5_0_BYTES = 22,
+    O_Q5_K_WEIGHTS = 256,
+    O_Q5_K_BYTES = 176,
+    O_Q6_K_WEIGHTS = 256,
+    O_Q6_K_BYTES = 210,
 };
+
+/* Weights and bytes of one block of `type`; 0 for an unknown type. */
+static int block_shape(int type, int* bytes)
+{
+    switch (type) {
+    case GQO_TYPE_Q8_0: *bytes = O_Q8_0_BYTES; return O_Q8_0_WEIGHTS;
+    case GQO_TYPE_Q4_K: *bytes = O_Q4_K_BYTES; return O_Q4_K_WEIGHTS;
+    case GQO_TYPE_Q5_0: *bytes = O_Q5_0_BYTES; return O_Q5_0_WEIGHTS;
+    case GQO_TYPE_Q5_K: *bytes = O_Q5_K_BYTES; return O_Q5_K_WEIGHTS;
+    case GQO_TYPE_Q6_K: *bytes = O_Q6_K_BYTES; return O_Q6_K_WEIGHTS;
+    default: *bytes = 0; return 0;
+    }
+}
 
 int64_t gqo_row_bytes(int type, int64_t cols)
 {
-    if (cols < 0)
+    int bytes;
+    int weights = block_shape(type, &bytes);
+    if (cols < 0 || weights == 0)
         return -1;
-    if (type == GQO_TYPE_Q8_0)
-        return ((cols + O_Q8_0_WEIGHTS - 1) / O_Q8_0_WEIGHTS) * O_Q8_0_BYTES;
-    if (type == GQO_TYPE_Q4_K)
-        return ((cols + O_Q4_K_WEIGHTS - 1) / O_Q4_K_WEIGHTS) * O_Q4_K_BYTES;
-    return -1;
+    return ((cols + weights - 1) / weights) * bytes;
 }
 
 /* ---------------------------------------------------------------- fp16 */
@@ -181,8 +217,96 @@ static void dequant_row_q4_k(const uint8_t* row, int64_t cols, float* out)
     }
 }
 
+static void dequant_row_q5_0(const uint8_t* row, int64_t cols, float* out)
+{
+    int64_t nb = (cols + O_Q5_0_WEIGHTS - 1) / O_Q5_0_WEIGHTS;
+    for (int64_t b = 0; b < nb; b++) {
+        const uint8_t* blk = row + b * O_Q5_0_BYTES;
+        float d = gqo_f16_to_f32(read_u16le(blk));
+        uint32_t qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) |
+                      ((uint32_t)blk[4] << 16) | ((uint32_t)blk[5] << 24);
+        const uint8_t* qs = blk + 6;
+        for (int i = 0; i < O_Q5_0_WEIGHTS; i++) {
+            int64_t c = b * O_Q5_0_WEIGHTS + i;
+            if (c >= cols)
+                break;
+            int lo = i < 16 ? (qs[i] & 0x0F) : (qs[i - 16] >> 4);
+            int code = lo | (int)(((qh >> i) & 1u) << 4);
+            out[c] = d * (float)(code - 16); /* exact: 11-bit x 5-bit */
+        }
+    }
+}
+
+static void dequant_row_q5_k(const uint8_t* row, int64_t cols, float* out)
+{
+    int64_t nb = (cols + O_Q5_K_WEIGHTS - 1) / O_Q5_K_WEIGHTS;
+    for (int64_t b = 0; b < nb; b++) {
+        const uint8_t* blk = row + b * O_Q5_K_BYTES;
+        float d = gqo_f16_to_f32(read_u16le(blk));
+        float dmin = gqo_f16_to_f32(read_u16le(blk + 2));
+        uint8_t sc[8], m[8];
+        gqo_q4_k_unpack_scales(blk + 4, sc, m);
+        const uint8_t* qh = blk + 16;
+        const uint8_t* qs = blk + 48;
+        for (int i = 0; i < O_Q5_K_WEIGHTS; i++) {
+            int64_t c = b * O_Q5_K_WEIGHTS + i;
+            if (c >= cols)
+                break;
+            int g = i / 64;
+            int h = (i / 32) % 2;
+            int l = i % 32;
+            int j = 2 * g + h;
+            uint8_t byte = qs[32 * g + l];
+            int lo = h ? (byte >> 4) : (byte & 0x0F);
+            int code = lo | (((qh[l] >> j) & 1) << 4);
+            float scale = d * (float)sc[j];  /* exact: 11-bit x 6-bit */
+            float minv = dmin * (float)m[j]; /* exact */
+            out[c] = scale * (float)code - minv; /* product exact (22 bits) */
+        }
+    }
+}
+
+static void dequant_row_q6_k(const uint8_t* row, int64_t cols, float* out)
+{
+    int64_t nb = (cols + O_Q6_K_WEIGHTS - 1) / O_Q6_K_WEIGHTS;
+    for (int64_t b = 0; b < nb; b++) {
+        const uint8_t* blk = row + b * O_Q6_K_BYTES;
+        const uint8_t* ql = blk;
+        const uint8_t* qh = blk + 128;
+        const int8_t* scales = (const int8_t*)(blk + 192);
+        float d = gqo_f16_to_f32(read_u16le(blk + 208));
+        for (int i = 0; i < O_Q6_K_WEIGHTS; i++) {
+            int64_t c = b * O_Q6_K_WEIGHTS + i;
+            if (c >= cols)
+                break;
+            int n = i / 128;
+            int k = (i / 32) % 4;
+            int l = i % 32;
+            uint8_t lbyte = ql[64 * n + 32 * (k & 1) + l];
+            int lo = (k >> 1) ? (lbyte >> 4) : (lbyte & 0x0F);
+            int hi = (qh[32 * n + l] >> (2 * k)) & 3;
+            int code = lo | (hi << 4);
+            float scale = d * (float)scales[i / 16]; /* exact: 11-bit x 8-bit */
+            /* exact: |d| significand x |scale*(code-32)| <= 2^11 x 2^12 */
+            out[c] = scale * (float)(code - 32);
+        }
+    }
+}
+
 static int dequant_row(int type, const uint8_t* row, int64_t cols, float* out)
 {
+    if (type == GQO_TYPE_Q5_0) {
+        dequant_row_q5_0(row, cols, out);
+        return 0;
+    }
+    if (type == GQO_TYPE_Q5_K) {
+        dequant_row_q5_k(row, cols, out);
+        return 0;
+    }
+    if (type == GQO_TYPE_Q6_K) {
+        dequant_row_q6_k(row, cols, out);
+        return 0;
+    }
     if (type == GQO_TYPE_Q8_0) {
         dequant_row_q8_0(row, cols, out);
         return 0;

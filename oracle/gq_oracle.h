@@ -1,5 +1,6 @@
 /*
- * gq_oracle.h -- CPU oracle for block-quantised (GGUF Q8_0 / Q4_K) dequant,
+ * gq_oracle.h -- CPU oracle for block-quantised (GGUF Q8_0 / Q4_K / Q5_0 /
+ * Q5_K / Q6_K) dequant,
  * matrix-vector and small matrix-matrix products.
  *
  * TEST INFRASTRUCTURE ONLY. This library defines what the GPU path must
@@ -14,9 +15,11 @@
  *  - same page, kernels.nu section, layout contract: W[out,in] row-major,
  *    y[r] = sum_c W[r*in + c] * x[c].
  *  - "nurllama" README, "What it runs": a row is a whole number of
- *    quantisation blocks; the formats Q8_0 and Q4_K are named.
- *  - The byte layouts of Q8_0 (34 B) and Q4_K (144 B) are not printed on the
- *    pages; the public GGUF definition is followed (see the .c file).
+ *    quantisation blocks; the formats Q8_0, Q4_K, Q5_0, Q5_K and Q6_K are
+ *    named there.
+ *  - The byte layouts of Q8_0 (34 B), Q4_K (144 B), Q5_0 (22 B), Q5_K (176 B)
+ *    and Q6_K (210 B) are not printed on the pages; the public GGUF
+ *    definitions are followed (see the .c file).
  *
  * Conventions: rows = output features, cols = input features. A row holds
  * ceil(cols / QK) blocks; codes at columns >= cols are ignored.
@@ -34,6 +37,9 @@ extern "C" {
 /* ggml tensor type ids accepted by the oracle. */
 #define GQO_TYPE_Q8_0 8
 #define GQO_TYPE_Q4_K 12
+#define GQO_TYPE_Q5_0 6
+#define GQO_TYPE_Q5_K 13
+#define GQO_TYPE_Q6_K 14
 
 /* Bytes of one row of `cols` input features, or -1 for an unknown type. */
 int64_t gqo_row_bytes(int type, int64_t cols);

@@ -1,7 +1,8 @@
 """Seeded synthetic inputs shared by the tests and the benchmark.
 
 This module draws random block fields and lays them out as packed GGUF bytes
-(Q8_0: 34 B per 32 weights, Q4_K: 144 B per 256 weights). It holds none of the
+(Q8_0: 34 B per 32 weights, Q4_K: 144 B, Q5_K: 176 B and Q6_K: 210 B per 256
+weights, Q5_0: 22 B per 32 weights). It holds none of the
 method's arithmetic: nothing here dequantises or multiplies. Both the oracle
 and the GPU library receive the very same bytes.
 
@@ -19,6 +20,16 @@ order is scales, then quants, then the activation vector):
   (a sub-block range of about 2 * 0.058 mapped onto 15 * 63 steps, and 0.058
   onto 63 steps); the other 140 bytes are uniform random, i.e. every 6-bit
   scale / min code is uniform on 0..63 and every 4-bit code on 0..15.
+* Q5_0: per block ``d = fp16(max|N(0, 0.02)| over 32 draws / 16)`` (drawn
+  as for Q8_0), then 20 uniform random bytes (every 5-bit code uniform on
+  0..31).
+* Q5_K: per super-block ``d = fp16(U[0.5, 1.5) * 5.9e-5)`` (2 * 0.058 onto
+  31 * 63 steps) and ``dmin = fp16(U[0.5, 1.5) * 9.2e-4)``, then 172 uniform
+  random bytes (scale / min codes, high bits and nibbles).
+* Q6_K: per super-block 208 uniform random bytes (nibbles, high bit pairs
+  and sixteen int8 scales uniform on -128..127), then
+  ``d = fp16(U[0.5, 1.5) * 1.4e-5)`` (0.058 onto 32 * 127 steps; like the
+  scales of real Q6_K tensors this lies in fp16's subnormal range).
 * Activations: ``standard_normal`` in float64, rounded to float32.
 """
 from __future__ import annotations
@@ -28,9 +39,13 @@ from scipy.special import erfinv
 
 FMT_Q8_0 = 8
 FMT_Q4_K = 12
+FMT_Q5_0 = 6
+FMT_Q5_K = 13
+FMT_Q6_K = 14
 
-_QK = {FMT_Q8_0: 32, FMT_Q4_K: 256}
-_BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4_K: 144}
+_QK = {FMT_Q8_0: 32, FMT_Q4_K: 256, FMT_Q5_0: 32, FMT_Q5_K: 256, FMT_Q6_K: 256}
+_BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4_K: 144, FMT_Q5_0: 22, FMT_Q5_K: 176,
+                FMT_Q6_K: 210}
 
 
 def blocks_per_row(fmt: int, cols: int) -> int:
@@ -82,11 +97,64 @@ def q4_k_weights(rows: int, cols: int, rng: np.random.Generator,
     return out.reshape(-1)
 
 
+def _random_fill(out: np.ndarray, c0: int, c1: int, rng: np.random.Generator,
+                 chunk_blocks: int = 1 << 22) -> None:
+    """Uniform random bytes into columns c0..c1-1 of a [blocks, bytes] array,
+    drawn in chunks of blocks so that no huge temporary is made."""
+    nblk = out.shape[0]
+    for b0 in range(0, nblk, chunk_blocks):
+        b1 = min(nblk, b0 + chunk_blocks)
+        out[b0:b1, c0:c1] = rng.integers(0, 256, size=(b1 - b0, c1 - c0), dtype=np.uint8)
+
+
+def _put_f16(out: np.ndarray, col: int, bits: np.ndarray) -> None:
+    out[:, col] = (bits & 0xFF).astype(np.uint8)
+    out[:, col + 1] = (bits >> 8).astype(np.uint8)
+
+
+def q5_0_weights(rows: int, cols: int, rng: np.random.Generator) -> np.ndarray:
+    """Packed Q5_0 bytes for a rows x cols matrix (flat uint8 array)."""
+    nblk = rows * blocks_per_row(FMT_Q5_0, cols)
+    u = rng.random(nblk)
+    amax = 0.02 * np.sqrt(2.0) * erfinv(u ** (1.0 / 32.0))
+    out = np.empty((nblk, 22), np.uint8)
+    _put_f16(out, 0, _fp16_bits(amax / 16.0))
+    _random_fill(out, 2, 22, rng)
+    return out.reshape(-1)
+
+
+def q5_k_weights(rows: int, cols: int, rng: np.random.Generator) -> np.ndarray:
+    """Packed Q5_K bytes for a rows x cols matrix (flat uint8 array)."""
+    nblk = rows * blocks_per_row(FMT_Q5_K, cols)
+    d16 = _fp16_bits(rng.uniform(0.5, 1.5, nblk) * 5.9e-5)
+    dmin16 = _fp16_bits(rng.uniform(0.5, 1.5, nblk) * 9.2e-4)
+    out = np.empty((nblk, 176), np.uint8)
+    _put_f16(out, 0, d16)
+    _put_f16(out, 2, dmin16)
+    _random_fill(out, 4, 176, rng)
+    return out.reshape(-1)
+
+
+def q6_k_weights(rows: int, cols: int, rng: np.random.Generator) -> np.ndarray:
+    """Packed Q6_K bytes for a rows x cols matrix (flat uint8 array)."""
+    nblk = rows * blocks_per_row(FMT_Q6_K, cols)
+    out = np.empty((nblk, 210), np.uint8)
+    _random_fill(out, 0, 208, rng)
+    _put_f16(out, 208, _fp16_bits(rng.uniform(0.5, 1.5, nblk) * 1.4e-5))
+    return out.reshape(-1)
+
+
 def weights(fmt: int, rows: int, cols: int, rng: np.random.Generator) -> np.ndarray:
     if fmt == FMT_Q8_0:
         return q8_0_weights(rows, cols, rng)
     if fmt == FMT_Q4_K:
         return q4_k_weights(rows, cols, rng)
+    if fmt == FMT_Q5_0:
+        return q5_0_weights(rows, cols, rng)
+    if fmt == FMT_Q5_K:
+        return q5_k_weights(rows, cols, rng)
+    if fmt == FMT_Q6_K:
+        return q6_k_weights(rows, cols, rng)
     raise ValueError(f"unknown format {fmt}")
 
 

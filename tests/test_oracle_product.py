@@ -21,6 +21,7 @@ def _exact(w_row: np.ndarray, x: np.ndarray) -> Fraction:
 
 @pytest.mark.parametrize("fmt,rows,cols", [
     (8, 1, 32), (8, 2, 64), (8, 3, 40), (12, 1, 256), (12, 2, 512), (12, 3, 300),
+    (6, 2, 64), (6, 3, 40), (13, 2, 512), (13, 3, 300), (14, 2, 512), (14, 3, 300),
 ])
 def test_brute_force_rational(oracle, fmt, rows, cols):
     rng = np.random.default_rng(fmt * 100 + rows)

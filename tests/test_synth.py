@@ -5,7 +5,8 @@ import synth
 
 
 def test_sizes_and_determinism():
-    for fmt, rows, cols in [(8, 5, 576), (12, 3, 896), (12, 2, 4864)]:
+    for fmt, rows, cols in [(8, 5, 576), (12, 3, 896), (12, 2, 4864), (6, 4, 896),
+                            (13, 3, 896), (14, 3, 4096)]:
         a = synth.weights(fmt, rows, cols, synth.rng_for(0, 1))
         b = synth.weights(fmt, rows, cols, synth.rng_for(0, 1))
         c = synth.weights(fmt, rows, cols, synth.rng_for(0, 2))
@@ -30,6 +31,34 @@ def test_q4_k_fields():
     assert dmin.min() >= 0.5 * 9.2e-4 * 0.999 and dmin.max() <= 1.5 * 9.2e-4 * 1.001
     # the 140 code bytes are uniform
     assert abs(W[:, 4:].mean() - 127.5) < 1.0
+
+
+def test_q5_0_fields():
+    W = synth.weights(6, 64, 896, synth.rng_for(0, 0)).reshape(-1, 22)
+    d = W[:, :2].copy().view(np.float16).astype(np.float64).ravel()
+    assert np.all(d > 0) and 2e-3 < np.median(d) < 5e-3   # ~0.02 * 2.4 / 16
+    assert abs(W[:, 2:].mean() - 127.5) < 1.5
+
+
+def test_q5_k_fields():
+    W = synth.weights(13, 256, 512, synth.rng_for(1, 0)).reshape(-1, 176)
+    d = W[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
+    dmin = W[:, 2:4].copy().view(np.float16).astype(np.float64).ravel()
+    assert d.min() >= 0.5 * 5.9e-5 * 0.999 and d.max() <= 1.5 * 5.9e-5 * 1.001
+    assert dmin.min() >= 0.5 * 9.2e-4 * 0.999 and dmin.max() <= 1.5 * 9.2e-4 * 1.001
+    assert abs(W[:, 4:].mean() - 127.5) < 1.0
+
+
+def test_q6_k_fields():
+    W = synth.weights(14, 256, 512, synth.rng_for(1, 0)).reshape(-1, 210)
+    d = W[:, 208:210].copy().view(np.float16).astype(np.float64).ravel()
+    # d lies in fp16's subnormal range (spacing 2^-24), as real Q6_K scales do
+    ulp = 2.0 ** -24
+    assert d.min() >= 0.5 * 1.4e-5 - ulp and d.max() <= 1.5 * 1.4e-5 + ulp
+    assert np.all(d < 2.0 ** -14)
+    sc = W[:, 192:208].view(np.int8)
+    assert sc.min() == -128 and sc.max() == 127
+    assert abs(W[:, :208].mean() - 127.5) < 1.0
 
 
 def test_prefill_weights_are_decode_layer0():
