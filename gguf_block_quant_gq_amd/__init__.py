@@ -10,7 +10,8 @@ is no CPU fallback: if the library is not built, loading raises.
     gq_matmul(fmt, W, rows, cols, X, Y=None)           -> Y [M, rows] fp32
 
 W is a uint8 CUDA tensor holding rows * gq_row_bytes(fmt, cols) bytes of
-GGUF blocks; fmt is FMT_Q8_0 (8) or FMT_Q4_K (12).
+GGUF blocks; fmt is FMT_Q8_0 (8), FMT_Q4_K (12), FMT_Q5_0 (6), FMT_Q5_K (13)
+or FMT_Q6_K (14).
 """
 from __future__ import annotations
 
@@ -22,6 +23,9 @@ LIB_PATH = os.path.join(HERE, "libgq.so")
 
 FMT_Q8_0 = 8
 FMT_Q4_K = 12
+FMT_Q5_0 = 6
+FMT_Q5_K = 13
+FMT_Q6_K = 14
 
 GQ_OK = 0
 GQ_ERR_NULL = 1

@@ -1,4 +1,5 @@
-// gemm_small.hip -- Y = X W^T for Q8_0 weights and several activation rows.
+// gemm_small.hip -- Y = X W^T for several activation rows and Q8_0, Q5_0,
+// Q5_K or Q6_K weights.
 //
 // The prompt-chunk form of the product ("nurllama 0.18.1 API", model.nu
 // section: the matmuls run over several positions at once so each weight is
@@ -145,11 +146,24 @@ hipError_t dispatch(const GemmArgs& a, int max_blocks, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s) {
-  // Q8_0 only: Q4_K products with several activation rows run on the
-  // matrix cores (gemm_mfma.hip).
-  if (fmt != kFmtQ8_0) return hipErrorInvalidValue;
-  a.units = (a.cols + 31) / 32;
-  return dispatch<Q8Unit, 2>(a, cus * 4, s);
+  // Q4_K products with several activation rows run on the matrix cores
+  // (gemm_mfma.hip); every other format streams W here.
+  switch (fmt) {
+    case kFmtQ8_0:
+      a.units = (a.cols + 31) / 32;
+      return dispatch<Q8Unit, 2>(a, cus * 4, s);
+    case kFmtQ5_0:
+      a.units = (a.cols + 31) / 32;
+      return dispatch<Q5_0Unit, 2>(a, cus * 4, s);
+    case kFmtQ5_K:
+      a.units = 4 * ((a.cols + 255) / 256);
+      return dispatch<Q5KUnit, 1>(a, cus * 4, s);
+    case kFmtQ6_K:
+      a.units = 4 * ((a.cols + 255) / 256);
+      return dispatch<Q6KUnit, 1>(a, cus * 4, s);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace gq

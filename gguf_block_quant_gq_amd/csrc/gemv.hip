@@ -1,4 +1,5 @@
-// gemv.hip -- y = W x for GGUF Q8_0 / Q4_K weights on gfx950.
+// gemv.hip -- y = W x for GGUF Q8_0 / Q4_K / Q5_0 / Q5_K / Q6_K weights on
+// gfx950.
 //
 // The decode-step matrix-vector product is bound by the bytes of W
 // (nx_f32_llm_v4 source, model binder: decode is memory-bandwidth bound, so
@@ -7,9 +8,9 @@
 //
 // Work decomposition ("row groups"): the 256 threads of a workgroup form
 // 256/G groups of G lanes (G a power of two, 4..256). A group owns RB rows at
-// a time; its lanes split each row into units -- a Q8_0 block (32 weights,
-// 34 B) or the 32 code bytes of one Q4_K sub-block pair (64 weights) -- lane
-// l owning unit l. Because a lane always owns the same unit, that unit's x
+// a time; its lanes split each row into units -- a Q8_0 or Q5_0 block (32
+// weights), a pair of Q8_0 blocks, or a quarter of a K-quant super-block (64
+// weights; gq_units.h) -- lane l owning unit l. Because a lane always owns the same unit, that unit's x
 // values are loaded once into registers and reused for every row the group
 // visits. Consecutive lanes own consecutive units, so each load instruction
 // of a wave reads one contiguous span of a row.
@@ -168,7 +169,7 @@ __device__ __forceinline__ void fetch_x(typename F::X& xr, const f32x4* xs, int 
   constexpr int C = F::kChunks;
   f32x4 c[C];
 #pragma unroll
-  for (int k = 0; k < C; ++k) c[k] = xs[x_slot<F, G>(C * gl + k)];
+  for (int k = 0; k < C; ++k) c[k] = xs[x_slot<F, G>(F::x_chunk(gl, k))];
   F::set_x(xr, c);
   F::finish_x(xr);
 }
@@ -354,7 +355,14 @@ hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s) {
     a.units = blocks;
     return dispatch<Q8Unit>(a, cus, s);
   }
+  if (fmt == kFmtQ5_0) {
+    a.units = (a.cols + 31) / 32;
+    return dispatch<Q5_0Unit>(a, cus, s);
+  }
+  // K-quants: four units per 256-weight super-block
   a.units = 4 * ((a.cols + 255) / 256);
+  if (fmt == kFmtQ5_K) return dispatch<Q5KUnit>(a, cus, s);
+  if (fmt == kFmtQ6_K) return dispatch<Q6KUnit>(a, cus, s);
   return dispatch<Q4KUnit>(a, cus, s);
 }
 

@@ -42,7 +42,7 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 // Shape and format checks shared by every entry point. On success *rb is
 // the row stride in bytes and *wbytes the size of W.
 int check_shape(int fmt, int64_t rows, int64_t cols, int64_t M, int64_t* rb, int64_t* wbytes) {
-  if (fmt != GQ_FMT_Q8_0 && fmt != GQ_FMT_Q4_K) return GQ_ERR_FMT;
+  if (gq_row_bytes(fmt, 1) < 0) return GQ_ERR_FMT;
   if (rows < 0 || cols <= 0 || M < 0) return GQ_ERR_SHAPE;
   if (rows > INT_MAX || cols > INT_MAX || M > INT_MAX) return GQ_ERR_SHAPE;
   *rb = gq_row_bytes(fmt, cols);
@@ -52,8 +52,12 @@ int check_shape(int fmt, int64_t rows, int64_t cols, int64_t M, int64_t* rb, int
   return GQ_OK;
 }
 
+// Formats whose block size is not a multiple of 4 bytes (Q8_0 34, Q5_0 22,
+// Q6_K 210) take 2-byte aligned W, so that a row range starting at any
+// block boundary is accepted; Q4_K and Q5_K blocks (144, 176 B) take 4.
 int check_align(int fmt, const void* W) {
-  uintptr_t need = fmt == GQ_FMT_Q8_0 ? 2 : 4;
+  const bool two = fmt == GQ_FMT_Q8_0 || fmt == GQ_FMT_Q5_0 || fmt == GQ_FMT_Q6_K;
+  const uintptr_t need = two ? 2 : 4;
   return ((uintptr_t)W % need) ? GQ_ERR_ALIGN : GQ_OK;
 }
 
@@ -63,9 +67,14 @@ int finish(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_DEVICE; }
 
 extern "C" int64_t gq_row_bytes(int fmt, int64_t cols) {
   if (cols < 0 || cols > INT64_MAX - 256) return -1;
-  if (fmt == GQ_FMT_Q8_0) return ((cols + 31) / 32) * 34;
-  if (fmt == GQ_FMT_Q4_K) return ((cols + 255) / 256) * 144;
-  return -1;
+  switch (fmt) {
+    case GQ_FMT_Q8_0: return ((cols + 31) / 32) * 34;
+    case GQ_FMT_Q5_0: return ((cols + 31) / 32) * 22;
+    case GQ_FMT_Q4_K: return ((cols + 255) / 256) * 144;
+    case GQ_FMT_Q5_K: return ((cols + 255) / 256) * 176;
+    case GQ_FMT_Q6_K: return ((cols + 255) / 256) * 210;
+    default: return -1;
+  }
 }
 
 extern "C" const char* gq_status_str(int status) {
@@ -136,8 +145,8 @@ extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, con
   // One activation row is the matvec (same rounding, its kernel). Q4_K with
   // two or more rows runs on the matrix cores: padded to 16 rows it was
   // measured faster than the fp32 few-row kernel from M = 2 on (the latter
-  // re-reads each activation row per weight-row batch). Q8_0 keeps the fp32
-  // kernel for M >= 2.
+  // re-reads each activation row per weight-row batch). The other formats
+  // keep the fp32 kernel for M >= 2.
   if (M == 1) {
     gq::GemvArgs v{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
     return finish(gq::launch_gemv(fmt, v, cus, (hipStream_t)stream));

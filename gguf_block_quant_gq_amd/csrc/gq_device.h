@@ -8,6 +8,16 @@
 //   Q4_K: 144 B = fp16 d | fp16 dmin | 12 B scales | 128 B 4-bit codes
 //         w = (d * sc_j) * code - dmin * m_j, sub-block j = 2g + h for weight
 //         64g + 32h + l, code = nibble h of code byte 32g + l.
+//   Q5_0: 22 B = fp16 d | 32-bit qh | 16 B nibbles   w = d * (code - 16);
+//         weight i < 16: low nibble of byte i, i >= 16: high nibble of byte
+//         i - 16; bit 4 of the code = bit i of qh.
+//   Q5_K: 176 B = the 16-byte Q4_K header | 32 B qh | 128 B nibbles placed as
+//         Q4_K's codes; bit 4 of weight 64g + 32h + l's code = bit 2g + h of
+//         qh[l]. w = (d * sc_j) * code - dmin * m_j.
+//   Q6_K: 210 B = 128 B ql | 64 B qh | 16 int8 scales | fp16 d; weight
+//         128n + 32k + l: low bits = nibble k >> 1 of ql[64n + 32(k & 1) + l],
+//         top two bits = bits 2k, 2k + 1 of qh[32n + l], scale i / 16;
+//         w = (d * scale) * (code - 32).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,6 +30,12 @@ constexpr int kQ8Bytes = 34;
 constexpr int kQ4KWeights = 256;
 constexpr int kQ4KBytes = 144;
 constexpr int kQ4KChunksPerBlock = 8;  // 16-byte code chunks per super-block
+constexpr int kQ5_0Weights = 32;
+constexpr int kQ5_0Bytes = 22;
+constexpr int kQ5KWeights = 256;
+constexpr int kQ5KBytes = 176;
+constexpr int kQ6KWeights = 256;
+constexpr int kQ6KBytes = 210;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -76,11 +92,9 @@ struct Q8Raw {
 };
 
 __device__ __forceinline__ void q8_load(const uint8_t* blk, Q8Raw& r) {
-  uintptr_t a = (uintptr_t)blk;
   r.d16 = load_u16(blk);
-  uintptr_t b = (a + 2) & ~(uintptr_t)3;
-  r.shift = (uint32_t)((a + 2) & 3);
-  const uint8_t* p = (const uint8_t*)b;
+  r.shift = (uint32_t)(((uintptr_t)blk + 2) & 3);
+  const uint8_t* p = blk + 2 - r.shift;  // 4-aligned; pointer arithmetic keeps global loads
   u32x4 v0 = load_u32x4(p);
   u32x4 v1 = load_u32x4(p + 16);
   r.w[0] = v0.x; r.w[1] = v0.y; r.w[2] = v0.z; r.w[3] = v0.w;

@@ -9,6 +9,9 @@ namespace gq {
 
 constexpr int kFmtQ8_0 = 8;
 constexpr int kFmtQ4_K = 12;
+constexpr int kFmtQ5_0 = 6;
+constexpr int kFmtQ5_K = 13;
+constexpr int kFmtQ6_K = 14;
 
 struct GemvArgs {
   const uint8_t* W;
@@ -26,7 +29,7 @@ struct DequantArgs {
   int64_t row_bytes;
   int64_t rows;
   int cols;
-  int units;  // per row: Q8_0 blocks or Q4_K super-blocks (set by the launcher)
+  int units;  // per row: blocks (Q8_0, Q5_0) or super-blocks (K-quants); set by the launcher
 };
 
 struct GemmArgs {

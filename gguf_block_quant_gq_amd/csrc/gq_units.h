@@ -53,6 +53,7 @@ struct Q8Unit {
 
   // x arrives as 16-byte chunks (4 floats): 8 per unit, in column order.
   static constexpr int kChunks = 8;
+  __device__ static int x_chunk(int gl, int k) { return kChunks * gl + k; }
   __device__ static void set_x(X& x, const f32x4 (&c)[kChunks]) {
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
@@ -135,6 +136,7 @@ struct Q8PairUnit {
   __device__ static void finish_x(X&) {}
 
   static constexpr int kChunks = 16;
+  __device__ static int x_chunk(int gl, int k) { return kChunks * gl + k; }
   __device__ static void set_x(X& x, const f32x4 (&c)[kChunks]) {
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
@@ -247,6 +249,7 @@ struct Q4KUnit {
   // x arrives as 16-byte chunks (4 floats): 16 per unit, in column order
   // (chunks 0-7 are x_a, 8-15 are x_b).
   static constexpr int kChunks = 16;
+  __device__ static int x_chunk(int gl, int k) { return kChunks * gl + k; }
   __device__ static void set_x(X& x, const f32x4 (&c)[kChunks]) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -335,6 +338,484 @@ struct Q4KUnit {
     const float qs = __builtin_fmaf(sc[1], s1, sc[0] * s0);
     const float ms = __builtin_fmaf(m[1], x.sb, m[0] * x.sa);
     return __builtin_fmaf(d, qs, -dmin * ms);
+  }
+};
+
+// ------------------------------------------------- 5- and 6-bit helpers
+// Byte t of w as an fp32 value (one v_cvt_f32_ubyte per weight).
+__device__ __forceinline__ float ubyte_at(uint32_t w, int t) {
+  return (float)((w >> (8 * t)) & 0xFFu);
+}
+
+// Four consecutive bits n (0..15) spread to bit 4 of bytes 0..3. The 24-bit
+// product n * (1 + 2^7 + 2^14 + 2^21) puts bit t of n at bit t + 7u for
+// every u, all 16 positions distinct (so nothing carries); bit t lands on
+// bit 8t exactly when u = t.
+__device__ __forceinline__ uint32_t spread4_bit4(uint32_t n) {
+  return (__umul24(n, 0x204081u) & 0x01010101u) << 4;
+}
+
+// Rotate right (v_alignbit with both halves the same register).
+__device__ __forceinline__ uint32_t rotr(uint32_t v, uint32_t r) {
+  return __builtin_amdgcn_alignbit(v, v, r);
+}
+
+// ------------------------------------------------------------- Q5_0 unit
+// Unit = one 22-byte block (32 weights, columns 32u .. 32u + 31). Blocks are
+// only 2-byte aligned, so the lane loads the six dwords from the 4-byte
+// boundary at or below the block start (their first bytes always lie inside
+// the block or the dword holding its first two bytes) and shifts them in
+// registers. code_i = nibble | (bit i of qh) << 4; w_i = d * (code_i - 16),
+// so the unit contributes d * (sum code_i x_i - 16 * sum x_i).
+struct Q5_0Unit {
+  using Base = Q5_0Unit;
+  static constexpr int kPerUnitCols = 32;
+  struct X {
+    float v[32];
+    float s;  // sum of the 32 x values
+  };
+  struct Raw {
+    uint32_t w[6];
+    uint32_t shift;  // 0 or 2: bytes between the 4-byte boundary and the block
+  };
+  struct Lane {};
+
+  __device__ static Lane lane(int) { return Lane{}; }
+
+  __device__ static bool valid(int unit, int units, int) { return unit < units; }
+
+  __device__ static void load_x(X& x, const float* xv, int unit, int cols) {
+    const int c0 = unit * 32;
+    if (c0 + 32 <= cols) {
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const f32x4 t = load_f32x4(xv + c0 + i);
+        x.v[i] = t.x; x.v[i + 1] = t.y; x.v[i + 2] = t.z; x.v[i + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x.v[i] = (c0 + i < cols) ? xv[c0 + i] : 0.f;
+    }
+  }
+
+  __device__ static void zero_x(X& x) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x.v[i] = 0.f;
+    x.s = 0.f;
+  }
+
+  __device__ static void finish_x(X& x) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+      s0 += x.v[i];
+      s1 += x.v[i + 1];
+    }
+    x.s = s0 + s1;
+  }
+
+  static constexpr int kChunks = 8;
+  __device__ static int x_chunk(int gl, int k) { return kChunks * gl + k; }
+  __device__ static void set_x(X& x, const f32x4 (&c)[kChunks]) {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      x.v[4 * k] = c[k].x; x.v[4 * k + 1] = c[k].y; x.v[4 * k + 2] = c[k].z; x.v[4 * k + 3] = c[k].w;
+    }
+  }
+
+  __device__ static void load(Raw& raw, const uint8_t* row, int unit) {
+    const uint8_t* blk = row + (int64_t)unit * kQ5_0Bytes;
+    raw.shift = (uint32_t)((uintptr_t)blk & 3u);
+    const uint8_t* p = blk - raw.shift;  // pointer arithmetic keeps global loads
+    const u32x4 v = load_u32x4(p);
+    raw.w[0] = v.x; raw.w[1] = v.y; raw.w[2] = v.z; raw.w[3] = v.w;
+    raw.w[4] = load_u32(p + 16);
+    raw.w[5] = load_u32(p + 20);
+  }
+
+  __device__ static void zero(Raw& raw) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) raw.w[k] = 0u;
+    raw.shift = 0u;
+  }
+
+  // The block's fields: fp16 d bits, qh, and the 16 nibble bytes as 4 dwords.
+  __device__ static void fields(const Raw& r, uint32_t& d16, uint32_t& qh, uint32_t q[4]) {
+    uint32_t b[6];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) b[k] = __builtin_amdgcn_alignbyte(r.w[k + 1], r.w[k], r.shift);
+    b[5] = __builtin_amdgcn_alignbyte(0u, r.w[5], r.shift);
+    d16 = b[0] & 0xFFFFu;
+    qh = __builtin_amdgcn_alignbyte(b[1], b[0], 2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_alignbyte(b[k + 2], b[k + 1], 2);
+  }
+
+  // codes of weights 4k..4k+3 (ca) and 16+4k..16+4k+3 (cb) as bytes 0..31
+  __device__ static void codes(uint32_t qh, const uint32_t q[4], int k, uint32_t& ca, uint32_t& cb) {
+    ca = (q[k] & 0x0F0F0F0Fu) | spread4_bit4(__builtin_amdgcn_ubfe(qh, 4 * k, 4));
+    cb = ((q[k] >> 4) & 0x0F0F0F0Fu) | spread4_bit4(__builtin_amdgcn_ubfe(qh, 16 + 4 * k, 4));
+  }
+
+  __device__ static float dot(const Raw& raw, const X& x, const Lane&) {
+    uint32_t d16, qh, q[4];
+    fields(raw, d16, qh, q);
+    float s0 = 0.f, s1 = 0.f, t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t ca, cb;
+      codes(qh, q, k, ca, cb);
+#pragma unroll
+      for (int t = 0; t < 4; t += 2) {
+        s0 = __builtin_fmaf(ubyte_at(ca, t), x.v[4 * k + t], s0);
+        t0 = __builtin_fmaf(ubyte_at(ca, t + 1), x.v[4 * k + t + 1], t0);
+        s1 = __builtin_fmaf(ubyte_at(cb, t), x.v[16 + 4 * k + t], s1);
+        t1 = __builtin_fmaf(ubyte_at(cb, t + 1), x.v[16 + 4 * k + t + 1], t1);
+      }
+    }
+    const float sum = (s0 + t0) + (s1 + t1);
+    return half_bits_to_float(d16) * __builtin_fmaf(-16.f, x.s, sum);
+  }
+
+  // Decoded form for several activation rows: w_i = d * (code_i - 16), exact.
+  struct Dec {
+    float w[32];
+  };
+
+  __device__ static void decode(Dec& dec, const Raw& raw, const Lane&) {
+    uint32_t d16, qh, q[4];
+    fields(raw, d16, qh, q);
+    const float d = half_bits_to_float(d16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t ca, cb;
+      codes(qh, q, k, ca, cb);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        dec.w[4 * k + t] = d * (ubyte_at(ca, t) - 16.f);
+        dec.w[16 + 4 * k + t] = d * (ubyte_at(cb, t) - 16.f);
+      }
+    }
+  }
+
+  __device__ static float dot_dec(const Dec& dec, const X& x) { return q8_block_dot_f(dec.w, x.v); }
+};
+
+// ------------------------------------------------------------- Q5_K unit
+// Same unit, x handling and scale fields as Q4_K (the 32 nibble bytes of
+// group g, columns 64u .. 64u + 63); bit 4 of each code comes from the 32 qh
+// bytes: bit 2g of qh[l] for weight 64g + l (sub-block 2g), bit 2g + 1 for
+// weight 64g + 32 + l. A rotation moves that bit of every byte to bit 4,
+// and the 5-bit codes are converted one byte at a time.
+struct Q5KUnit : Q4KUnit {
+  using Base = Q5KUnit;
+  struct Raw {
+    u32x4 h, qh0, qh1, q0, q1;
+  };
+  struct Lane : Q4KUnit::Lane {
+    uint32_t rot_a, rot_b;  // rotate-right amounts taking bit 2g / 2g+1 to bit 4
+  };
+
+  __device__ static Lane lane(int gl) {
+    Lane l;
+    static_cast<Q4KUnit::Lane&>(l) = Q4KUnit::lane(gl);
+    l.rot_a = (2u * l.g + 28u) & 31u;
+    l.rot_b = (2u * l.g + 29u) & 31u;
+    return l;
+  }
+
+  __device__ static void load(Raw& raw, const uint8_t* row, int unit) {
+    const uint8_t* blk = row + (int64_t)(unit >> 2) * kQ5KBytes;
+    const int g = unit & 3;
+    raw.h = load_u32x4(blk);
+    raw.qh0 = load_u32x4(blk + 16);
+    raw.qh1 = load_u32x4(blk + 32);
+    raw.q0 = load_u32x4(blk + 48 + 32 * g);
+    raw.q1 = load_u32x4(blk + 64 + 32 * g);
+  }
+
+  __device__ static void zero(Raw& raw) {
+    raw.h = raw.qh0 = raw.qh1 = raw.q0 = raw.q1 = u32x4{0, 0, 0, 0};
+  }
+
+  // 5-bit codes of weights 64g + 4k.. (ca, sub-block 2g) and 64g + 32 + 4k..
+  // (cb, sub-block 2g + 1) as bytes.
+  __device__ static void codes(const Raw& raw, const Lane& ln, int k, uint32_t& ca, uint32_t& cb) {
+    const uint32_t w[8] = {raw.q0.x, raw.q0.y, raw.q0.z, raw.q0.w,
+                           raw.q1.x, raw.q1.y, raw.q1.z, raw.q1.w};
+    const uint32_t hq[8] = {raw.qh0.x, raw.qh0.y, raw.qh0.z, raw.qh0.w,
+                            raw.qh1.x, raw.qh1.y, raw.qh1.z, raw.qh1.w};
+    ca = (rotr(hq[k], ln.rot_a) & 0x10101010u) | (w[k] & 0x0F0F0F0Fu);
+    cb = (rotr(hq[k], ln.rot_b) & 0x10101010u) | ((w[k] >> 4) & 0x0F0F0F0Fu);
+  }
+
+  __device__ static void scale_codes(const Raw& raw, const Lane& ln, float sc[2], float m[2]) {
+    Q4KUnit::Raw hr;
+    hr.h = raw.h;
+    Q4KUnit::scales(hr, ln, sc, m);
+  }
+
+  __device__ static float dot(const Raw& raw, const X& x, const Lane& ln) {
+    float s0 = 0.f, s1 = 0.f, t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t ca, cb;
+      codes(raw, ln, k, ca, cb);
+      s0 = __builtin_fmaf(ubyte_at(ca, 0), x.a[4 * k + 0], s0);
+      s1 = __builtin_fmaf(ubyte_at(cb, 0), x.b[4 * k + 0], s1);
+      t0 = __builtin_fmaf(ubyte_at(ca, 1), x.a[4 * k + 1], t0);
+      t1 = __builtin_fmaf(ubyte_at(cb, 1), x.b[4 * k + 1], t1);
+      s0 = __builtin_fmaf(ubyte_at(ca, 2), x.a[4 * k + 2], s0);
+      s1 = __builtin_fmaf(ubyte_at(cb, 2), x.b[4 * k + 2], s1);
+      t0 = __builtin_fmaf(ubyte_at(ca, 3), x.a[4 * k + 3], t0);
+      t1 = __builtin_fmaf(ubyte_at(cb, 3), x.b[4 * k + 3], t1);
+    }
+    s0 += t0;
+    s1 += t1;
+    float sc[2], m[2];
+    scale_codes(raw, ln, sc, m);
+    const float d = half_bits_to_float(raw.h.x & 0xFFFFu);
+    const float dmin = half_bits_to_float(raw.h.x >> 16);
+    const float qs = __builtin_fmaf(sc[1], s1, sc[0] * s0);
+    const float ms = __builtin_fmaf(m[1], x.sb, m[0] * x.sa);
+    return __builtin_fmaf(d, qs, -dmin * ms);
+  }
+
+  // Decoded form: w = (d * sc_j) * code - dmin * m_j (one rounding).
+  struct Dec {
+    float a[32], b[32];
+  };
+
+  __device__ static void decode(Dec& dec, const Raw& raw, const Lane& ln) {
+    float sc[2], m[2];
+    scale_codes(raw, ln, sc, m);
+    const float d = half_bits_to_float(raw.h.x & 0xFFFFu);
+    const float dmin = half_bits_to_float(raw.h.x >> 16);
+    const float A0 = d * sc[0], A1 = d * sc[1], B0 = dmin * m[0], B1 = dmin * m[1];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t ca, cb;
+      codes(raw, ln, k, ca, cb);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        dec.a[4 * k + t] = __builtin_fmaf(A0, ubyte_at(ca, t), -B0);
+        dec.b[4 * k + t] = __builtin_fmaf(A1, ubyte_at(cb, t), -B1);
+      }
+    }
+  }
+
+  __device__ static float dot_dec(const Dec& dec, const X& x) {
+    return q8_block_dot_f(dec.a, x.a) + q8_block_dot_f(dec.b, x.b);
+  }
+};
+
+// ------------------------------------------------------------- Q6_K unit
+// Unit u: super-block u >> 2, part p = u & 3 = 2n + e (n = half, e = 0/1).
+// Its 64 weights are two 32-runs that share their code bytes: run a =
+// weights 128n + 32e + l (low nibbles of ql[64n + 32e + l], top bits 2e and
+// 2e + 1 of qh[32n + l], scales 8n + 2e + l/16) and run b = weights
+// 128n + 32e + 64 + l (high nibbles of the same bytes, top bits 2e + 4 and
+// 2e + 5, scales 8n + 2e + 4 + l/16). The x slices are therefore the column
+// ranges [128n + 32e, +32) and [128n + 32e + 64, +32) of the super-block;
+// the four parts together cover it once.
+// Super-blocks are only 2-byte aligned (210 B), so each field is loaded from
+// the 4-byte boundary at or below it and shifted in registers. With
+// w = (d * scale) * (code - 32), a scale group of 16 weights contributes
+// d * scale * (sum code * x - 32 * sum x); the four x sums are kept with x.
+struct Q6KUnit {
+  using Base = Q6KUnit;
+  static constexpr int kPerUnitCols = 64;
+  struct X {
+    float a[32], b[32];
+    float s[4];  // sums of a[0..15], a[16..31], b[0..15], b[16..31]
+  };
+  struct Raw {
+    uint32_t l[9], h[9], s[3];
+    uint32_t d16;
+    uint32_t shift;  // 0 or 2
+  };
+  struct Lane {
+    uint32_t n, e;
+    uint32_t rot_a;   // rotate right: bits 2e, 2e+1 of each qh byte -> 4, 5
+    uint32_t rot_b;   // bits 2e+4, 2e+5 -> 4, 5
+    uint32_t sc_off;  // bit offset of the run's first scale in its dword (16e)
+  };
+
+  __device__ static Lane lane(int gl) {
+    Lane l;
+    const uint32_t p = (uint32_t)gl & 3u;
+    l.n = p >> 1;
+    l.e = p & 1u;
+    l.rot_a = (2u * l.e + 28u) & 31u;
+    l.rot_b = 2u * l.e;
+    l.sc_off = 16u * l.e;
+    return l;
+  }
+
+  __device__ static int col_a(int unit) {
+    const int p = unit & 3;
+    return (unit >> 2) * kQ6KWeights + 128 * (p >> 1) + 32 * (p & 1);
+  }
+
+  __device__ static bool valid(int unit, int units, int cols) {
+    return unit < units && col_a(unit) < cols;
+  }
+
+  __device__ static void load_run(float* v, const float* xv, int c0, int cols) {
+    if (c0 + 32 <= cols) {
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const f32x4 t = load_f32x4(xv + c0 + i);
+        v[i] = t.x; v[i + 1] = t.y; v[i + 2] = t.z; v[i + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = (c0 + i < cols) ? xv[c0 + i] : 0.f;
+    }
+  }
+
+  __device__ static void load_x(X& x, const float* xv, int unit, int cols) {
+    const int c0 = col_a(unit);
+    load_run(x.a, xv, c0, cols);
+    load_run(x.b, xv, c0 + 64, cols);
+  }
+
+  __device__ static void zero_x(X& x) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x.a[i] = x.b[i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x.s[i] = 0.f;
+  }
+
+  __device__ static void finish_x(X& x) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float sa = 0.f, sb = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sa += x.a[16 * h + i];
+        sb += x.b[16 * h + i];
+      }
+      x.s[h] = sa;
+      x.s[2 + h] = sb;
+    }
+  }
+
+  // The unit's 16 x chunks: 8 of run a, then 8 of run b; in the staged x
+  // of a group (4 units per super-block, 64 chunks) they sit at
+  // 64 (gl >> 2) + 32n + 8e + [0, 8) and 16 chunks further on.
+  static constexpr int kChunks = 16;
+  __device__ static int x_chunk(int gl, int k) {
+    const int p = gl & 3;
+    return 64 * (gl >> 2) + 32 * (p >> 1) + 8 * (p & 1) + k + (k >= 8 ? 8 : 0);
+  }
+  __device__ static void set_x(X& x, const f32x4 (&c)[kChunks]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      x.a[4 * k] = c[k].x; x.a[4 * k + 1] = c[k].y; x.a[4 * k + 2] = c[k].z; x.a[4 * k + 3] = c[k].w;
+      x.b[4 * k] = c[8 + k].x; x.b[4 * k + 1] = c[8 + k].y;
+      x.b[4 * k + 2] = c[8 + k].z; x.b[4 * k + 3] = c[8 + k].w;
+    }
+  }
+
+  __device__ static void load9(uint32_t (&w)[9], const uint8_t* p) {
+    const u32x4 v0 = load_u32x4(p);
+    const u32x4 v1 = load_u32x4(p + 16);
+    w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+    w[8] = load_u32(p + 32);
+  }
+
+  __device__ static void load(Raw& raw, const uint8_t* row, int unit) {
+    const uint8_t* blk = row + (int64_t)(unit >> 2) * kQ6KBytes;
+    const int p = unit & 3, n = p >> 1, e = p & 1;
+    raw.shift = (uint32_t)((uintptr_t)blk & 3u);
+    const uint8_t* base = blk - raw.shift;  // pointer arithmetic keeps global loads
+    load9(raw.l, base + 64 * n + 32 * e);
+    load9(raw.h, base + 128 + 32 * n);
+    const uint8_t* sp = base + 192 + 8 * n;
+    raw.s[0] = load_u32(sp);
+    raw.s[1] = load_u32(sp + 4);
+    raw.s[2] = load_u32(sp + 8);
+    raw.d16 = load_u16(blk + 208);
+  }
+
+  __device__ static void zero(Raw& raw) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) raw.l[k] = raw.h[k] = 0u;
+    raw.s[0] = raw.s[1] = raw.s[2] = 0u;
+    raw.d16 = 0u;
+    raw.shift = 0u;
+  }
+
+  // 6-bit codes of run a (ca) and run b (cb), weights 4k..4k+3, as bytes.
+  __device__ static void codes(const Raw& raw, const Lane& ln, int k, uint32_t& ca, uint32_t& cb) {
+    const uint32_t L = __builtin_amdgcn_alignbyte(raw.l[k + 1], raw.l[k], raw.shift);
+    const uint32_t H = __builtin_amdgcn_alignbyte(raw.h[k + 1], raw.h[k], raw.shift);
+    ca = (rotr(H, ln.rot_a) & 0x30303030u) | (L & 0x0F0F0F0Fu);
+    cb = (rotr(H, ln.rot_b) & 0x30303030u) | ((L >> 4) & 0x0F0F0F0Fu);
+  }
+
+  // The four int8 scales of the unit: a0, a1, b0, b1.
+  __device__ static void scales(const Raw& raw, const Lane& ln, float sc[4]) {
+    const uint32_t s0 = __builtin_amdgcn_alignbyte(raw.s[1], raw.s[0], raw.shift);
+    const uint32_t s1 = __builtin_amdgcn_alignbyte(raw.s[2], raw.s[1], raw.shift);
+    // signed bytes through int8_t: a signed bit-field builtin here was
+    // converted to float as unsigned by the compiler
+    sc[0] = (float)(int8_t)(s0 >> ln.sc_off);
+    sc[1] = (float)(int8_t)(s0 >> (ln.sc_off + 8));
+    sc[2] = (float)(int8_t)(s1 >> ln.sc_off);
+    sc[3] = (float)(int8_t)(s1 >> (ln.sc_off + 8));
+  }
+
+  __device__ static float dot(const Raw& raw, const X& x, const Lane& ln) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};  // a0, a1, b0, b1
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t ca, cb;
+      codes(raw, ln, k, ca, cb);
+      const int h = k >> 2;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[h] = __builtin_fmaf(ubyte_at(ca, t), x.a[4 * k + t], acc[h]);
+        acc[2 + h] = __builtin_fmaf(ubyte_at(cb, t), x.b[4 * k + t], acc[2 + h]);
+      }
+    }
+    float sc[4];
+    scales(raw, ln, sc);
+    float r = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r = __builtin_fmaf(sc[q], __builtin_fmaf(-32.f, x.s[q], acc[q]), r);
+    return half_bits_to_float(raw.d16) * r;
+  }
+
+  // Decoded form: w = (d * scale) * (code - 32), exact.
+  struct Dec {
+    float a[32], b[32];
+  };
+
+  __device__ static void decode(Dec& dec, const Raw& raw, const Lane& ln) {
+    float sc[4];
+    scales(raw, ln, sc);
+    const float d = half_bits_to_float(raw.d16);
+    float A[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) A[q] = d * sc[q];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t ca, cb;
+      codes(raw, ln, k, ca, cb);
+      const int h = k >> 2;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        dec.a[4 * k + t] = A[h] * (ubyte_at(ca, t) - 32.f);
+        dec.b[4 * k + t] = A[2 + h] * (ubyte_at(cb, t) - 32.f);
+      }
+    }
+  }
+
+  __device__ static float dot_dec(const Dec& dec, const X& x) {
+    return q8_block_dot_f(dec.a, x.a) + q8_block_dot_f(dec.b, x.b);
   }
 };
 

@@ -1,6 +1,7 @@
 /*
- * gq.h -- C ABI of libgq: block-quantised (GGUF Q8_0 / Q4_K) weight matrices
- * times fp32 activations on an AMD MI355X (gfx950), dequantised on the fly.
+ * gq.h -- C ABI of libgq: block-quantised (GGUF Q8_0 / Q4_K / Q5_0 / Q5_K /
+ * Q6_K) weight matrices times fp32 activations on an AMD MI355X (gfx950),
+ * dequantised on the fly.
  *
  * The operation: a weight matrix W[out, in] stored row-major as GGUF blocks,
  * each row a whole number of blocks, multiplied by fp32 activations
@@ -21,6 +22,22 @@
  *     packed 6-bit scale/min codes (sc_j, m_j, j < 8), 128 bytes of 4-bit
  *     codes; weight 64g+32h+l takes nibble h of code byte 32g+l and belongs
  *     to sub-block j = 2g+h; w = (d*sc_j)*code - dmin*m_j.
+ *   Q5_0 (fmt 6):  22 B per 32 weights: fp16 d, a 32-bit little-endian word
+ *     qh, 16 bytes of nibbles; weight i < 16 takes the low nibble of byte i,
+ *     weight 16 + i the high nibble of byte i, and bit 4 of every code is
+ *     bit i of qh; w = d*(code - 16).
+ *   Q5_K (fmt 13): 176 B per 256 weights: the 16 header bytes of Q4_K, 32
+ *     bytes qh, 128 bytes of nibbles placed as Q4_K's codes; bit 4 of weight
+ *     64g+32h+l's code is bit 2g+h of qh[l]; w = (d*sc_j)*code - dmin*m_j.
+ *   Q6_K (fmt 14): 210 B per 256 weights: 128 bytes ql, 64 bytes qh, 16 int8
+ *     scales, fp16 d; weight 128n+32k+l takes nibble k>>1 of
+ *     ql[64n + 32(k&1) + l] as its low four bits and bits 2k, 2k+1 of
+ *     qh[32n + l] as its top two, scale number i/16 for weight i;
+ *     w = (d*scale)*(code - 32).
+ *   Q5_0, Q5_K and Q6_K appear next to Q4_K in the model files the pages run
+ *   ("nurllama" README, "What it runs"; their per-format matvec kernels are
+ *   listed in "nurllama 0.18.1 API", kernels.nu section). The byte layouts
+ *   are GGUF's public ones; the pages do not print them.
  *
  * Ownership and threading
  *   All pointers are device pointers owned by the caller; the library never
@@ -37,8 +54,9 @@
  *   different streams may run concurrently.
  *
  * Alignment
- *   Q8_0 W: 2-byte aligned (a row range of a Q8_0 tensor starts on any
- *   34-byte block boundary). Q4_K W: 4-byte aligned. x, y, X, Y, out: 4-byte
+ *   Q8_0, Q5_0 and Q6_K W: 2-byte aligned (a row range of such a tensor
+ *   starts on any block boundary, and their blocks are 34, 22 and 210 bytes).
+ *   Q4_K and Q5_K W: 4-byte aligned. x, y, X, Y, out: 4-byte
  *   aligned. An output that overlaps an input is rejected (GQ_ERR_OVERLAP).
  *
  * Errors
@@ -61,16 +79,19 @@ extern "C" {
 #endif
 
 /* ggml tensor type ids ("nurllama 0.18.1 API", convert.nu section, gives
- * Q8_0 = 8; Q4_K = 12 is GGUF's id for the K-quant). */
+ * Q8_0 = 8; the others are GGUF's ids). */
 enum gq_fmt {
+    GQ_FMT_Q5_0 = 6,
     GQ_FMT_Q8_0 = 8,
     GQ_FMT_Q4_K = 12,
+    GQ_FMT_Q5_K = 13,
+    GQ_FMT_Q6_K = 14,
 };
 
 enum gq_status {
     GQ_OK = 0,
     GQ_ERR_NULL = 1,   /* a required pointer is NULL */
-    GQ_ERR_FMT = 2,    /* fmt is not Q8_0 or Q4_K */
+    GQ_ERR_FMT = 2,    /* fmt is not one of enum gq_fmt */
     GQ_ERR_SHAPE = 3,  /* rows or M < 0, cols <= 0, or a size that overflows */
     GQ_ERR_ALIGN = 4,  /* a pointer breaks the alignment rules above */
     GQ_ERR_DEVICE = 5, /* the HIP runtime reported an error */
@@ -86,9 +107,9 @@ const char* gq_status_str(int status);
 
 /*
  * out[r*cols + c] = w(r, c) as fp32, for r < rows, c < cols.
- * Bit-exact: Q8_0 w = d*q and Q4_K w = (d*sc)*code - dmin*m, where every
- * product is exact in fp32 and the Q4_K subtraction rounds once to nearest
- * even; fp16 subnormal scales are decoded exactly. This is the device
+ * Bit-exact: w as defined per format above, where every product is exact
+ * in fp32 and the Q4_K / Q5_K subtraction rounds once to nearest even;
+ * fp16 subnormal scales are decoded exactly. This is the device
  * counterpart of the host dequant fallback ("nurllama 0.18.1 API", model.nu
  * section). Runs on the null stream and returns after it has finished.
  * out: rows*cols floats.
@@ -113,8 +134,9 @@ int gq_matvec(int fmt, const void* W, int64_t rows, int64_t cols,
  * The batched form used for prompt chunks ("nurllama 0.18.1 API", model.nu
  * section: the matmuls run over up to 64 positions at once, each weight read
  * once per chunk). M == 1 runs the gq_matvec kernel. Q4_K with M >= 2 runs
- * on the matrix cores (with the workspace described above); Q8_0 with
- * M >= 2 streams W once per 15 activation rows with fp32 arithmetic. Same
+ * on the matrix cores (with the workspace described above); the other
+ * formats with M >= 2 stream W once per 15 activation rows with fp32
+ * arithmetic. Same
  * accuracy bound as gq_matvec; repeated calls give bit-identical results.
  * Asynchronous on `stream`.
  */

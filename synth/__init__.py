@@ -184,13 +184,36 @@ LLAMA3_8B_LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096),
 LLAMA3_8B_LAYERS = 32
 PREFILL_M = (16, 64, 512)
 
+# Shapes of the other formats that Q4_K_M / Q5_K_M files mix in: the
+# Llama-3-8B lm_head and some ffn_down tensors are Q6_K, Qwen2.5-0.5B's
+# 896-wide tensors (not a multiple of 256 columns) use Q5_0, and Q5_K_M
+# files store the Llama-3-8B projections as Q5_K. Seed 5, matrix_id = index.
+MIXED_FORMATS = [
+    ("llama3_8b_lm_head_q6_k", FMT_Q6_K, 128256, 4096),
+    ("llama3_8b_down_q6_k", FMT_Q6_K, 4096, 14336),
+    ("llama3_8b_q_q5_k", FMT_Q5_K, 4096, 4096),
+    ("llama3_8b_gate_q5_k", FMT_Q5_K, 14336, 4096),
+    ("llama3_8b_down_q5_k", FMT_Q5_K, 4096, 14336),
+    ("qwen05b_896x896_q5_0", FMT_Q5_0, 896, 896),
+    ("qwen05b_128x896_q5_0", FMT_Q5_0, 128, 896),
+    ("qwen05b_4864x896_q5_0", FMT_Q5_0, 4864, 896),
+]
+
 WORKLOADS = {
     "smollm135m_ffn_up_q8_0": dict(seed=0, shapes=[SMOLLM_FFN_UP]),
     "qwen05b_decode_q4_k": dict(seed=1, shapes=QWEN05_DECODE),
     "qwen05b_lm_head_q8_0": dict(seed=2, shapes=[QWEN05_LM_HEAD]),
     "llama3_8b_decode_step_q4_k": dict(seed=3),
     "llama3_8b_prefill_q4_k": dict(seed=4),
+    "mixed_formats": dict(seed=5, shapes=[(f, r, c) for _, f, r, c in MIXED_FORMATS]),
 }
+
+
+def mixed_format_weight_and_x(i: int):
+    """(name, fmt, rows, cols, W bytes, x) of MIXED_FORMATS[i]."""
+    name, fmt, rows, cols = MIXED_FORMATS[i]
+    W, x = matrix_and_x(fmt, rows, cols, 5, i)
+    return name, fmt, rows, cols, W, x
 
 
 def llama3_8b_matrix(layer: int, proj: int):

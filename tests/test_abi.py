@@ -42,12 +42,15 @@ def test_row_bytes(lib):
     assert gq.gq_row_bytes(12, 256) == 144
     assert gq.gq_row_bytes(12, 896) == 4 * 144
     assert gq.gq_row_bytes(12, 14336) == 56 * 144
+    assert gq.gq_row_bytes(6, 896) == 28 * 22
+    assert gq.gq_row_bytes(13, 896) == 4 * 176
+    assert gq.gq_row_bytes(14, 4096) == 16 * 210
     assert gq.gq_row_bytes(7, 256) < 0
     assert gq.gq_row_bytes(8, -1) < 0
 
 
 def test_row_bytes_matches_oracle(oracle):
-    for fmt in (8, 12):
+    for fmt in (6, 8, 12, 13, 14):
         for cols in (1, 31, 32, 33, 255, 256, 257, 896, 4096, 4864, 14336):
             assert gq.gq_row_bytes(fmt, cols) == oracle.row_bytes(fmt, cols)
 
@@ -77,8 +80,8 @@ def _dq(lib, fmt=12, W=W_OK, rows=4, cols=256, out=Y_OK):
 
 @pytest.mark.parametrize("call", [_mv, _mm, _dq])
 def test_validation_before_any_device_call(lib, call):
-    assert call(lib, fmt=0) == gq.GQ_ERR_FMT
-    assert call(lib, fmt=14) == gq.GQ_ERR_FMT
+    for bad in (0, 7, 10, 11, 15, -1):   # Q5_1, Q2_K, Q3_K, IQ... have no kernels
+        assert call(lib, fmt=bad) == gq.GQ_ERR_FMT
     assert call(lib, rows=-1) == gq.GQ_ERR_SHAPE
     assert call(lib, cols=0) == gq.GQ_ERR_SHAPE
     assert call(lib, cols=-5) == gq.GQ_ERR_SHAPE
@@ -86,6 +89,9 @@ def test_validation_before_any_device_call(lib, call):
     assert call(lib, W=None) == gq.GQ_ERR_NULL
     assert call(lib, W=W_OK + 2) == gq.GQ_ERR_ALIGN        # Q4_K needs 4-byte W
     assert call(lib, fmt=8, W=W_OK + 1) == gq.GQ_ERR_ALIGN  # Q8_0 needs 2-byte W
+    assert call(lib, fmt=6, W=W_OK + 1) == gq.GQ_ERR_ALIGN  # Q5_0 likewise
+    assert call(lib, fmt=14, W=W_OK + 1) == gq.GQ_ERR_ALIGN  # Q6_K likewise
+    assert call(lib, fmt=13, W=W_OK + 2) == gq.GQ_ERR_ALIGN  # Q5_K needs 4-byte W
     # empty products succeed without touching anything
     assert call(lib, rows=0, W=None) == gq.GQ_OK
 
@@ -108,3 +114,6 @@ def test_validation_vectors(lib):
     # a Q8_0 row range may start on any 34-byte block, i.e. a 2-byte boundary
     # (the alignment check passes, the overlap check after it fires)
     assert _mv(lib, fmt=8, W=W_OK + 34, y=W_OK + 40) == gq.GQ_ERR_OVERLAP
+    # likewise Q5_0 (22-byte blocks) and Q6_K (210-byte super-blocks)
+    assert _mv(lib, fmt=6, W=W_OK + 22, y=W_OK + 24) == gq.GQ_ERR_OVERLAP
+    assert _mv(lib, fmt=14, W=W_OK + 210, y=W_OK + 212) == gq.GQ_ERR_OVERLAP
