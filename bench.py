@@ -311,6 +311,30 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
                          GBps=round(b / (ms * 1e-3) / 1e9, 1))
     log(f"small shapes: { {k: v for k, v in out.items() if 'q4_k' in k or 'smollm' in k} }")
 
+    # the formats that Q4_K_M / Q5_K_M files mix in (Q6_K lm_head and
+    # ffn_down, Q5_K projections, Q5_0 896-wide tensors), cold: enough
+    # rotating copies to exceed 600 MB per pass
+    for i, (name, f, r, c) in enumerate(synth.MIXED_FORMATS):
+        _, _, _, _, W, x = synth.mixed_format_weight_and_x(i)
+        ncopy = max(1, min(16, -(-600_000_000 // W.size)))
+        cs = [torch.from_numpy(W).cuda() for _ in range(ncopy)]
+        xd2 = torch.from_numpy(x).cuda()
+        y2 = torch.empty(r, dtype=torch.float32, device="cuda")
+        b = gemv_bytes(gq.gq_row_bytes(f, c), r, c)
+
+        def mv(f=f, r=r, c=c, cs=cs, xd2=xd2, y2=y2):
+            sp = stream_ptr()
+            for w in cs:
+                lib.gq_matvec(f, w.data_ptr(), r, c, xd2.data_ptr(), y2.data_ptr(), sp)
+
+        g = capture(torch, mv)
+        ms = timer.time(g.replay, max(5, iters // 2), warmup=2) / ncopy
+        out[name] = dict(shape=[r, c], us_per_call=round(ms * 1e3, 2),
+                         GBps=round(b / (ms * 1e-3) / 1e9, 1),
+                         pct_hbm=round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1))
+        del cs, g
+    log(f"mixed formats: { {k: out[k] for k, *_ in synth.MIXED_FORMATS} }")
+
     # Q4_K products with a few (M = 4, 8) and many activation rows at the
     # Llama-3-8B prefill shapes (matrix cores)
     for which in ("gate", "down"):

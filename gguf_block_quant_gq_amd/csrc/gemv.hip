@@ -60,10 +60,22 @@ constexpr int kThreads = 256;
 #ifndef GQ_GEMV_RB1_WAVES_PER_CU
 #define GQ_GEMV_RB1_WAVES_PER_CU 8
 #endif
+// Q5_K and Q6_K (more registers and ALU work per weight)
+#ifndef GQ_GEMV_K56_RBN
+#define GQ_GEMV_K56_RBN GQ_GEMV_RBN
+#endif
+#ifndef GQ_GEMV_K56_WG_PER_CU
+#define GQ_GEMV_K56_WG_PER_CU GQ_GEMV_WG_PER_CU_RBN
+#endif
 
 template <class F>
 constexpr bool is_q8() {
   return std::is_same<typename F::Base, Q8Unit>::value || std::is_same<typename F::Base, Q8PairUnit>::value;
+}
+
+template <class F>
+constexpr bool is_k56() {
+  return std::is_same<typename F::Base, Q5KUnit>::value || std::is_same<typename F::Base, Q6KUnit>::value;
 }
 
 template <class F, int RB>
@@ -310,7 +322,10 @@ hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s) {
   // As many workgroups as can be resident at once (4 per CU at <= 128
   // VGPRs, else 2); each loops over row batches.
   constexpr bool kQ8 = is_q8<F>();
-  const int64_t cap = (int64_t)cus * (kQ8 ? GQ_GEMV_Q8_WG_PER_CU : RB == 1 ? GQ_GEMV_WG_PER_CU_RB1 : GQ_GEMV_WG_PER_CU_RBN);
+  constexpr int kPerCu = kQ8 ? GQ_GEMV_Q8_WG_PER_CU
+                         : RB == 1 ? GQ_GEMV_WG_PER_CU_RB1
+                         : is_k56<F>() ? GQ_GEMV_K56_WG_PER_CU : GQ_GEMV_WG_PER_CU_RBN;
+  const int64_t cap = (int64_t)cus * kPerCu;
   const int blocks = (int)(iters < cap ? iters : cap);
   if (a.units <= G)
     hipLaunchKernelGGL((gemv_kernel<F, G, RB>), dim3(blocks), dim3(kThreads), 0, s, a);
@@ -326,8 +341,15 @@ template <class F, int G>
 hipError_t with_g(const GemvArgs& a, int cus, hipStream_t s) {
   const int64_t groups_needed = (int64_t)cus * GQ_GEMV_RB1_WAVES_PER_CU * (G >= 64 ? 1 : 64 / G);
   if ((int64_t)a.rows < 2 * groups_needed) return launch_one<F, G, 1>(a, cus, s);
-  constexpr bool kQ8 = is_q8<F>();
-  return launch_one<F, G, kQ8 ? GQ_GEMV_Q8_RBN : GQ_GEMV_RBN>(a, cus, s);
+  // Q5_K / Q6_K on tall matrices (an lm_head, 14336-row projections): one
+  // row per group at more workgroups per CU measured faster (more waves to
+  // hide latency behind their heavier unpacking); two rows per group stay
+  // ahead for shorter matrices and for wide rows.
+  if constexpr (is_k56<F>() && G <= 128) {
+    if ((int64_t)a.rows >= 4 * groups_needed) return launch_one<F, G, 1>(a, cus, s);
+  }
+  constexpr int kRB = is_q8<F>() ? GQ_GEMV_Q8_RBN : is_k56<F>() ? GQ_GEMV_K56_RBN : GQ_GEMV_RBN;
+  return launch_one<F, G, kRB>(a, cus, s);
 }
 
 template <class F>
