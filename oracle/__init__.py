@@ -166,3 +166,25 @@ def quantize(fmt: int, w) -> np.ndarray:
         raise ValueError(f"unknown type {fmt}")
     _check(fn(_ptr(w), rows, cols, _ptr(out)), "quantize")
     return out
+
+
+def silu(v):
+    """silu(v) = v / (1 + e^-v) = v * sigmoid(v), in f64: the activation of the
+    SwiGLU feed-forward ("nurllama 0.18.1 API", model.nu section: the llama
+    shape's SwiGLU FFN; kernels.nu section: g <- silu(g) * u in place). For
+    very negative v, e^-v overflows to inf and the result is -0."""
+    v = np.asarray(v, np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def swiglu_matvec(fmt: int, W, rows: int, cols: int, x, nthreads: int = 1):
+    """The fused gate|up projection: W holds 2*rows rows, gate rows first and
+    up rows after them (one tensor whose parts are row ranges: "nurllama"
+    README, "What it runs", phi3's ffn_up). Returns (y, g, u, S_g, S_u) with
+    g, u the f64 matvecs of the two halves, y = silu(g) * u in f64 and S the
+    sums of |w*x| of each half."""
+    Y, S = matvec(fmt, W, 2 * rows, cols, x, nthreads)
+    g, u = Y[:rows], Y[rows:]
+    return silu(g) * u, g, u, S[:rows], S[rows:]
+
