@@ -203,6 +203,8 @@ def main() -> int:
                     bytes_per_launch=round(dom_bytes), avg_launch_us=round(dom_us, 3))
     log(f"roofline: {roofline}")
 
+    fused = fused_step_variant(torch, gq, lib, synth, mats, timer, stream_ptr, args)
+
     extras = {}
     if not args.no_extras:
         extras = run_extras(torch, gq, lib, synth, timer, stream_ptr, args)
@@ -241,12 +243,69 @@ def main() -> int:
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "per_projection": per_proj,
+        "fused_step_variant": fused,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "workloads": extras,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def fused_step_variant(torch, gq, lib, synth, mats, timer, stream_ptr, args):
+    """A labelled variant of the same decode step with the fused launches of
+    the pages' design: per layer one gq_matvec over the q|k|v tensor (the
+    three weight matrices concatenated row-wise, as a fused attn_qkv tensor
+    stores them), gq_matvec_acc for o and for down (the residual add folded
+    into the store), and gq_matvec_swiglu over the gate|up tensor: 128
+    launches, the same 3.93 GB of weights."""
+    f = gq.FMT_Q4_K
+    layers = []
+    nbytes = 0
+    for layer in range(synth.LLAMA3_8B_LAYERS):
+        m = mats[7 * layer:7 * layer + 7]
+        q, k, v, o, gate, up, down = m
+        wqkv = torch.cat([q["W"], k["W"], v["W"]])
+        wgu = torch.cat([gate["W"], up["W"]])
+        yqkv = torch.empty(q["rows"] + k["rows"] + v["rows"], dtype=torch.float32, device="cuda")
+        h = torch.empty(gate["rows"], dtype=torch.float32, device="cuda")
+        resid = torch.zeros(o["rows"], dtype=torch.float32, device="cuda")
+        calls = [
+            (lib.gq_matvec, (f, wqkv.data_ptr(), yqkv.numel(), q["cols"], q["x"].data_ptr(),
+                             yqkv.data_ptr())),
+            (lib.gq_matvec_acc, (f, o["W"].data_ptr(), o["rows"], o["cols"], o["x"].data_ptr(),
+                                 resid.data_ptr())),
+            (lib.gq_matvec_swiglu, (f, wgu.data_ptr(), gate["rows"], gate["cols"],
+                                    gate["x"].data_ptr(), h.data_ptr())),
+            (lib.gq_matvec_acc, (f, down["W"].data_ptr(), down["rows"], down["cols"],
+                                 down["x"].data_ptr(), resid.data_ptr())),
+        ]
+        w = sum(t["W"].numel() for t in m)
+        vec = 4 * (q["cols"] + yqkv.numel() + o["cols"] + 2 * o["rows"] + gate["cols"]
+                   + gate["rows"] + down["cols"] + 2 * down["rows"])
+        nbytes += w + vec
+        layers.append(dict(keep=(wqkv, wgu, yqkv, h, resid), calls=calls))
+
+    def fstep():
+        sp = stream_ptr()
+        for L in layers:
+            for fn, a in L["calls"]:
+                st = fn(*a, sp)
+                if st != 0:
+                    raise gq.GQError(st, "fused step")
+
+    g = capture(torch, fstep)
+    ms = timer.time(g.replay, args.steps, warmup=args.warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = dict(launch="hipGraph replay of 128 launches: q|k|v matvec, o matvec_acc, gate|up "
+                      "matvec_swiglu, down matvec_acc per layer",
+               launches_per_step=4 * len(layers), ms_per_step=round(ms, 4),
+               bytes_per_step=nbytes, GBps=round(gbs, 1),
+               pct_hbm=round(100 * gbs / HBM_PEAK_GBS, 2))
+    log(f"fused decode step variant: {out}")
+    del g, layers
+    torch.cuda.synchronize()
+    return out
 
 
 def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):

@@ -7,6 +7,8 @@ is no CPU fallback: if the library is not built, loading raises.
 
     gq_dequant(fmt, W, rows, cols, out=None)           -> out [rows, cols] fp32
     gq_matvec(fmt, W, rows, cols, x, y=None)           -> y [rows] fp32
+    gq_matvec_acc(fmt, W, rows, cols, x, y)            -> y += W x
+    gq_matvec_swiglu(fmt, W, rows, cols, x, y=None)    -> y = silu(W_gate x) * (W_up x)
     gq_matmul(fmt, W, rows, cols, X, Y=None)           -> Y [M, rows] fp32
 
 W is a uint8 CUDA tensor holding rows * gq_row_bytes(fmt, cols) bytes of
@@ -35,7 +37,8 @@ GQ_ERR_ALIGN = 4
 GQ_ERR_DEVICE = 5
 GQ_ERR_OVERLAP = 6
 
-EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matmul")
+EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matvec_acc",
+           "gq_matvec_swiglu", "gq_matmul")
 
 _lib = None
 
@@ -62,8 +65,9 @@ def load_library():
     lib.gq_status_str.restype = ctypes.c_char_p
     lib.gq_dequant.argtypes = [i32, vp, i64, i64, vp]
     lib.gq_dequant.restype = i32
-    lib.gq_matvec.argtypes = [i32, vp, i64, i64, vp, vp, vp]
-    lib.gq_matvec.restype = i32
+    for name in ("gq_matvec", "gq_matvec_acc", "gq_matvec_swiglu"):
+        getattr(lib, name).argtypes = [i32, vp, i64, i64, vp, vp, vp]
+        getattr(lib, name).restype = i32
     lib.gq_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
     lib.gq_matmul.restype = i32
     _lib = lib
@@ -128,10 +132,9 @@ def gq_dequant(fmt: int, W, rows: int, cols: int, out=None):
     return out
 
 
-def gq_matvec(fmt: int, W, rows: int, cols: int, x, y=None, stream=None):
-    """y = W x on `stream` (default: torch's current stream), asynchronous."""
+def _matvec(name: str, fmt: int, W, rows: int, cols: int, x, y, stream, wrows: int):
     torch = _torch()
-    _check_w(fmt, W, rows, cols)
+    _check_w(fmt, W, wrows, cols)
     _check_dev(x, "x", torch.float32)
     if x.numel() < cols:
         raise ValueError("x is too small")
@@ -140,11 +143,29 @@ def gq_matvec(fmt: int, W, rows: int, cols: int, x, y=None, stream=None):
     _check_dev(y, "y", torch.float32)
     if y.numel() < rows:
         raise ValueError("y is too small")
-    st = load_library().gq_matvec(int(fmt), _ptr(W), int(rows), int(cols), _ptr(x), _ptr(y),
-                                  _stream_handle(stream))
+    st = getattr(load_library(), name)(int(fmt), _ptr(W), int(rows), int(cols), _ptr(x), _ptr(y),
+                                       _stream_handle(stream))
     if st != GQ_OK:
-        raise GQError(st, "gq_matvec")
+        raise GQError(st, name)
     return y
+
+
+def gq_matvec(fmt: int, W, rows: int, cols: int, x, y=None, stream=None):
+    """y = W x on `stream` (default: torch's current stream), asynchronous."""
+    return _matvec("gq_matvec", fmt, W, rows, cols, x, y, stream, rows)
+
+
+def gq_matvec_acc(fmt: int, W, rows: int, cols: int, x, y, stream=None):
+    """y += W x (y holds the addend), asynchronous."""
+    if y is None:
+        raise ValueError("gq_matvec_acc needs y")
+    return _matvec("gq_matvec_acc", fmt, W, rows, cols, x, y, stream, rows)
+
+
+def gq_matvec_swiglu(fmt: int, W, rows: int, cols: int, x, y=None, stream=None):
+    """y[r] = silu(g_r) * u_r for the gate|up tensor W (2 * rows weight rows:
+    gate rows first, then up rows), asynchronous."""
+    return _matvec("gq_matvec_swiglu", fmt, W, rows, cols, x, y, stream, 2 * rows)
 
 
 def gq_matmul(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):

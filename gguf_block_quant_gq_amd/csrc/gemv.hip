@@ -78,28 +78,61 @@ constexpr bool is_k56() {
   return std::is_same<typename F::Base, Q5KUnit>::value || std::is_same<typename F::Base, Q6KUnit>::value;
 }
 
-template <class F, int RB>
+// Output rows per group per batch: RB, except for the gate|up epilogue,
+// where a group's two weight rows (r and rows + r) make one output.
+template <int EPI, int RB>
+constexpr int out_rows() {
+  return EPI == kEpiSwiglu ? 1 : RB;
+}
+
+// The weight rows of a batch whose first output row is obase (clamped to
+// the last row: a batch past the end re-reads it and discards the result).
+template <class F, int RB, int EPI>
 __device__ __forceinline__ void load_rows(typename F::Raw (&raw)[RB], const GemvArgs& a,
-                                          int rbase, int unit_ld) {
+                                          int obase, int unit_ld) {
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
-    int row = rbase + i;
-    row = row < a.rows ? row : a.rows - 1;
+    int row;
+    if constexpr (EPI == kEpiSwiglu) {
+      row = (obase < a.rows ? obase : a.rows - 1) + i * a.rows;  // gate, then up
+    } else {
+      row = obase + i;
+      row = row < a.rows ? row : a.rows - 1;
+    }
     F::load(raw[i], a.W + (int64_t)row * a.row_bytes, unit_ld);
   }
 }
 
-template <int G, int RB>
-__device__ __forceinline__ void reduce_store(float (&acc)[RB], const GemvArgs& a, int rbase,
+// silu(g) * u = g / (1 + e^-g) * u, in fp32 (e^-g overflows to inf for very
+// negative g, giving -0 * u).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.f + expf(-g)) * u;
+}
+
+// Write the finished sums of output rows obase.. (v[i] for weight row i of
+// the batch): overwrite, accumulate, or the SwiGLU of the gate|up pair.
+template <int EPI, int RB>
+__device__ __forceinline__ void epi_store(const GemvArgs& a, int obase, const float (&v)[RB]) {
+  if constexpr (EPI == kEpiSwiglu) {
+    if (obase < a.rows) a.y[obase] = silu_mul(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if (obase + i < a.rows) {
+        if constexpr (EPI == kEpiAcc) a.y[obase + i] += v[i];
+        else a.y[obase + i] = v[i];
+      }
+    }
+  }
+}
+
+template <int G, int RB, int EPI>
+__device__ __forceinline__ void reduce_store(float (&acc)[RB], const GemvArgs& a, int obase,
                                              int gl, int grp, float (*red)[RB]) {
   if constexpr (G <= 64) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) acc[i] = group_sum_last<G>(acc[i]);
-    if (gl == G - 1) {
-#pragma unroll
-      for (int i = 0; i < RB; ++i)
-        if (rbase + i < a.rows) a.y[rbase + i] = acc[i];
-    }
+    if (gl == G - 1) epi_store<EPI, RB>(a, obase, acc);
   } else {
     constexpr int kWavesPerGroup = G / 64;
 #pragma unroll
@@ -110,13 +143,16 @@ __device__ __forceinline__ void reduce_store(float (&acc)[RB], const GemvArgs& a
       for (int i = 0; i < RB; ++i) red[tid >> 6][i] = acc[i];
     }
     __syncthreads();
-    if (gl < RB) {
+    if (gl == 0) {
       const int w0 = grp * kWavesPerGroup;
-      float v = red[w0][gl];
+      float v[RB];
 #pragma unroll
-      for (int w = 1; w < kWavesPerGroup; ++w) v += red[w0 + w][gl];
-      const int row = rbase + gl;
-      if (row < a.rows) a.y[row] = v;
+      for (int i = 0; i < RB; ++i) {
+        v[i] = red[w0][i];
+#pragma unroll
+        for (int w = 1; w < kWavesPerGroup; ++w) v[i] += red[w0 + w][i];
+      }
+      epi_store<EPI, RB>(a, obase, v);
     }
     __syncthreads();
   }
@@ -191,11 +227,13 @@ __device__ __forceinline__ void fetch_x(typename F::X& xr, const f32x4* xs, int 
 // the waves' partial sums; instead each wave parks its partials in an LDS
 // ring of kSlots batches and the ring is folded (and y stored) once per
 // kSlots batches, so the waves run unsynchronised in between.
-template <class F, int G, int RB>
+template <class F, int G, int RB, int EPI>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   static_assert(G >= 4 && G <= kThreads && (G & (G - 1)) == 0, "G");
+  static_assert(EPI != kEpiSwiglu || RB == 2, "the gate|up epilogue pairs two rows");
   constexpr int kGroups = kThreads / G;
-  constexpr int kRowsPerIter = kGroups * RB;
+  constexpr int kOut = out_rows<EPI, RB>();
+  constexpr int kRowsPerIter = kGroups * kOut;  // output rows per batch
   constexpr int kWavesPerGroup = G > 64 ? G / 64 : 1;
   constexpr int kSlots = 8;
   constexpr bool kQ8 = is_q8<F>();
@@ -219,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   XStage<F, G> st;
   issue_x<F, G>(st, a.x, a.cols, 0);
   typename F::Raw buf[RB];
-  load_rows<F, RB>(buf, a, it0 * kRowsPerIter + grp * RB, unit_ld);
+  load_rows<F, RB, EPI>(buf, a, it0 * kRowsPerIter + grp * kOut, unit_ld);
   commit_x<F, G>(xs, st);
   __syncthreads();
   typename F::X xr;
@@ -228,14 +266,17 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   // fold the ring: slot s holds batch it0 + (n0 + s) * stride
   auto flush = [&](int n0, int used) {
     __syncthreads();
-    if (gl < used * RB) {
-      const int s = gl / RB, i = gl % RB;
+    if (gl < used) {
+      const int s = gl;
       const int w0 = grp * kWavesPerGroup;
-      float v = ring[s][w0][i];
+      float v[RB];
 #pragma unroll
-      for (int w = 1; w < kWavesPerGroup; ++w) v += ring[s][w0 + w][i];
-      const int row = (it0 + (n0 + s) * stride) * kRowsPerIter + grp * RB + i;
-      if (row < a.rows) a.y[row] = v;
+      for (int i = 0; i < RB; ++i) {
+        v[i] = ring[s][w0][i];
+#pragma unroll
+        for (int w = 1; w < kWavesPerGroup; ++w) v[i] += ring[s][w0 + w][i];
+      }
+      epi_store<EPI, RB>(a, (it0 + (n0 + s) * stride) * kRowsPerIter + grp * kOut, v);
     }
     __syncthreads();
   };
@@ -251,16 +292,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     // more, smaller batches) after it: each order measured faster for its
     // format.
     const int nx = it + stride < iters ? it + stride : iters - 1;
-    if constexpr (!kQ8) load_rows<F, RB>(buf, a, nx * kRowsPerIter + grp * RB, unit_ld);
+    if constexpr (!kQ8) load_rows<F, RB, EPI>(buf, a, nx * kRowsPerIter + grp * kOut, unit_ld);
     if constexpr (G <= 64) {
-      const int rbase = it * kRowsPerIter + grp * RB;
 #pragma unroll
       for (int i = 0; i < RB; ++i) acc[i] = group_sum_last<G>(acc[i]);
-      if (gl == G - 1) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-          if (rbase + i < a.rows) a.y[rbase + i] = acc[i];
-      }
+      if (gl == G - 1) epi_store<EPI, RB>(a, it * kRowsPerIter + grp * kOut, acc);
     } else {
 #pragma unroll
       for (int i = 0; i < RB; ++i) acc[i] = group_sum_last<64>(acc[i]);
@@ -271,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
       }
       if (slot == kSlots - 1) flush(n - (kSlots - 1), kSlots);
     }
-    if constexpr (kQ8) load_rows<F, RB>(buf, a, nx * kRowsPerIter + grp * RB, unit_ld);
+    if constexpr (kQ8) load_rows<F, RB, EPI>(buf, a, nx * kRowsPerIter + grp * kOut, unit_ld);
   }
   if constexpr (G > 64) {
     const int used = n % kSlots;
@@ -281,10 +317,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
 
 // Rows wider than G units: each row batch walks the row in segments of G
 // units, reloading the lane's x values per segment.
-template <class F, int G, int RB>
+template <class F, int G, int RB, int EPI>
 __global__ __launch_bounds__(kThreads) void gemv_seg_kernel(GemvArgs a) {
   constexpr int kGroups = kThreads / G;
-  constexpr int kRowsPerIter = kGroups * RB;
+  constexpr int kOut = out_rows<EPI, RB>();
+  constexpr int kRowsPerIter = kGroups * kOut;
   __shared__ float red[kThreads / 64][RB];
 
   const int tid = threadIdx.x;
@@ -295,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void gemv_seg_kernel(GemvArgs a) {
   const int iters = (a.rows + kRowsPerIter - 1) / kRowsPerIter;
 
   for (int it = blockIdx.x; it < iters; it += gridDim.x) {
-    const int rbase = it * kRowsPerIter + grp * RB;
+    const int obase = it * kRowsPerIter + grp * kOut;
     float acc[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i) acc[i] = 0.f;
@@ -303,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void gemv_seg_kernel(GemvArgs a) {
       const int unit = seg * G + gl;
       const int unit_ld = unit < a.units ? unit : a.units - 1;
       typename F::Raw raw[RB];
-      load_rows<F, RB>(raw, a, rbase, unit_ld);
+      load_rows<F, RB, EPI>(raw, a, obase, unit_ld);
       typename F::X xr;
       if (F::valid(unit, a.units, a.cols)) F::load_x(xr, a.x, unit, a.cols);
       else F::zero_x(xr);
@@ -311,13 +348,13 @@ __global__ __launch_bounds__(kThreads) void gemv_seg_kernel(GemvArgs a) {
 #pragma unroll
       for (int i = 0; i < RB; ++i) acc[i] += F::dot(raw[i], xr, ln);
     }
-    reduce_store<G, RB>(acc, a, rbase, gl, grp, red);
+    reduce_store<G, RB, EPI>(acc, a, obase, gl, grp, red);
   }
 }
 
-template <class F, int G, int RB>
+template <class F, int G, int RB, int EPI>
 hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s) {
-  constexpr int kRowsPerIter = (kThreads / G) * RB;
+  constexpr int kRowsPerIter = (kThreads / G) * out_rows<EPI, RB>();
   const int64_t iters = ((int64_t)a.rows + kRowsPerIter - 1) / kRowsPerIter;
   // As many workgroups as can be resident at once (4 per CU at <= 128
   // VGPRs, else 2); each loops over row batches.
@@ -328,64 +365,79 @@ hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s) {
   const int64_t cap = (int64_t)cus * kPerCu;
   const int blocks = (int)(iters < cap ? iters : cap);
   if (a.units <= G)
-    hipLaunchKernelGGL((gemv_kernel<F, G, RB>), dim3(blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<F, G, RB, EPI>), dim3(blocks), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((gemv_seg_kernel<typename F::Base, G, RB>), dim3(blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemv_seg_kernel<typename F::Base, G, RB, EPI>), dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 // G: the smallest power of two >= the row's units (max 256; wider rows use
 // segments). RB: rows per group per iteration -- 1 when the matrix is too
-// short to give every CU a few groups, else 2.
-template <class F, int G>
+// short to give every CU a few groups, else 2; always 2 (the gate row and
+// the up row) for the gate|up epilogue.
+template <class F, int G, int EPI>
 hipError_t with_g(const GemvArgs& a, int cus, hipStream_t s) {
-  const int64_t groups_needed = (int64_t)cus * GQ_GEMV_RB1_WAVES_PER_CU * (G >= 64 ? 1 : 64 / G);
-  if ((int64_t)a.rows < 2 * groups_needed) return launch_one<F, G, 1>(a, cus, s);
-  // Q5_K / Q6_K on tall matrices (an lm_head, 14336-row projections): one
-  // row per group at more workgroups per CU measured faster (more waves to
-  // hide latency behind their heavier unpacking); two rows per group stay
-  // ahead for shorter matrices and for wide rows.
-  if constexpr (is_k56<F>() && G <= 128) {
-    if ((int64_t)a.rows >= 4 * groups_needed) return launch_one<F, G, 1>(a, cus, s);
+  if constexpr (EPI == kEpiSwiglu) {
+    return launch_one<F, G, 2, EPI>(a, cus, s);
+  } else {
+    const int64_t groups_needed = (int64_t)cus * GQ_GEMV_RB1_WAVES_PER_CU * (G >= 64 ? 1 : 64 / G);
+    if ((int64_t)a.rows < 2 * groups_needed) return launch_one<F, G, 1, EPI>(a, cus, s);
+    // Q5_K / Q6_K on tall matrices (an lm_head, 14336-row projections): one
+    // row per group at more workgroups per CU measured faster (more waves to
+    // hide latency behind their heavier unpacking); two rows per group stay
+    // ahead for shorter matrices and for wide rows.
+    if constexpr (is_k56<F>() && G <= 128) {
+      if ((int64_t)a.rows >= 4 * groups_needed) return launch_one<F, G, 1, EPI>(a, cus, s);
+    }
+    constexpr int kRB = is_q8<F>() ? GQ_GEMV_Q8_RBN : is_k56<F>() ? GQ_GEMV_K56_RBN : GQ_GEMV_RBN;
+    return launch_one<F, G, kRB, EPI>(a, cus, s);
   }
-  constexpr int kRB = is_q8<F>() ? GQ_GEMV_Q8_RBN : is_k56<F>() ? GQ_GEMV_K56_RBN : GQ_GEMV_RBN;
-  return launch_one<F, G, kRB>(a, cus, s);
+}
+
+template <class F, int EPI>
+hipError_t dispatch_g(const GemvArgs& a, int cus, hipStream_t s) {
+  const int n = a.units;
+  if (n <= 4) return with_g<F, 4, EPI>(a, cus, s);
+  if (n <= 8) return with_g<F, 8, EPI>(a, cus, s);
+  if (n <= 16) return with_g<F, 16, EPI>(a, cus, s);
+  if (n <= 32) return with_g<F, 32, EPI>(a, cus, s);
+  if (n <= 64) return with_g<F, 64, EPI>(a, cus, s);
+  if (n <= 128) return with_g<F, 128, EPI>(a, cus, s);
+  return with_g<F, 256, EPI>(a, cus, s);
 }
 
 template <class F>
-hipError_t dispatch(const GemvArgs& a, int cus, hipStream_t s) {
-  const int n = a.units;
-  if (n <= 4) return with_g<F, 4>(a, cus, s);
-  if (n <= 8) return with_g<F, 8>(a, cus, s);
-  if (n <= 16) return with_g<F, 16>(a, cus, s);
-  if (n <= 32) return with_g<F, 32>(a, cus, s);
-  if (n <= 64) return with_g<F, 64>(a, cus, s);
-  if (n <= 128) return with_g<F, 128>(a, cus, s);
-  return with_g<F, 256>(a, cus, s);
+hipError_t dispatch(const GemvArgs& a, int cus, hipStream_t s, int epi) {
+  switch (epi) {
+    case kEpiStore: return dispatch_g<F, kEpiStore>(a, cus, s);
+    case kEpiAcc: return dispatch_g<F, kEpiAcc>(a, cus, s);
+    case kEpiSwiglu: return dispatch_g<F, kEpiSwiglu>(a, cus, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s) {
+hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi) {
   if (fmt == kFmtQ8_0) {
     const int blocks = (a.cols + 31) / 32;
     // an even block count keeps every row 4-byte aligned: pairs of blocks
     if (blocks % 2 == 0 && (uintptr_t)a.W % 4 == 0) {
       a.units = blocks / 2;
-      return dispatch<Q8PairUnit>(a, cus, s);
+      return dispatch<Q8PairUnit>(a, cus, s, epi);
     }
     a.units = blocks;
-    return dispatch<Q8Unit>(a, cus, s);
+    return dispatch<Q8Unit>(a, cus, s, epi);
   }
   if (fmt == kFmtQ5_0) {
     a.units = (a.cols + 31) / 32;
-    return dispatch<Q5_0Unit>(a, cus, s);
+    return dispatch<Q5_0Unit>(a, cus, s, epi);
   }
   // K-quants: four units per 256-weight super-block
   a.units = 4 * ((a.cols + 255) / 256);
-  if (fmt == kFmtQ5_K) return dispatch<Q5KUnit>(a, cus, s);
-  if (fmt == kFmtQ6_K) return dispatch<Q6KUnit>(a, cus, s);
-  return dispatch<Q4KUnit>(a, cus, s);
+  if (fmt == kFmtQ5_K) return dispatch<Q5KUnit>(a, cus, s, epi);
+  if (fmt == kFmtQ6_K) return dispatch<Q6KUnit>(a, cus, s, epi);
+  return dispatch<Q4KUnit>(a, cus, s, epi);
 }
 
 }  // namespace gq

@@ -108,10 +108,16 @@ extern "C" int gq_dequant(int fmt, const void* W, int64_t rows, int64_t cols, fl
   return finish(hipStreamSynchronize(0));
 }
 
-extern "C" int gq_matvec(int fmt, const void* W, int64_t rows, int64_t cols, const float* x,
-                         float* y, void* stream) {
+namespace {
+
+// Shared by the three matvec entry points: validation, then one launch. The
+// gate|up epilogue reads 2 * rows weight rows and writes rows outputs.
+int matvec_common(int fmt, const void* W, int64_t rows, int64_t cols, const float* x, float* y,
+                  void* stream, int epi) {
+  const int64_t wmul = epi == gq::kEpiSwiglu ? 2 : 1;
+  if (rows > INT_MAX / wmul) return GQ_ERR_SHAPE;
   int64_t rb = 0, wbytes = 0;
-  int st = check_shape(fmt, rows, cols, 1, &rb, &wbytes);
+  int st = check_shape(fmt, rows * wmul, cols, 1, &rb, &wbytes);
   if (st != GQ_OK) return st;
   if (rows == 0) return GQ_OK;
   if (!W || !x || !y) return GQ_ERR_NULL;
@@ -123,7 +129,24 @@ extern "C" int gq_matvec(int fmt, const void* W, int64_t rows, int64_t cols, con
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
   gq::GemvArgs a{(const uint8_t*)W, x, y, rb, (int)rows, (int)cols, 0};
-  return finish(gq::launch_gemv(fmt, a, cus, (hipStream_t)stream));
+  return finish(gq::launch_gemv(fmt, a, cus, (hipStream_t)stream, epi));
+}
+
+}  // namespace
+
+extern "C" int gq_matvec(int fmt, const void* W, int64_t rows, int64_t cols, const float* x,
+                         float* y, void* stream) {
+  return matvec_common(fmt, W, rows, cols, x, y, stream, gq::kEpiStore);
+}
+
+extern "C" int gq_matvec_acc(int fmt, const void* W, int64_t rows, int64_t cols, const float* x,
+                             float* y, void* stream) {
+  return matvec_common(fmt, W, rows, cols, x, y, stream, gq::kEpiAcc);
+}
+
+extern "C" int gq_matvec_swiglu(int fmt, const void* W, int64_t rows, int64_t cols,
+                                const float* x, float* y, void* stream) {
+  return matvec_common(fmt, W, rows, cols, x, y, stream, gq::kEpiSwiglu);
 }
 
 extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,

@@ -18,9 +18,16 @@ struct GemvArgs {
   const float* x;
   float* y;
   int64_t row_bytes;
-  int rows;
+  int rows;   // output rows (the gate|up epilogue reads 2 * rows weight rows)
   int cols;
   int units;  // units per row (set by the launcher)
+};
+
+// What the matvec does with each finished row sum.
+enum GemvEpilogue : int {
+  kEpiStore = 0,   // y[r] = sum
+  kEpiAcc = 1,     // y[r] += sum
+  kEpiSwiglu = 2,  // y[r] = silu(sum of row r) * (sum of row rows + r)
 };
 
 struct DequantArgs {
@@ -46,7 +53,7 @@ struct GemmArgs {
 // All launchers enqueue on `s` and return the launch status.
 // `units` is filled in by the launcher; `cus` is the device's CU count.
 hipError_t launch_dequant(int fmt, DequantArgs a, hipStream_t s);
-hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s);
+hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi = kEpiStore);
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
 hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s);
 

@@ -129,6 +129,34 @@ int gq_matvec(int fmt, const void* W, int64_t rows, int64_t cols,
               const float* x, float* y, void* stream);
 
 /*
+ * y[r] += sum_{c < cols} w(r, c) * x[c] for r < rows: the matvec with its
+ * result added to y (one fp32 addition per output) instead of overwriting
+ * it, for a projection that feeds a residual stream (the llama shape has
+ * residuals around attention and the feed-forward: "nurllama 0.18.1 API",
+ * model.nu section; its kernels.nu section lists the separate vector add
+ * this removes, and the Loom inventory has an "acc" mode for its GEMMs). Same arguments, accuracy and stream behaviour as gq_matvec; y
+ * must hold the addend.
+ */
+int gq_matvec_acc(int fmt, const void* W, int64_t rows, int64_t cols,
+                  const float* x, float* y, void* stream);
+
+/*
+ * The gate|up projection of a SwiGLU feed-forward with its activation fused
+ * in: W holds 2*rows weight rows, the gate rows 0..rows-1 followed by the up
+ * rows rows..2*rows-1 (one tensor whose parts are row ranges, as the
+ * "nurllama" README, "What it runs", describes for phi3's fused ffn_up), and
+ *   y[r] = silu(g_r) * u_r,  g_r = sum_c w(r, c) x[c],  u_r = sum_c w(rows+r, c) x[c],
+ * silu(g) = g / (1 + exp(-g)) ("nurllama 0.18.1 API", kernels.nu section:
+ * the in-place g <- silu(g) * u kernel that follows the two matvecs). One
+ * launch: each row group computes its gate and up sums together and applies
+ * the activation before the single store. g_r and u_r are bit-identical to
+ * what gq_matvec returns for those rows; the activation is evaluated in
+ * fp32. W holds 2*rows*gq_row_bytes(fmt, cols) bytes; y: rows floats.
+ */
+int gq_matvec_swiglu(int fmt, const void* W, int64_t rows, int64_t cols,
+                     const float* x, float* y, void* stream);
+
+/*
  * Y[m*rows + r] = sum_{c < cols} w(r, c) * X[m*cols + c], for m < M, r < rows;
  * Y is overwritten. X: [M, cols] row-major fp32; Y: [M, rows] row-major fp32.
  * The batched form used for prompt chunks ("nurllama 0.18.1 API", model.nu

@@ -70,6 +70,14 @@ def _mv(lib, fmt=12, W=W_OK, rows=4, cols=256, x=X_OK, y=Y_OK):
     return lib.gq_matvec(fmt, W, rows, cols, x, y, None)
 
 
+def _mva(lib, fmt=12, W=W_OK, rows=4, cols=256, x=X_OK, y=Y_OK):
+    return lib.gq_matvec_acc(fmt, W, rows, cols, x, y, None)
+
+
+def _mvs(lib, fmt=12, W=W_OK, rows=4, cols=256, x=X_OK, y=Y_OK):
+    return lib.gq_matvec_swiglu(fmt, W, rows, cols, x, y, None)
+
+
 def _mm(lib, fmt=12, W=W_OK, rows=4, cols=256, X=X_OK, M=2, Y=Y_OK):
     return lib.gq_matmul(fmt, W, rows, cols, X, M, Y, None)
 
@@ -78,7 +86,7 @@ def _dq(lib, fmt=12, W=W_OK, rows=4, cols=256, out=Y_OK):
     return lib.gq_dequant(fmt, W, rows, cols, out)
 
 
-@pytest.mark.parametrize("call", [_mv, _mm, _dq])
+@pytest.mark.parametrize("call", [_mv, _mva, _mvs, _mm, _dq])
 def test_validation_before_any_device_call(lib, call):
     for bad in (0, 7, 10, 11, 15, -1):   # Q5_1, Q2_K, Q3_K, IQ... have no kernels
         assert call(lib, fmt=bad) == gq.GQ_ERR_FMT
@@ -114,6 +122,13 @@ def test_validation_vectors(lib):
     # a Q8_0 row range may start on any 34-byte block, i.e. a 2-byte boundary
     # (the alignment check passes, the overlap check after it fires)
     assert _mv(lib, fmt=8, W=W_OK + 34, y=W_OK + 40) == gq.GQ_ERR_OVERLAP
+    # the gate|up epilogue reads 2 * rows weight rows: an output placed just
+    # past rows * row_bytes still overlaps W; 2^30 rows overflow the row index
+    assert _mvs(lib, rows=4, y=W_OK + 4 * 144) == gq.GQ_ERR_OVERLAP
+    assert _mv(lib, rows=4, y=W_OK + 4 * 144) != gq.GQ_ERR_OVERLAP
+    assert _mvs(lib, rows=1 << 30) == gq.GQ_ERR_SHAPE
+    assert _mva(lib, y=None) == gq.GQ_ERR_NULL
+    assert _mva(lib, y=W_OK + 8) == gq.GQ_ERR_OVERLAP
     # likewise Q5_0 (22-byte blocks) and Q6_K (210-byte super-blocks)
     assert _mv(lib, fmt=6, W=W_OK + 22, y=W_OK + 24) == gq.GQ_ERR_OVERLAP
     assert _mv(lib, fmt=14, W=W_OK + 210, y=W_OK + 212) == gq.GQ_ERR_OVERLAP
