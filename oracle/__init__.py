@@ -188,3 +188,24 @@ def swiglu_matvec(fmt: int, W, rows: int, cols: int, x, nthreads: int = 1):
     g, u = Y[:rows], Y[rows:]
     return silu(g) * u, g, u, S[:rows], S[rows:]
 
+
+def experts_matvec(fmt: int, W, n_expert: int, rows: int, cols: int, X, xk: int, expid,
+                   nthreads: int = 1):
+    """The expert-batched matvec of a mixture-of-experts layer ("nurllama
+    0.18.1 API", kernels.nu section: one batched matvec over all expert
+    assignments, output row a using expert expid[a] and input row a / xk of
+    x). W holds the n_expert matrices back to back. Returns (Y, S), both
+    [n_assign, rows] f64; an id outside [0, n_expert) gives a NaN row."""
+    Wb = _as_bytes(W)
+    eb = rows * row_bytes(fmt, cols)
+    if Wb.size < n_expert * eb:
+        raise ValueError("W holds fewer bytes than n_expert * rows * row_bytes")
+    X = np.ascontiguousarray(X, dtype=np.float32).reshape(-1, cols)
+    ids = np.asarray(expid, dtype=np.int64).reshape(-1)
+    Y = np.full((ids.size, rows), np.nan)
+    S = np.full((ids.size, rows), np.nan)
+    for a, e in enumerate(ids):
+        if 0 <= e < n_expert:
+            Y[a], S[a] = matvec(fmt, Wb[e * eb:(e + 1) * eb], rows, cols, X[a // xk], nthreads)
+    return Y, S
+
