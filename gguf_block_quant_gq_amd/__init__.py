@@ -9,6 +9,8 @@ is no CPU fallback: if the library is not built, loading raises.
     gq_matvec(fmt, W, rows, cols, x, y=None)           -> y [rows] fp32
     gq_matvec_acc(fmt, W, rows, cols, x, y)            -> y += W x
     gq_matvec_swiglu(fmt, W, rows, cols, x, y=None)    -> y = silu(W_gate x) * (W_up x)
+    gq_matvec_experts(fmt, W, n_expert, rows, cols, X, xk, expid, Y=None)
+                                                       -> Y[a] = W[expid[a]] X[a // xk]
     gq_matmul(fmt, W, rows, cols, X, Y=None)           -> Y [M, rows] fp32
 
 W is a uint8 CUDA tensor holding rows * gq_row_bytes(fmt, cols) bytes of
@@ -38,7 +40,7 @@ GQ_ERR_DEVICE = 5
 GQ_ERR_OVERLAP = 6
 
 EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matvec_acc",
-           "gq_matvec_swiglu", "gq_matmul")
+           "gq_matvec_swiglu", "gq_matvec_experts", "gq_matmul")
 
 _lib = None
 
@@ -68,6 +70,8 @@ def load_library():
     for name in ("gq_matvec", "gq_matvec_acc", "gq_matvec_swiglu"):
         getattr(lib, name).argtypes = [i32, vp, i64, i64, vp, vp, vp]
         getattr(lib, name).restype = i32
+    lib.gq_matvec_experts.argtypes = [i32, vp, i64, i64, i64, vp, i64, vp, i64, vp, vp]
+    lib.gq_matvec_experts.restype = i32
     lib.gq_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
     lib.gq_matmul.restype = i32
     _lib = lib
@@ -166,6 +170,30 @@ def gq_matvec_swiglu(fmt: int, W, rows: int, cols: int, x, y=None, stream=None):
     """y[r] = silu(g_r) * u_r for the gate|up tensor W (2 * rows weight rows:
     gate rows first, then up rows), asynchronous."""
     return _matvec("gq_matvec_swiglu", fmt, W, rows, cols, x, y, stream, 2 * rows)
+
+
+def gq_matvec_experts(fmt: int, W, n_expert: int, rows: int, cols: int, X, xk: int, expid,
+                      Y=None, stream=None):
+    """Y[a] = W[expid[a]] @ X[a // xk] for every assignment a (expid: int32
+    CUDA tensor of n_assign ids), asynchronous."""
+    torch = _torch()
+    _check_w(fmt, W, n_expert * rows, cols)
+    _check_dev(X, "X", torch.float32)
+    _check_dev(expid, "expid", torch.int32)
+    n_assign = expid.numel()
+    if X.numel() < -(-n_assign // max(1, xk)) * cols:
+        raise ValueError("X is too small")
+    if Y is None:
+        Y = torch.empty((n_assign, rows), dtype=torch.float32, device=W.device)
+    _check_dev(Y, "Y", torch.float32)
+    if Y.numel() < n_assign * rows:
+        raise ValueError("Y is too small")
+    st = load_library().gq_matvec_experts(int(fmt), _ptr(W), int(n_expert), int(rows), int(cols),
+                                          _ptr(X), int(xk), _ptr(expid), int(n_assign), _ptr(Y),
+                                          _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_matvec_experts")
+    return Y
 
 
 def gq_matmul(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):

@@ -223,13 +223,34 @@ __device__ __forceinline__ void fetch_x(typename F::X& xr, const f32x4* xs, int 
 }
 
 // Rows fit in one segment: x stays in registers for the whole kernel.
+// Expert-batched calls: point a (the workgroup's copy of the arguments) at
+// the expert, activation row and output row of assignment blockIdx.y. An
+// expert id outside [0, n_expert) reads no weights: the assignment's output
+// row is filled with NaN instead. Returns false when there is nothing more
+// to do.
+__device__ __forceinline__ bool bind_assignment(GemvArgs& a) {
+  const int as = blockIdx.y;
+  const int e = a.expid[as];
+  a.x += (int64_t)(as / a.xk) * a.cols;
+  a.y += (int64_t)as * a.rows;
+  if (e < 0 || e >= a.n_expert) {
+    for (int r = blockIdx.x * kThreads + threadIdx.x; r < a.rows; r += gridDim.x * kThreads)
+      a.y[r] = __builtin_nanf("");
+    return false;
+  }
+  a.W += (int64_t)e * a.expert_bytes;
+  return true;
+}
+
 // Row groups wider than a wave (G > 64) would need a barrier per batch to add
 // the waves' partial sums; instead each wave parks its partials in an LDS
 // ring of kSlots batches and the ring is folded (and y stored) once per
 // kSlots batches, so the waves run unsynchronised in between.
 template <class F, int G, int RB, int EPI>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs args) {
   static_assert(G >= 4 && G <= kThreads && (G & (G - 1)) == 0, "G");
+  GemvArgs a = args;
+  if (a.expid && !bind_assignment(a)) return;  // uniform per workgroup
   static_assert(EPI != kEpiSwiglu || RB == 2, "the gate|up epilogue pairs two rows");
   constexpr int kGroups = kThreads / G;
   constexpr int kOut = out_rows<EPI, RB>();
@@ -318,7 +339,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
 // Rows wider than G units: each row batch walks the row in segments of G
 // units, reloading the lane's x values per segment.
 template <class F, int G, int RB, int EPI>
-__global__ __launch_bounds__(kThreads) void gemv_seg_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kThreads) void gemv_seg_kernel(GemvArgs args) {
+  GemvArgs a = args;
+  if (a.expid && !bind_assignment(a)) return;  // uniform per workgroup
   constexpr int kGroups = kThreads / G;
   constexpr int kOut = out_rows<EPI, RB>();
   constexpr int kRowsPerIter = kGroups * kOut;
@@ -362,12 +385,15 @@ hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s) {
   constexpr int kPerCu = kQ8 ? GQ_GEMV_Q8_WG_PER_CU
                          : RB == 1 ? GQ_GEMV_WG_PER_CU_RB1
                          : is_k56<F>() ? GQ_GEMV_K56_WG_PER_CU : GQ_GEMV_WG_PER_CU_RBN;
-  const int64_t cap = (int64_t)cus * kPerCu;
+  // (expert-batched calls share that many workgroups among their assignments)
+  int64_t cap = (int64_t)cus * kPerCu / a.n_assign;
+  if (cap < 1) cap = 1;
   const int blocks = (int)(iters < cap ? iters : cap);
+  const dim3 grid(blocks, a.n_assign);
   if (a.units <= G)
-    hipLaunchKernelGGL((gemv_kernel<F, G, RB, EPI>), dim3(blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<F, G, RB, EPI>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((gemv_seg_kernel<typename F::Base, G, RB, EPI>), dim3(blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemv_seg_kernel<typename F::Base, G, RB, EPI>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

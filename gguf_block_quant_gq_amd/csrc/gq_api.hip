@@ -149,6 +149,41 @@ extern "C" int gq_matvec_swiglu(int fmt, const void* W, int64_t rows, int64_t co
   return matvec_common(fmt, W, rows, cols, x, y, stream, gq::kEpiSwiglu);
 }
 
+extern "C" int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64_t rows,
+                                 int64_t cols, const float* X, int64_t xk, const int32_t* expid,
+                                 int64_t n_assign, float* Y, void* stream) {
+  int64_t rb = 0, ebytes = 0;
+  int st = check_shape(fmt, rows, cols, 1, &rb, &ebytes);
+  if (st != GQ_OK) return st;
+  // the assignments are the grid's second dimension (at most 65535)
+  if (n_expert < 1 || n_expert > INT_MAX || xk < 1 || xk > INT_MAX || n_assign < 0 ||
+      n_assign > 65535)
+    return GQ_ERR_SHAPE;
+  if (rows == 0 || n_assign == 0) return GQ_OK;
+  if (ebytes > INT64_MAX / n_expert) return GQ_ERR_SHAPE;
+  const int64_t wbytes = ebytes * n_expert;
+  const int64_t xrows = (n_assign + xk - 1) / xk;
+  if (rows > INT64_MAX / 4 / n_assign) return GQ_ERR_SHAPE;
+  const int64_t xbytes = xrows * cols * 4, ybytes = n_assign * rows * 4;
+  if (!W || !X || !expid || !Y) return GQ_ERR_NULL;
+  if ((st = check_align(fmt, W)) != GQ_OK) return st;
+  if ((uintptr_t)X % 4 || (uintptr_t)Y % 4 || (uintptr_t)expid % 4) return GQ_ERR_ALIGN;
+  if (overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, X, xbytes) ||
+      overlaps(Y, ybytes, expid, n_assign * 4))
+    return GQ_ERR_OVERLAP;
+
+  const int cus = current_cus();
+  if (cus <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  gq::GemvArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
+  a.expid = expid;
+  a.expert_bytes = ebytes;
+  a.n_expert = (int)n_expert;
+  a.xk = (int)xk;
+  a.n_assign = (int)n_assign;
+  return finish(gq::launch_gemv(fmt, a, cus, (hipStream_t)stream, gq::kEpiStore));
+}
+
 extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,
                          int64_t M, float* Y, void* stream) {
   int64_t rb = 0, wbytes = 0;

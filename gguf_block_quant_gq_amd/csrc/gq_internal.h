@@ -21,6 +21,14 @@ struct GemvArgs {
   int rows;   // output rows (the gate|up epilogue reads 2 * rows weight rows)
   int cols;
   int units;  // units per row (set by the launcher)
+  // Expert-batched form (null expid: a single matvec). Assignment a =
+  // blockIdx.y multiplies expert expid[a] (at W + expid[a] * expert_bytes)
+  // by activation row a / xk of x and writes row a of y (rows floats each).
+  const int32_t* expid = nullptr;
+  int64_t expert_bytes = 0;
+  int n_expert = 0;
+  int xk = 1;
+  int n_assign = 1;
 };
 
 // What the matvec does with each finished row sum.

@@ -157,6 +157,26 @@ int gq_matvec_swiglu(int fmt, const void* W, int64_t rows, int64_t cols,
                      const float* x, float* y, void* stream);
 
 /*
+ * Expert-batched matvec for mixture-of-experts layers: one call over all
+ * n_assign (position, expert) assignments ("nurllama 0.18.1 API", kernels.nu
+ * section: the batched expert matvec, where output row a uses expert
+ * expid[a] and input row a / xk of x):
+ *   Y[a*rows + r] = sum_{c < cols} w_e(r, c) * X[(a / xk)*cols + c],  e = expid[a],
+ * for a < n_assign, r < rows. W holds the n_expert matrices back to back
+ * (a fused 3-D expert tensor: expert e's rows start at byte
+ * e * rows * gq_row_bytes(fmt, cols)); X is [ceil(n_assign / xk), cols]
+ * (xk = experts per position); expid is a device array of n_assign int32
+ * expert ids; Y is [n_assign, rows]. Each assignment is the gq_matvec of its
+ * expert and activation row, bit for bit. An id outside [0, n_expert) reads
+ * no weights and fills that assignment's output row with NaN (the ids live
+ * on the device, so they cannot be checked before the launch). n_assign is
+ * at most 65535 (GQ_ERR_SHAPE beyond). Asynchronous on `stream`.
+ */
+int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, int64_t cols,
+                      const float* X, int64_t xk, const int32_t* expid, int64_t n_assign,
+                      float* Y, void* stream);
+
+/*
  * Y[m*rows + r] = sum_{c < cols} w(r, c) * X[m*cols + c], for m < M, r < rows;
  * Y is overwritten. X: [M, cols] row-major fp32; Y: [M, rows] row-major fp32.
  * The batched form used for prompt chunks ("nurllama 0.18.1 API", model.nu

@@ -132,3 +132,27 @@ def test_validation_vectors(lib):
     # likewise Q5_0 (22-byte blocks) and Q6_K (210-byte super-blocks)
     assert _mv(lib, fmt=6, W=W_OK + 22, y=W_OK + 24) == gq.GQ_ERR_OVERLAP
     assert _mv(lib, fmt=14, W=W_OK + 210, y=W_OK + 212) == gq.GQ_ERR_OVERLAP
+
+
+def _mx(lib, fmt=12, W=W_OK, n_expert=4, rows=4, cols=256, X=X_OK, xk=2, expid=0x40000,
+        n_assign=8, Y=Y_OK):
+    return lib.gq_matvec_experts(fmt, W, n_expert, rows, cols, X, xk, expid, n_assign, Y, None)
+
+
+def test_validation_experts(lib):
+    for bad in (0, 7, 15):
+        assert _mx(lib, fmt=bad) == gq.GQ_ERR_FMT
+    assert _mx(lib, n_expert=0) == gq.GQ_ERR_SHAPE
+    assert _mx(lib, xk=0) == gq.GQ_ERR_SHAPE
+    assert _mx(lib, n_assign=-1) == gq.GQ_ERR_SHAPE
+    assert _mx(lib, n_assign=65536) == gq.GQ_ERR_SHAPE
+    assert _mx(lib, cols=0) == gq.GQ_ERR_SHAPE
+    assert _mx(lib, n_assign=0, W=None, expid=None) == gq.GQ_OK
+    assert _mx(lib, rows=0, W=None) == gq.GQ_OK
+    assert _mx(lib, expid=None) == gq.GQ_ERR_NULL
+    assert _mx(lib, X=None) == gq.GQ_ERR_NULL
+    assert _mx(lib, W=W_OK + 2) == gq.GQ_ERR_ALIGN
+    assert _mx(lib, expid=0x40002) == gq.GQ_ERR_ALIGN
+    # Y overlapping the expert ids, or the last expert's weights
+    assert _mx(lib, expid=Y_OK + 16) == gq.GQ_ERR_OVERLAP
+    assert _mx(lib, Y=W_OK + 4 * 4 * 144 - 4) == gq.GQ_ERR_OVERLAP

@@ -1,0 +1,75 @@
+"""gq_matvec_experts on the GPU: every assignment equals the plain gq_matvec
+of its expert and activation row bit for bit, the outputs are within the
+product tolerance of the f64 oracle, invalid expert ids give NaN rows
+without disturbing the others, and shapes cover mixture-of-experts decode
+(top-k of many small experts) and prefill-sized assignment batches."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import assert_within_tolerance, oracle_threads, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+# (fmt, n_expert, rows, cols, positions, xk)
+CASES = [
+    (12, 16, 768, 2048, 1, 8),     # 128-expert-style gate/up expert, top-8 decode
+    (12, 16, 2048, 768, 1, 8),     # its down projection (three 256-column super-blocks)
+    (8, 8, 768, 2048, 2, 4),       # Q8_0 experts (block pairs)
+    (14, 8, 2048, 768, 1, 8),      # Q6_K down experts
+    (13, 8, 768, 2048, 3, 2),      # Q5_K
+    (6, 4, 300, 896, 2, 2),        # Q5_0, 896-wide
+    (12, 8, 14336, 4096, 1, 2),    # Mixtral-style experts, top-2
+    (12, 6, 64, 1024, 48, 8),      # a prefill batch: 384 assignments
+    (12, 3, 5, 300, 5, 1),         # ragged rows, one expert per position
+    (8, 5, 9, 40000, 1, 3),        # rows wider than 256 units: segmented kernel
+]
+
+
+@pytest.mark.parametrize("fmt,n_expert,rows,cols,positions,xk", CASES)
+def test_experts(gq, oracle, fmt, n_expert, rows, cols, positions, xk):
+    import torch
+    rng = synth.rng_for(960, fmt * 10 ** 6 + n_expert * 1000 + rows)
+    W = synth.weights(fmt, n_expert * rows, cols, rng)
+    X = synth.activations((positions, cols), rng)
+    n_assign = positions * xk
+    expid = rng.integers(0, n_expert, n_assign).astype(np.int32)
+    print(f"[experts] fmt={fmt} n_expert={n_expert} rows={rows} cols={cols} "
+          f"n_assign={n_assign}", flush=True)
+    Wd, Xd = to_dev(W), to_dev(X)
+    Y = torch.full((n_assign + 1, rows), float("nan"), dtype=torch.float32, device="cuda")
+    gq.gq_matvec_experts(fmt, Wd, n_expert, rows, cols, Xd, xk, to_dev(expid), Y=Y)
+    got = to_host(Y)
+    assert np.isnan(got[n_assign]).all(), "wrote past the last assignment"
+    got = got[:n_assign]
+    ref, S = oracle.experts_matvec(fmt, W, n_expert, rows, cols, X, xk, expid,
+                                   nthreads=oracle_threads())
+    assert_within_tolerance(got, ref, S, "experts")
+    # each assignment is the plain matvec of its expert, bit for bit
+    rb = gq.gq_row_bytes(fmt, cols)
+    for a in sorted(set([0, n_assign - 1] + list(range(0, n_assign, max(1, n_assign // 6))))):
+        e = int(expid[a])
+        y = gq.gq_matvec(fmt, Wd[e * rows * rb:(e + 1) * rows * rb], rows, cols, Xd[a // xk])
+        assert np.array_equal(to_host(y).view(np.uint32), got[a].view(np.uint32)), a
+
+
+def test_invalid_ids_and_empty(gq, oracle):
+    import torch
+    fmt, n_expert, rows, cols = 12, 4, 300, 1024
+    rng = synth.rng_for(961, 0)
+    W = synth.weights(fmt, n_expert * rows, cols, rng)
+    X = synth.activations((3, cols), rng)
+    expid = np.array([3, -1, 0, 4, 2, 1 << 30], np.int32)
+    Wd, Xd = to_dev(W), to_dev(X)
+    Y = gq.gq_matvec_experts(fmt, Wd, n_expert, rows, cols, Xd, 2, to_dev(expid))
+    got = to_host(Y)
+    for a in (1, 3, 5):
+        assert np.isnan(got[a]).all(), a
+    ref, S = oracle.experts_matvec(fmt, W, n_expert, rows, cols, X, 2, expid)
+    for a in (0, 2, 4):
+        assert_within_tolerance(got[a], ref[a], S[a], f"assignment {a}")
+    # no assignments: nothing is launched or written
+    Y0 = torch.full((1, rows), 7.0, device="cuda")
+    gq.gq_matvec_experts(fmt, Wd, n_expert, rows, cols, Xd, 2,
+                         torch.empty(0, dtype=torch.int32, device="cuda"), Y=Y0)
+    assert (to_host(Y0) == 7.0).all()
