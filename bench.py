@@ -79,7 +79,7 @@ def gemv_bytes(fmt_row_bytes: int, rows: int, cols: int) -> int:
     return rows * fmt_row_bytes + 4 * cols + 4 * rows
 
 
-DOMINANT_KERNEL = "gemv_kernel<Q4KUnit, 64, 2>"
+DOMINANT_KERNEL = "gemv_kernel<Q4KUnit, 64, 2, 0, false>"  # unit, group width, rows per group, store epilogue, not expert-batched
 # HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE
 # and WRITE_SIZE (bench.py --traffic-probe), each scaled by the same counter
 # on a 256 MiB plain copy (FETCH x 2.000, WRITE x 1.000); set to None whenever
@@ -393,6 +393,41 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
                          pct_hbm=round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1))
         del cs, g
     log(f"mixed formats: { {k: out[k] for k, *_ in synth.MIXED_FORMATS} }")
+
+    # mixture-of-experts decode: one expert-batched launch per layer
+    # projection (Qwen3-30B-A3B-style: 128 experts of 768 x 2048, top 8;
+    # Mixtral-style: 8 experts of 14336 x 4096, top 2), random distinct
+    # expert ids per call. The 128-expert tensor (113 MB) fits in the 256 MB
+    # Infinity Cache, so its figure is partly warm; the 8-expert one (264 MB)
+    # is not.
+    for name, (f, n_expert, r, c, topk) in {
+            "moe_top8_of_128_768x2048_q4_k": (12, 128, 768, 2048, 8),
+            "moe_top2_of_8_14336x4096_q4_k": (12, 8, 14336, 4096, 2)}.items():
+        rng = synth.rng_for(6, n_expert)
+        W = synth.weights(f, n_expert * r, c, rng)
+        Wd = torch.from_numpy(W).cuda()
+        del W
+        xd2 = torch.from_numpy(synth.activations(c, rng)).cuda()
+        ncall = 16
+        ids = [torch.from_numpy(rng.permutation(n_expert)[:topk].astype(np.int32)).cuda()
+               for _ in range(ncall)]
+        Y2 = torch.empty((topk, r), dtype=torch.float32, device="cuda")
+        b = topk * gemv_bytes(gq.gq_row_bytes(f, c), r, c)
+
+        def moe(f=f, n_expert=n_expert, r=r, c=c, topk=topk, Wd=Wd, xd2=xd2, ids=ids, Y2=Y2):
+            sp = stream_ptr()
+            for e in ids:
+                st = lib.gq_matvec_experts(f, Wd.data_ptr(), n_expert, r, c, xd2.data_ptr(), topk,
+                                           e.data_ptr(), topk, Y2.data_ptr(), sp)
+                assert st == 0
+
+        g = capture(torch, moe)
+        ms = timer.time(g.replay, max(5, iters // 2), warmup=2) / ncall
+        out[name] = dict(us_per_call=round(ms * 1e3, 2), expert_bytes_per_call=int(b),
+                         GBps=round(b / (ms * 1e-3) / 1e9, 1),
+                         pct_hbm=round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1))
+        del g, Wd
+    log(f"moe: { {k: v for k, v in out.items() if k.startswith('moe')} }")
 
     # Q4_K products with a few (M = 4, 8) and many activation rows at the
     # Llama-3-8B prefill shapes (matrix cores)

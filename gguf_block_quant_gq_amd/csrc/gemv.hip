@@ -223,22 +223,35 @@ __device__ __forceinline__ void fetch_x(typename F::X& xr, const f32x4* xs, int 
 }
 
 // Rows fit in one segment: x stays in registers for the whole kernel.
+// Kernel arguments: the plain form, or the expert-batched form with the
+// expert table appended.
+struct GemvExpertArgs {
+  GemvArgs g;
+  ExpertArgs e;
+};
+
+template <bool EXPERTS>
+using KernelArgs = typename std::conditional<EXPERTS, GemvExpertArgs, GemvArgs>::type;
+
+__device__ __forceinline__ GemvArgs base_args(const GemvArgs& a) { return a; }
+__device__ __forceinline__ GemvArgs base_args(const GemvExpertArgs& a) { return a.g; }
+
 // Expert-batched calls: point a (the workgroup's copy of the arguments) at
 // the expert, activation row and output row of assignment blockIdx.y. An
 // expert id outside [0, n_expert) reads no weights: the assignment's output
 // row is filled with NaN instead. Returns false when there is nothing more
 // to do.
-__device__ __forceinline__ bool bind_assignment(GemvArgs& a) {
+__device__ __forceinline__ bool bind_assignment(GemvArgs& a, const ExpertArgs& ex) {
   const int as = blockIdx.y;
-  const int e = a.expid[as];
-  a.x += (int64_t)(as / a.xk) * a.cols;
+  const int e = ex.expid[as];
+  a.x += (int64_t)(as / ex.xk) * a.cols;
   a.y += (int64_t)as * a.rows;
-  if (e < 0 || e >= a.n_expert) {
+  if (e < 0 || e >= ex.n_expert) {
     for (int r = blockIdx.x * kThreads + threadIdx.x; r < a.rows; r += gridDim.x * kThreads)
       a.y[r] = __builtin_nanf("");
     return false;
   }
-  a.W += (int64_t)e * a.expert_bytes;
+  a.W += (int64_t)e * ex.expert_bytes;
   return true;
 }
 
@@ -246,11 +259,13 @@ __device__ __forceinline__ bool bind_assignment(GemvArgs& a) {
 // the waves' partial sums; instead each wave parks its partials in an LDS
 // ring of kSlots batches and the ring is folded (and y stored) once per
 // kSlots batches, so the waves run unsynchronised in between.
-template <class F, int G, int RB, int EPI>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs args) {
+template <class F, int G, int RB, int EPI, bool EXPERTS>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(KernelArgs<EXPERTS> args) {
   static_assert(G >= 4 && G <= kThreads && (G & (G - 1)) == 0, "G");
-  GemvArgs a = args;
-  if (a.expid && !bind_assignment(a)) return;  // uniform per workgroup
+  GemvArgs a = base_args(args);
+  if constexpr (EXPERTS) {
+    if (!bind_assignment(a, args.e)) return;  // uniform per workgroup
+  }
   static_assert(EPI != kEpiSwiglu || RB == 2, "the gate|up epilogue pairs two rows");
   constexpr int kGroups = kThreads / G;
   constexpr int kOut = out_rows<EPI, RB>();
@@ -287,17 +302,33 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs args) {
   // fold the ring: slot s holds batch it0 + (n0 + s) * stride
   auto flush = [&](int n0, int used) {
     __syncthreads();
-    if (gl < used) {
-      const int s = gl;
-      const int w0 = grp * kWavesPerGroup;
-      float v[RB];
+    const int w0 = grp * kWavesPerGroup;
+    if constexpr (EPI == kEpiSwiglu) {
+      // one lane per slot: the gate and up sums of its output row
+      if (gl < used) {
+        const int s = gl;
+        float v[RB];
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        v[i] = ring[s][w0][i];
+        for (int i = 0; i < RB; ++i) {
+          v[i] = ring[s][w0][i];
 #pragma unroll
-        for (int w = 1; w < kWavesPerGroup; ++w) v[i] += ring[s][w0 + w][i];
+          for (int w = 1; w < kWavesPerGroup; ++w) v[i] += ring[s][w0 + w][i];
+        }
+        epi_store<EPI, RB>(a, (it0 + (n0 + s) * stride) * kRowsPerIter + grp * kOut, v);
       }
-      epi_store<EPI, RB>(a, (it0 + (n0 + s) * stride) * kRowsPerIter + grp * kOut, v);
+    } else {
+      // one lane per (slot, row)
+      if (gl < used * RB) {
+        const int s = gl / RB, i = gl % RB;
+        float v = ring[s][w0][i];
+#pragma unroll
+        for (int w = 1; w < kWavesPerGroup; ++w) v += ring[s][w0 + w][i];
+        const int row = (it0 + (n0 + s) * stride) * kRowsPerIter + grp * RB + i;
+        if (row < a.rows) {
+          if constexpr (EPI == kEpiAcc) a.y[row] += v;
+          else a.y[row] = v;
+        }
+      }
     }
     __syncthreads();
   };
@@ -338,10 +369,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs args) {
 
 // Rows wider than G units: each row batch walks the row in segments of G
 // units, reloading the lane's x values per segment.
-template <class F, int G, int RB, int EPI>
-__global__ __launch_bounds__(kThreads) void gemv_seg_kernel(GemvArgs args) {
-  GemvArgs a = args;
-  if (a.expid && !bind_assignment(a)) return;  // uniform per workgroup
+template <class F, int G, int RB, int EPI, bool EXPERTS>
+__global__ __launch_bounds__(kThreads) void gemv_seg_kernel(KernelArgs<EXPERTS> args) {
+  GemvArgs a = base_args(args);
+  if constexpr (EXPERTS) {
+    if (!bind_assignment(a, args.e)) return;  // uniform per workgroup
+  }
   constexpr int kGroups = kThreads / G;
   constexpr int kOut = out_rows<EPI, RB>();
   constexpr int kRowsPerIter = kGroups * kOut;
@@ -376,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void gemv_seg_kernel(GemvArgs args) {
 }
 
 template <class F, int G, int RB, int EPI>
-hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s) {
+hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s, const ExpertArgs* ex) {
   constexpr int kRowsPerIter = (kThreads / G) * out_rows<EPI, RB>();
   const int64_t iters = ((int64_t)a.rows + kRowsPerIter - 1) / kRowsPerIter;
   // As many workgroups as can be resident at once (4 per CU at <= 128
@@ -386,14 +419,27 @@ hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s) {
                          : RB == 1 ? GQ_GEMV_WG_PER_CU_RB1
                          : is_k56<F>() ? GQ_GEMV_K56_WG_PER_CU : GQ_GEMV_WG_PER_CU_RBN;
   // (expert-batched calls share that many workgroups among their assignments)
-  int64_t cap = (int64_t)cus * kPerCu / a.n_assign;
+  const int n_assign = ex ? ex->n_assign : 1;
+  int64_t cap = (int64_t)cus * kPerCu / n_assign;
   if (cap < 1) cap = 1;
   const int blocks = (int)(iters < cap ? iters : cap);
-  const dim3 grid(blocks, a.n_assign);
+  const dim3 grid(blocks, n_assign);
+  // the expert-batched form is a separate instantiation, so the plain
+  // matvec's prologue and arguments carry none of its indirection
+  if constexpr (EPI == kEpiStore) {
+    if (ex) {
+      const GemvExpertArgs ea{a, *ex};
+      if (a.units <= G)
+        hipLaunchKernelGGL((gemv_kernel<F, G, RB, EPI, true>), grid, dim3(kThreads), 0, s, ea);
+      else
+        hipLaunchKernelGGL((gemv_seg_kernel<typename F::Base, G, RB, EPI, true>), grid, dim3(kThreads), 0, s, ea);
+      return hipGetLastError();
+    }
+  }
   if (a.units <= G)
-    hipLaunchKernelGGL((gemv_kernel<F, G, RB, EPI>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<F, G, RB, EPI, false>), grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((gemv_seg_kernel<typename F::Base, G, RB, EPI>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemv_seg_kernel<typename F::Base, G, RB, EPI, false>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -402,68 +448,70 @@ hipError_t launch_one(const GemvArgs& a, int cus, hipStream_t s) {
 // short to give every CU a few groups, else 2; always 2 (the gate row and
 // the up row) for the gate|up epilogue.
 template <class F, int G, int EPI>
-hipError_t with_g(const GemvArgs& a, int cus, hipStream_t s) {
+hipError_t with_g(const GemvArgs& a, int cus, hipStream_t s, const ExpertArgs* ex) {
   if constexpr (EPI == kEpiSwiglu) {
-    return launch_one<F, G, 2, EPI>(a, cus, s);
+    return launch_one<F, G, 2, EPI>(a, cus, s, ex);
   } else {
     const int64_t groups_needed = (int64_t)cus * GQ_GEMV_RB1_WAVES_PER_CU * (G >= 64 ? 1 : 64 / G);
-    if ((int64_t)a.rows < 2 * groups_needed) return launch_one<F, G, 1, EPI>(a, cus, s);
+    if ((int64_t)a.rows < 2 * groups_needed) return launch_one<F, G, 1, EPI>(a, cus, s, ex);
     // Q5_K / Q6_K on tall matrices (an lm_head, 14336-row projections): one
     // row per group at more workgroups per CU measured faster (more waves to
     // hide latency behind their heavier unpacking); two rows per group stay
     // ahead for shorter matrices and for wide rows.
     if constexpr (is_k56<F>() && G <= 128) {
-      if ((int64_t)a.rows >= 4 * groups_needed) return launch_one<F, G, 1, EPI>(a, cus, s);
+      if ((int64_t)a.rows >= 4 * groups_needed) return launch_one<F, G, 1, EPI>(a, cus, s, ex);
     }
     constexpr int kRB = is_q8<F>() ? GQ_GEMV_Q8_RBN : is_k56<F>() ? GQ_GEMV_K56_RBN : GQ_GEMV_RBN;
-    return launch_one<F, G, kRB, EPI>(a, cus, s);
+    return launch_one<F, G, kRB, EPI>(a, cus, s, ex);
   }
 }
 
 template <class F, int EPI>
-hipError_t dispatch_g(const GemvArgs& a, int cus, hipStream_t s) {
+hipError_t dispatch_g(const GemvArgs& a, int cus, hipStream_t s, const ExpertArgs* ex) {
   const int n = a.units;
-  if (n <= 4) return with_g<F, 4, EPI>(a, cus, s);
-  if (n <= 8) return with_g<F, 8, EPI>(a, cus, s);
-  if (n <= 16) return with_g<F, 16, EPI>(a, cus, s);
-  if (n <= 32) return with_g<F, 32, EPI>(a, cus, s);
-  if (n <= 64) return with_g<F, 64, EPI>(a, cus, s);
-  if (n <= 128) return with_g<F, 128, EPI>(a, cus, s);
-  return with_g<F, 256, EPI>(a, cus, s);
+  if (n <= 4) return with_g<F, 4, EPI>(a, cus, s, ex);
+  if (n <= 8) return with_g<F, 8, EPI>(a, cus, s, ex);
+  if (n <= 16) return with_g<F, 16, EPI>(a, cus, s, ex);
+  if (n <= 32) return with_g<F, 32, EPI>(a, cus, s, ex);
+  if (n <= 64) return with_g<F, 64, EPI>(a, cus, s, ex);
+  if (n <= 128) return with_g<F, 128, EPI>(a, cus, s, ex);
+  return with_g<F, 256, EPI>(a, cus, s, ex);
 }
 
 template <class F>
-hipError_t dispatch(const GemvArgs& a, int cus, hipStream_t s, int epi) {
+hipError_t dispatch(const GemvArgs& a, int cus, hipStream_t s, int epi, const ExpertArgs* ex) {
+  if (ex && epi != kEpiStore) return hipErrorInvalidValue;
   switch (epi) {
-    case kEpiStore: return dispatch_g<F, kEpiStore>(a, cus, s);
-    case kEpiAcc: return dispatch_g<F, kEpiAcc>(a, cus, s);
-    case kEpiSwiglu: return dispatch_g<F, kEpiSwiglu>(a, cus, s);
+    case kEpiStore: return dispatch_g<F, kEpiStore>(a, cus, s, ex);
+    case kEpiAcc: return dispatch_g<F, kEpiAcc>(a, cus, s, nullptr);
+    case kEpiSwiglu: return dispatch_g<F, kEpiSwiglu>(a, cus, s, nullptr);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi) {
+hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi,
+                       const ExpertArgs* ex) {
   if (fmt == kFmtQ8_0) {
     const int blocks = (a.cols + 31) / 32;
     // an even block count keeps every row 4-byte aligned: pairs of blocks
     if (blocks % 2 == 0 && (uintptr_t)a.W % 4 == 0) {
       a.units = blocks / 2;
-      return dispatch<Q8PairUnit>(a, cus, s, epi);
+      return dispatch<Q8PairUnit>(a, cus, s, epi, ex);
     }
     a.units = blocks;
-    return dispatch<Q8Unit>(a, cus, s, epi);
+    return dispatch<Q8Unit>(a, cus, s, epi, ex);
   }
   if (fmt == kFmtQ5_0) {
     a.units = (a.cols + 31) / 32;
-    return dispatch<Q5_0Unit>(a, cus, s, epi);
+    return dispatch<Q5_0Unit>(a, cus, s, epi, ex);
   }
   // K-quants: four units per 256-weight super-block
   a.units = 4 * ((a.cols + 255) / 256);
-  if (fmt == kFmtQ5_K) return dispatch<Q5KUnit>(a, cus, s, epi);
-  if (fmt == kFmtQ6_K) return dispatch<Q6KUnit>(a, cus, s, epi);
-  return dispatch<Q4KUnit>(a, cus, s, epi);
+  if (fmt == kFmtQ5_K) return dispatch<Q5KUnit>(a, cus, s, epi, ex);
+  if (fmt == kFmtQ6_K) return dispatch<Q6KUnit>(a, cus, s, epi, ex);
+  return dispatch<Q4KUnit>(a, cus, s, epi, ex);
 }
 
 }  // namespace gq

@@ -176,12 +176,8 @@ extern "C" int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
   gq::GemvArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
-  a.expid = expid;
-  a.expert_bytes = ebytes;
-  a.n_expert = (int)n_expert;
-  a.xk = (int)xk;
-  a.n_assign = (int)n_assign;
-  return finish(gq::launch_gemv(fmt, a, cus, (hipStream_t)stream, gq::kEpiStore));
+  const gq::ExpertArgs ex{expid, ebytes, (int)n_expert, (int)xk, (int)n_assign};
+  return finish(gq::launch_gemv(fmt, a, cus, (hipStream_t)stream, gq::kEpiStore, &ex));
 }
 
 extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,

@@ -21,14 +21,18 @@ struct GemvArgs {
   int rows;   // output rows (the gate|up epilogue reads 2 * rows weight rows)
   int cols;
   int units;  // units per row (set by the launcher)
-  // Expert-batched form (null expid: a single matvec). Assignment a =
-  // blockIdx.y multiplies expert expid[a] (at W + expid[a] * expert_bytes)
-  // by activation row a / xk of x and writes row a of y (rows floats each).
-  const int32_t* expid = nullptr;
-  int64_t expert_bytes = 0;
-  int n_expert = 0;
-  int xk = 1;
-  int n_assign = 1;
+};
+
+// The expert-batched form (gq_matvec_experts): assignment a = blockIdx.y
+// multiplies expert expid[a] (at W + expid[a] * expert_bytes) by activation
+// row a / xk of x and writes row a of y (rows floats each). Kept out of
+// GemvArgs so that the plain matvec's kernel arguments stay small.
+struct ExpertArgs {
+  const int32_t* expid;
+  int64_t expert_bytes;
+  int n_expert;
+  int xk;
+  int n_assign;
 };
 
 // What the matvec does with each finished row sum.
@@ -61,7 +65,8 @@ struct GemmArgs {
 // All launchers enqueue on `s` and return the launch status.
 // `units` is filled in by the launcher; `cus` is the device's CU count.
 hipError_t launch_dequant(int fmt, DequantArgs a, hipStream_t s);
-hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi = kEpiStore);
+hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi = kEpiStore,
+                       const ExpertArgs* ex = nullptr);
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
 hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s);
 
