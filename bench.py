@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 SMALL_M = (4, 8)               # few activation rows (padded to 16 on the matrix cores)
 
 
@@ -428,6 +429,29 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
                          pct_hbm=round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1))
         del g, Wd
     log(f"moe: { {k: v for k, v in out.items() if k.startswith('moe')} }")
+
+    # prefill products of the other formats on the fp32 matrix cores (the
+    # Llama-3-8B Q6_K down and Q5_K gate shapes)
+    for i in (1, 3):
+        name, f, r, c, W, _ = synth.mixed_format_weight_and_x(i)
+        Wd = torch.from_numpy(W).cuda()
+        del W
+        for M in synth.PREFILL_M:
+            Xd = torch.from_numpy(synth.activations((M, c), synth.rng_for(911, M))).cuda()
+            Yd = torch.empty((M, r), dtype=torch.float32, device="cuda")
+
+            def mmf(f=f, r=r, c=c, M=M, Wd=Wd, Xd=Xd, Yd=Yd):
+                st = lib.gq_matmul(f, Wd.data_ptr(), r, c, Xd.data_ptr(), M, Yd.data_ptr(),
+                                   stream_ptr())
+                assert st == 0
+
+            ms = timer.time(mmf, 10 if M < 512 else 5, warmup=1)
+            tf = 2.0 * M * r * c / (ms * 1e-3) / 1e12
+            out[f"matmul_{name}_M{M}"] = dict(
+                us_per_call=round(ms * 1e3, 1), TFLOPs=round(tf, 2),
+                pct_mfma_f32_peak=round(100 * tf / MFMA_F32_PEAK_TFLOPS, 2))
+        del Wd
+    log(f"mixed-format prefill: { {k: v for k, v in out.items() if k.startswith('matmul_llama3')} }")
 
     # Q4_K products with a few (M = 4, 8) and many activation rows at the
     # Llama-3-8B prefill shapes (matrix cores)

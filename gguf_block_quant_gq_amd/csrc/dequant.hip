@@ -19,6 +19,7 @@
 // stay inside one span of the row of at most 272 bytes.
 #include "gq_device.h"
 #include "gq_internal.h"
+#include "gq_quads.h"
 
 namespace gq {
 
@@ -98,9 +99,7 @@ __global__ __launch_bounds__(kThreads) void dequant_q4_k_kernel(DequantArgs a) {
 }
 
 // Wave item = (row, 8-block group), as for Q8_0. Lane l: block 8 gi + (l >> 3),
-// weights i0 = 4 (l & 7) .. +3: nibble bytes (i0 & 15) .. +3 (low nibbles for
-// i0 < 16, high ones above), bits i0 .. i0+3 of qh. Blocks are 2-byte
-// aligned, so everything is read with 2-byte loads.
+// weights 4 (l & 7) .. +3 of it (decode in Q5_0Quad, 2-byte loads only).
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void dequant_q5_0_kernel(DequantArgs a) {
   const int lane = threadIdx.x & 63;
@@ -114,85 +113,48 @@ __global__ __launch_bounds__(kThreads) void dequant_q5_0_kernel(DequantArgs a) {
     const int blk = 8 * gi + (lane >> 3);
     const int c0 = blk * kQ5_0Weights + i0;
     if (c0 >= a.cols) continue;
-    const uint8_t* p = a.W + row * a.row_bytes + (int64_t)blk * kQ5_0Bytes;
-    const float d = half_bits_to_float(load_u16(p));
-    const uint32_t hb = (load_u16(p + 2 + 2 * (i0 >> 4)) >> (i0 & 15)) & 0xFu;
-    const uint8_t* qp = p + 6 + (i0 & 15);
-    const uint32_t q = load_u16(qp) | (load_u16(qp + 2) << 16);
-    const uint32_t nib = (i0 >= 16 ? q >> 4 : q) & 0x0F0F0F0Fu;
     float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int code = (int)(((nib >> (8 * e)) & 0xFu) | (((hb >> e) & 1u) << 4));
-      v[e] = d * (float)(code - 16);
-    }
+    Q5_0Quad::get(a.W + row * a.row_bytes, c0, v);
     float* o = a.out + row * a.cols + c0;
     store_quad<VEC>(o, c0, a.cols, v[0], v[1], v[2], v[3]);
   }
 }
 
-// Wave item = (row, super-block), lanes as for Q4_K: sub-block j = l >> 3,
-// outputs 32 j + 4 (l & 7) .. +3; bit 4 of their codes is bit j of qh bytes
-// 4 (l & 7) .. +3.
+// Wave item = (row, super-block); lane l produces outputs 4l .. 4l+3
+// (sub-block l >> 3; decode in Q5KQuad).
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void dequant_q5_k_kernel(DequantArgs a) {
   const int lane = threadIdx.x & 63;
   const int nsb = a.units;
   const int64_t items = a.rows * (int64_t)nsb;
-  const int j = lane >> 3, g = j >> 1, h = j & 1, l0 = 4 * (lane & 7);
   for (int64_t it = blockIdx.x * (int64_t)kWaves + (threadIdx.x >> 6); it < items;
        it += (int64_t)gridDim.x * kWaves) {
     const int64_t row = it / nsb;
     const int sb = (int)(it - row * nsb);
     const int c0 = sb * kQ5KWeights + 4 * lane;
     if (c0 >= a.cols) continue;
-    const uint8_t* blk = a.W + row * a.row_bytes + (int64_t)sb * kQ5KBytes;
-    const u32x4 hd = load_u32x4(blk);
-    const uint32_t qh = load_u32(blk + 16 + l0);
-    const uint32_t w = load_u32(blk + 48 + 32 * g + l0);
-    uint32_t sc[2], m[2];
-    q4k_scales(q4k_scale_sel(g), hd.y, hd.z, hd.w, sc, m);
-    const float d = half_bits_to_float(hd.x & 0xFFFFu);
-    const float dmin = half_bits_to_float(hd.x >> 16);
-    const float A = d * (float)sc[h];     // exact
-    const float B = dmin * (float)m[h];   // exact
-    const uint32_t code = ((h ? w >> 4 : w) & 0x0F0F0F0Fu) | (((qh >> j) & 0x01010101u) << 4);
     float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = A * (float)((code >> (8 * e)) & 0xFFu) - B;
+    Q5KQuad::get(a.W + row * a.row_bytes, c0, v);
     float* o = a.out + row * a.cols + c0;
     store_quad<VEC>(o, c0, a.cols, v[0], v[1], v[2], v[3]);
   }
 }
 
-// Wave item = (row, super-block). Lane l: outputs i0 = 4 l .. +3, i.e. half
-// n = l >> 5, run k = (l >> 3) & 3, positions l0 = 4 (l & 7) .. +3 of the
-// run: nibble k >> 1 of ql bytes 64 n + 32 (k & 1) + l0 .., bits 2k, 2k+1
-// of qh bytes 32 n + l0 .., scale l >> 2. Super-blocks are 2-byte aligned.
+// Wave item = (row, super-block); lane l produces outputs 4l .. 4l+3 (half
+// l >> 5, run (l >> 3) & 3; decode in Q6KQuad).
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void dequant_q6_k_kernel(DequantArgs a) {
   const int lane = threadIdx.x & 63;
   const int nsb = a.units;
   const int64_t items = a.rows * (int64_t)nsb;
-  const int n = lane >> 5, k = (lane >> 3) & 3, l0 = 4 * (lane & 7), si = lane >> 2;
   for (int64_t it = blockIdx.x * (int64_t)kWaves + (threadIdx.x >> 6); it < items;
        it += (int64_t)gridDim.x * kWaves) {
     const int64_t row = it / nsb;
     const int sb = (int)(it - row * nsb);
     const int c0 = sb * kQ6KWeights + 4 * lane;
     if (c0 >= a.cols) continue;
-    const uint8_t* blk = a.W + row * a.row_bytes + (int64_t)sb * kQ6KBytes;
-    const uint8_t* lp = blk + 64 * n + 32 * (k & 1) + l0;
-    const uint8_t* hp = blk + 128 + 32 * n + l0;
-    const uint32_t ql = load_u16(lp) | (load_u16(lp + 2) << 16);
-    const uint32_t qh = load_u16(hp) | (load_u16(hp + 2) << 16);
-    const uint32_t s2 = load_u16(blk + 192 + (si & ~1));
-    const float scale = (float)(int8_t)(s2 >> (8 * (si & 1)));
-    const float A = half_bits_to_float(load_u16(blk + 208)) * scale;  // exact
-    const uint32_t code = ((k >> 1 ? ql >> 4 : ql) & 0x0F0F0F0Fu) | (((qh >> (2 * k)) & 0x03030303u) << 4);
     float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = A * (float)((int)((code >> (8 * e)) & 0xFFu) - 32);
+    Q6KQuad::get(a.W + row * a.row_bytes, c0, v);
     float* o = a.out + row * a.cols + c0;
     store_quad<VEC>(o, c0, a.cols, v[0], v[1], v[2], v[3]);
   }

@@ -473,13 +473,6 @@ __global__ __launch_bounds__(256) void gemm_q4k_mfma_kernel(MmArgs a) {
 }
 
 // Y = sum over the ks super-block splits, in split order.
-__global__ __launch_bounds__(256) void split_sum_kernel(const float* part, float* y, int64_t n, int ks) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= n) return;
-  float v = part[idx];
-  for (int z = 1; z < ks; ++z) v += part[(int64_t)z * n + idx];
-  y[idx] = v;
-}
 
 template <int WR, int WM>
 hipError_t launch_main(const MmArgs& m, int gx, int gy, hipStream_t s) {
@@ -488,6 +481,19 @@ hipError_t launch_main(const MmArgs& m, int gx, int gy, hipStream_t s) {
 }
 
 }  // namespace
+
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* part, float* y, int64_t n, int ks) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  float v = part[idx];
+  for (int z = 1; z < ks; ++z) v += part[(int64_t)z * n + idx];
+  y[idx] = v;
+}
+
+hipError_t launch_split_sum(const float* part, float* y, int64_t n, int ks, hipStream_t s) {
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, y, n, ks);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s) {
   a.units = 0;
@@ -532,9 +538,7 @@ hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s) {
   }
   if (e == hipSuccess && ks > 1) {
     const int64_t n = (int64_t)a.M * a.rows;
-    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       (const float*)m.out, a.Y, n, ks);
-    e = hipGetLastError();
+    e = launch_split_sum((const float*)m.out, a.Y, n, ks, s);
   }
   const hipError_t ef = ws_free(ws, s);
   return e != hipSuccess ? e : ef;

@@ -63,6 +63,21 @@ int check_align(int fmt, const void* W) {
 
 int finish(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_DEVICE; }
 
+// Activation rows from which the Q8_0 / Q5_0 / Q5_K / Q6_K products run on
+// the fp32 matrix cores (gemm_f32.hip) instead of the fp32 few-row kernel
+// (measured: K-quants are faster there from M = 2 on; Q8_0 at M = 4 is still
+// faster on the few-row kernel, 21 vs 31 us for 4096 x 4096, and 2.8x slower
+// at M = 16).
+#ifndef GQ_F32_MIN_M_KQUANT
+#define GQ_F32_MIN_M_KQUANT 2
+#endif
+#ifndef GQ_F32_MIN_M_BLOCK32
+#define GQ_F32_MIN_M_BLOCK32 8
+#endif
+int64_t f32_matrix_core_min_m(int fmt) {
+  return (fmt == GQ_FMT_Q5_K || fmt == GQ_FMT_Q6_K) ? GQ_F32_MIN_M_KQUANT : GQ_F32_MIN_M_BLOCK32;
+}
+
 }  // namespace
 
 extern "C" int64_t gq_row_bytes(int fmt, int64_t cols) {
@@ -197,15 +212,17 @@ extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, con
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
   // One activation row is the matvec (same rounding, its kernel). Q4_K with
-  // two or more rows runs on the matrix cores: padded to 16 rows it was
-  // measured faster than the fp32 few-row kernel from M = 2 on (the latter
-  // re-reads each activation row per weight-row batch). The other formats
-  // keep the fp32 kernel for M >= 2.
+  // two or more rows runs on the fp16 matrix cores (exact operands): padded
+  // to 16 rows it was measured faster than the fp32 few-row kernel from M = 2
+  // on (the latter re-reads each activation row per weight-row batch). The
+  // other formats run on the fp32 matrix cores from a per-format M.
   if (M == 1) {
     gq::GemvArgs v{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
     return finish(gq::launch_gemv(fmt, v, cus, (hipStream_t)stream));
   }
   gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
   if (fmt == GQ_FMT_Q4_K) return finish(gq::launch_gemm_mfma(fmt, a, cus, (hipStream_t)stream));
+  if (M >= f32_matrix_core_min_m(fmt))
+    return finish(gq::launch_gemm_f32(fmt, a, cus, (hipStream_t)stream));
   return finish(gq::launch_gemm_small(fmt, a, cus, (hipStream_t)stream));
 }

@@ -69,6 +69,10 @@ hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi = kE
                        const ExpertArgs* ex = nullptr);
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
 hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s);
+hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s);
+
+// y[i] = sum over z < ks of part[z * n + i], in split order (deterministic).
+hipError_t launch_split_sum(const float* part, float* y, int64_t n, int ks, hipStream_t s);
 
 // Stream-ordered scratch from a per-device pool (workspace.hip): the block is
 // usable by work enqueued on `s` after ws_alloc and before ws_free.

@@ -41,13 +41,13 @@
  *
  * Ownership and threading
  *   All pointers are device pointers owned by the caller; the library never
- *   frees or keeps them. gq_dequant and gq_matvec use no memory beyond their
- *   arguments. gq_matmul on the matrix cores (Q4_K, M >= 2) takes a
+ *   frees or keeps them. gq_dequant and the gq_matvec family use no memory
+ *   beyond their arguments. gq_matmul on the matrix cores takes a
  *   stream-ordered workspace from a library-owned HIP memory pool (one per
  *   device, created on first use, memory kept until the process ends):
- *   17472 * ceil(M/16) * ceil(cols/256) bytes of prepared activations,
- *   plus 4 * M * rows bytes per extra split when the K range is split over
- *   workgroups. It is allocated and released on the caller's stream, so the
+ *   Q4_K 17472 * ceil(M/16) * ceil(cols/256) bytes of prepared activations,
+ *   and for every format 4 * M * rows bytes per split when the K range is
+ *   split over workgroups. It is allocated and released on the caller's stream, so the
  *   call stays asynchronous and calls on different streams never share it;
  *   an allocation failure returns GQ_ERR_DEVICE. Global state: that pool and
  *   a per-device cache of device properties, each filled once. Calls on
@@ -182,9 +182,12 @@ int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, in
  * The batched form used for prompt chunks ("nurllama 0.18.1 API", model.nu
  * section: the matmuls run over up to 64 positions at once, each weight read
  * once per chunk). M == 1 runs the gq_matvec kernel. Q4_K with M >= 2 runs
- * on the matrix cores (with the workspace described above); the other
- * formats with M >= 2 stream W once per 15 activation rows with fp32
- * arithmetic. Same
+ * on the fp16 matrix cores with exact operands (workspace described above).
+ * Q5_K and Q6_K with M >= 2, and Q8_0 and Q5_0 with M >= 8, run on the fp32
+ * matrix cores: each k-chunk of W is dequantised exactly to fp32 and
+ * multiplied with the fp32 activations (a workspace of 4 * M * rows bytes per
+ * extra split when the k range is split over workgroups). Q8_0 and Q5_0 with
+ * 2 <= M < 8 stream W once per 15 activation rows on the fp32 vector units. Same
  * accuracy bound as gq_matvec; repeated calls give bit-identical results.
  * Asynchronous on `stream`.
  */
