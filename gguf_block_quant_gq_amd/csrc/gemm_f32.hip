@@ -13,8 +13,9 @@
 // range of k-chunks (split over blockIdx.z when the tiles alone cannot fill
 // the GPU; the split partial products are added in split order afterwards).
 // Per chunk of 128 k: every thread decodes 8 quads of weights into the W
-// tile and loads its share of the X tile; then wave w multiplies weight
-// rows 16w..16w+15 by all activation rows. Within each group of 16 k, lane
+// tile and stores its share of the X tile (both requested into registers
+// during the previous chunk); then wave w multiplies weight rows
+// 16w..16w+15 by all activation rows. Within each group of 16 k, lane
 // (i, q) = (lane & 15, lane >> 4) supplies k = 4q + s at MFMA step s for both
 // operands (the same permutation of k on both sides leaves the sum
 // unchanged), so each operand is one 16-byte LDS read per 16 k.
@@ -60,29 +61,23 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(F32Args a) {
 #pragma unroll
   for (int t = 0; t < WM; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c = c_begin; c < c_end; ++c) {
+  // The next chunk's raw weight bytes and activations are requested into
+  // registers before the current chunk is multiplied, so their latency hides
+  // behind the matrix-core work; they are decoded into LDS after it.
+  typename Q::Raw wr[8];
+  f32x4 xr[2 * WM];
+  auto fetch = [&](int c) {
     const int k0 = c * kKC;
-    // weight tile: 64 rows x 128 k = 2048 quads, 8 per thread (32 threads per row)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; ++j) {  // 64 rows x 128 k = 2048 quads, 32 threads per row
       const int qd = tid + 256 * j;
-      const int rl = qd >> 5, kk = 4 * (qd & 31);
-      const int row = r0 + rl, k = k0 + kk;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (row < a.rows && k < a.cols) {
-        Q::get(a.W + (int64_t)row * a.row_bytes, k, v);
-#pragma unroll
-        for (int e = 1; e < 4; ++e)
-          if (k + e >= a.cols) v[e] = 0.f;  // past the row's last column
-      }
-      *(f32x4*)&Wl[rl * kLD + kk] = f32x4{v[0], v[1], v[2], v[3]};
+      const int row = r0 + (qd >> 5), k = k0 + 4 * (qd & 31);
+      if (row < a.rows && k < a.cols) Q::load(wr[j], a.W + (int64_t)row * a.row_bytes, k);
     }
-    // activation tile: 16*WM rows x 128 k, zero past M and cols
 #pragma unroll
-    for (int j = 0; j < 2 * WM; ++j) {
+    for (int j = 0; j < 2 * WM; ++j) {  // 16*WM rows x 128 k, zero past M and cols
       const int qd = tid + 256 * j;
-      const int ml = qd >> 5, kk = 4 * (qd & 31);
-      const int m = m0 + ml, k = k0 + kk;
+      const int m = m0 + (qd >> 5), k = k0 + 4 * (qd & 31);
       f32x4 xv = {0.f, 0.f, 0.f, 0.f};
       if (m < a.M) {
         const float* xp = a.X + (int64_t)m * a.cols + k;
@@ -95,9 +90,37 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(F32Args a) {
           xv.w = k + 3 < a.cols ? xp[3] : 0.f;
         }
       }
-      *(f32x4*)&Xl[ml * kLD + kk] = xv;
+      xr[j] = xv;
     }
+  };
+  auto commit = [&](int c) {
+    const int k0 = c * kKC;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int qd = tid + 256 * j;
+      const int rl = qd >> 5, kk = 4 * (qd & 31);
+      const int row = r0 + rl, k = k0 + kk;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (row < a.rows && k < a.cols) {
+        Q::decode(wr[j], k, v);
+#pragma unroll
+        for (int e = 1; e < 4; ++e)
+          if (k + e >= a.cols) v[e] = 0.f;  // past the row's last column
+      }
+      *(f32x4*)&Wl[rl * kLD + kk] = f32x4{v[0], v[1], v[2], v[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * WM; ++j) {
+      const int qd = tid + 256 * j;
+      *(f32x4*)&Xl[(qd >> 5) * kLD + 4 * (qd & 31)] = xr[j];
+    }
+  };
+
+  if (c_begin < c_end) fetch(c_begin);
+  for (int c = c_begin; c < c_end; ++c) {
+    commit(c);
     __syncthreads();
+    if (c + 1 < c_end) fetch(c + 1);
 #pragma unroll 4
     for (int k16 = 0; k16 < kKC; k16 += 16) {
       const f32x4 wf = *(const f32x4*)&Wl[(16 * wave + i) * kLD + k16 + 4 * q];
