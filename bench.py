@@ -109,6 +109,33 @@ def traffic_probe(torch, gq, lib, mats, stream_ptr):
                       / len(dominant_launches(mats))}), flush=True)
 
 
+def prefill_probe(torch, gq, lib, synth, stream_ptr):
+    """One call of each prefill product at M = 512 (after one warm-up call):
+    Q4_K gate and down on the fp16 matrix cores, Q6_K down and Q5_K gate on
+    the fp32 matrix cores; for rocprofv3 --pmc runs (MFMA busy cycles and
+    executed matrix ops per dispatch)."""
+    M = 512
+    cases = []
+    for which in ("gate", "down"):
+        W, X, rows, cols = synth.prefill_inputs(which, M)
+        cases.append((f"q4_k_{which}", 12, W, X, rows, cols))
+    for i in (1, 3):
+        name, f, r, c, W, _ = synth.mixed_format_weight_and_x(i)
+        cases.append((name, f, W, synth.activations((M, c), synth.rng_for(911, M)), r, c))
+    out = {}
+    for name, f, W, X, rows, cols in cases:
+        Wd, Xd = torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda()
+        Yd = torch.empty((M, rows), dtype=torch.float32, device="cuda")
+        for _ in range(2):
+            st = lib.gq_matmul(f, Wd.data_ptr(), rows, cols, Xd.data_ptr(), M, Yd.data_ptr(),
+                               stream_ptr())
+            assert st == 0
+        torch.cuda.synchronize()
+        out[name] = dict(fmt=f, rows=rows, cols=cols, M=M, flops=2.0 * M * rows * cols)
+        del Wd, Xd, Yd
+    print(json.dumps(out), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +144,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--prefill-probe", action="store_true",
+                    help="run each prefill product at M = 512 twice (for counter runs) and exit")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 256 MiB copy and one pass of the dominant kernel, then exit")
     args = ap.parse_args()
@@ -135,6 +164,10 @@ def main() -> int:
     lib = gq.load_library()
     timer = Timer(torch)
     stream_ptr = lambda: int(torch.cuda.current_stream().cuda_stream)  # noqa: E731
+
+    if args.prefill_probe:
+        prefill_probe(torch, gq, lib, synth, stream_ptr)
+        return 0
 
     # ------------------------------------------------ decode step workload
     t0 = time.time()
