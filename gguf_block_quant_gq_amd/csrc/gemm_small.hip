@@ -1,5 +1,5 @@
-// gemm_small.hip -- Y = X W^T for several activation rows and Q8_0, Q5_0,
-// Q5_K or Q6_K weights.
+// gemm_small.hip -- Y = X W^T for a few activation rows and Q8_0 or Q5_0
+// weights.
 //
 // The prompt-chunk form of the product ("nurllama 0.18.1 API", model.nu
 // section: the matmuls run over several positions at once so each weight is
@@ -10,10 +10,10 @@
 // L2: M * cols * 4 bytes). Accumulators are kept per (row, m) and folded
 // across the group at the end, in a fixed order.
 //
-// W is streamed from HBM once per tile of kMaxM activation rows. (Q4_K
-// products with M >= 2 run on the matrix cores instead, which was measured
-// faster: this kernel re-reads every activation row for each batch of weight
-// rows, from L2.)
+// W is streamed from HBM once per tile of kMaxM activation rows. It serves
+// 2 <= M < 8 only: from there on (and for the K-quants from M = 2) the
+// matrix-core kernels were measured faster, since this kernel re-reads every
+// activation row from L2 for each batch of weight rows.
 #include "gq_device.h"
 #include "gq_internal.h"
 #include "gq_units.h"
@@ -146,8 +146,8 @@ hipError_t dispatch(const GemmArgs& a, int max_blocks, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s) {
-  // Q4_K products with several activation rows run on the matrix cores
-  // (gemm_mfma.hip); every other format streams W here.
+  // Q8_0 and Q5_0 with a few activation rows (below the fp32 matrix-core
+  // threshold); the K-quants always run on the matrix cores.
   switch (fmt) {
     case kFmtQ8_0:
       a.units = (a.cols + 31) / 32;
@@ -155,12 +155,6 @@ hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s) {
     case kFmtQ5_0:
       a.units = (a.cols + 31) / 32;
       return dispatch<Q5_0Unit, 2>(a, cus * 4, s);
-    case kFmtQ5_K:
-      a.units = 4 * ((a.cols + 255) / 256);
-      return dispatch<Q5KUnit, 1>(a, cus * 4, s);
-    case kFmtQ6_K:
-      a.units = 4 * ((a.cols + 255) / 256);
-      return dispatch<Q6KUnit, 1>(a, cus * 4, s);
     default:
       return hipErrorInvalidValue;
   }

@@ -580,33 +580,6 @@ struct Q5KUnit : Q4KUnit {
     const float ms = __builtin_fmaf(m[1], x.sb, m[0] * x.sa);
     return __builtin_fmaf(d, qs, -dmin * ms);
   }
-
-  // Decoded form: w = (d * sc_j) * code - dmin * m_j (one rounding).
-  struct Dec {
-    float a[32], b[32];
-  };
-
-  __device__ static void decode(Dec& dec, const Raw& raw, const Lane& ln) {
-    float sc[2], m[2];
-    scale_codes(raw, ln, sc, m);
-    const float d = half_bits_to_float(raw.h.x & 0xFFFFu);
-    const float dmin = half_bits_to_float(raw.h.x >> 16);
-    const float A0 = d * sc[0], A1 = d * sc[1], B0 = dmin * m[0], B1 = dmin * m[1];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t ca, cb;
-      codes(raw, ln, k, ca, cb);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        dec.a[4 * k + t] = __builtin_fmaf(A0, ubyte_at(ca, t), -B0);
-        dec.b[4 * k + t] = __builtin_fmaf(A1, ubyte_at(cb, t), -B1);
-      }
-    }
-  }
-
-  __device__ static float dot_dec(const Dec& dec, const X& x) {
-    return q8_block_dot_f(dec.a, x.a) + q8_block_dot_f(dec.b, x.b);
-  }
 };
 
 // ------------------------------------------------------------- Q6_K unit
@@ -787,35 +760,6 @@ struct Q6KUnit {
 #pragma unroll
     for (int q = 0; q < 4; ++q) r = __builtin_fmaf(sc[q], __builtin_fmaf(-32.f, x.s[q], acc[q]), r);
     return half_bits_to_float(raw.d16) * r;
-  }
-
-  // Decoded form: w = (d * scale) * (code - 32), exact.
-  struct Dec {
-    float a[32], b[32];
-  };
-
-  __device__ static void decode(Dec& dec, const Raw& raw, const Lane& ln) {
-    float sc[4];
-    scales(raw, ln, sc);
-    const float d = half_bits_to_float(raw.d16);
-    float A[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) A[q] = d * sc[q];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t ca, cb;
-      codes(raw, ln, k, ca, cb);
-      const int h = k >> 2;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        dec.a[4 * k + t] = A[h] * (ubyte_at(ca, t) - 32.f);
-        dec.b[4 * k + t] = A[2 + h] * (ubyte_at(cb, t) - 32.f);
-      }
-    }
-  }
-
-  __device__ static float dot_dec(const Dec& dec, const X& x) {
-    return q8_block_dot_f(dec.a, x.a) + q8_block_dot_f(dec.b, x.b);
   }
 };
 

@@ -58,3 +58,64 @@ def test_graph_replays_match_eager(gq, oracle):
             Wh = to_host(mats[k])
             ref, S = oracle.matvec(fmt, Wh, rows, cols, host_x[k], nthreads=oracle_threads())
             assert_within_tolerance(got[k], ref, S, f"graph replay {rep} fmt={fmt} {rows}x{cols}")
+
+
+def test_graph_replays_of_fused_variants(gq, oracle):
+    """gq_matvec_acc, gq_matvec_swiglu and gq_matvec_experts captured in one
+    graph: each replay (after eager resets of the accumulated output and new
+    activations) equals the same calls made eagerly, bit for bit."""
+    import torch
+
+    rng = synth.rng_for(810, 0)
+    rows, cols = 600, 1024
+    Wacc = to_dev(synth.weights(12, rows, cols, rng))
+    Wgu = to_dev(synth.weights(14, 2 * rows, cols, rng))
+    n_expert, erows, xk, n_assign = 6, 300, 2, 8
+    Wex = to_dev(synth.weights(13, n_expert * erows, cols, rng))
+    ids = to_dev(rng.integers(0, n_expert, n_assign).astype(np.int32))
+    x = torch.empty(cols, dtype=torch.float32, device="cuda")
+    X = torch.empty((n_assign // xk, cols), dtype=torch.float32, device="cuda")
+    y0 = torch.empty(rows, dtype=torch.float32, device="cuda")
+    yacc = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ysw = torch.empty(rows, dtype=torch.float32, device="cuda")
+    Yex = torch.empty((n_assign, erows), dtype=torch.float32, device="cuda")
+
+    def step():
+        gq.gq_matvec_acc(12, Wacc, rows, cols, x, yacc)
+        gq.gq_matvec_swiglu(14, Wgu, rows, cols, x, y=ysw)
+        gq.gq_matvec_experts(13, Wex, n_expert, erows, cols, X, xk, ids, Y=Yex)
+
+    def fill(rep):
+        r = synth.rng_for(811 + rep, 0)
+        x.copy_(torch.from_numpy(synth.activations(cols, r)))
+        X.copy_(torch.from_numpy(synth.activations((n_assign // xk, cols), r)))
+        y0.copy_(torch.from_numpy(synth.activations(rows, r)))
+        yacc.copy_(y0)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fill(0)
+        step()  # warm up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+
+    for rep in range(3):
+        fill(rep + 1)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [to_host(t).copy() for t in (yacc, ysw, Yex)]
+        yacc.copy_(y0)
+        step()
+        eager = [to_host(t) for t in (yacc, ysw, Yex)]
+        print(f"[graph] fused variants replay {rep}", flush=True)
+        for g, e in zip(got, eager):
+            assert np.array_equal(g.view(np.uint32), e.view(np.uint32)), rep
+        # the accumulated output is y0 + W x within the product tolerance
+        ref, S = oracle.matvec(12, to_host(Wacc), rows, cols, to_host(x))
+        assert_within_tolerance(got[0] - to_host(y0), ref, S + np.abs(to_host(y0)) * 1e-3,
+                                f"graph acc replay {rep}")
