@@ -29,6 +29,7 @@ TYPE_Q4_K = 12
 TYPE_Q5_0 = 6
 TYPE_Q5_K = 13
 TYPE_Q6_K = 14
+TYPE_Q8_0_SPLIT = 1008
 
 _lib = None
 
@@ -67,6 +68,8 @@ def _load():
     lib.gqo_matvec.restype = i32
     lib.gqo_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp, i32]
     lib.gqo_matmul.restype = i32
+    lib.gqo_q8_0_split_repack.argtypes = [vp, i64, i64, vp]
+    lib.gqo_q8_0_split_repack.restype = i32
     lib.gqo_quantize_q8_0.argtypes = [vp, i64, i64, vp]
     lib.gqo_quantize_q8_0.restype = i32
     lib.gqo_quantize_q4_k.argtypes = [vp, i64, i64, vp]
@@ -208,4 +211,16 @@ def experts_matvec(fmt: int, W, n_expert: int, rows: int, cols: int, X, xk: int,
         if 0 <= e < n_expert:
             Y[a], S[a] = matvec(fmt, Wb[e * eb:(e + 1) * eb], rows, cols, X[a // xk], nthreads)
     return Y, S
+
+
+def q8_0_split_repack(W, rows: int, cols: int) -> np.ndarray:
+    """Q8_0 rows repacked into the split per-row layout (scales first, padded
+    to 16 bytes, then the codes): the oracle's reading of the q8_0 repack of
+    "nurllama 0.18.1 API", kernels.nu section."""
+    Wb = _as_bytes(W)
+    if Wb.size < rows * row_bytes(TYPE_Q8_0, cols):
+        raise ValueError("W holds fewer bytes than rows * row_bytes")
+    out = np.empty(rows * row_bytes(TYPE_Q8_0_SPLIT, cols), np.uint8)
+    _check(_load().gqo_q8_0_split_repack(_ptr(Wb), rows, cols, _ptr(out)), "q8_0_split_repack")
+    return out
 

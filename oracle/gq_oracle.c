@@ -39,6 +39,11 @@
  *        i = 128n + 32k + l (n<2, k<4, l<32): low four bits = nibble k>>1 of
  *        ql[64n + 32(k&1) + l], high two bits = bits 2k..2k+1 of qh[32n + l];
  *        code in 0..63, w_i = (d*scale_{i/16})*(code - 32).
+ *      Q8_0 split per-row layout (a repack of Q8_0 rows that stores the
+ *        scales apart from the quants: "nurllama 0.18.1 API", kernels.nu
+ *        section, the q8_0 repack kernel; the layout itself is not printed,
+ *        this is the reading taken): per row the nb fp16 scales, zero padding
+ *        to a multiple of 16 bytes, then the nb * 32 codes in block order.
  *    Formats other than these are not decoded (the pages list Q5_K, Q6_K and
  *    Q5_0 next to Q4_K: "nurllama" README, "What it runs"; "nurllama 0.18.1
  *    API", kernels.nu section, its per-format kernel list).
@@ -67,6 +72,12 @@ enum {
 };
 
 /* Weights and bytes of one block of `type`; 0 for an unknown type. */
+/* Bytes of the scale region of a split Q8_0 row (nb fp16, padded to 16). */
+static int64_t split_scale_bytes(int64_t nb)
+{
+    return ((2 * nb + 15) / 16) * 16;
+}
+
 static int block_shape(int type, int* bytes)
 {
     switch (type) {
@@ -81,9 +92,15 @@ static int block_shape(int type, int* bytes)
 
 int64_t gqo_row_bytes(int type, int64_t cols)
 {
+    if (cols < 0)
+        return -1;
+    if (type == GQO_TYPE_Q8_0_SPLIT) {
+        int64_t nb = (cols + O_Q8_0_WEIGHTS - 1) / O_Q8_0_WEIGHTS;
+        return split_scale_bytes(nb) + nb * O_Q8_0_WEIGHTS;
+    }
     int bytes;
     int weights = block_shape(type, &bytes);
-    if (cols < 0 || weights == 0)
+    if (weights == 0)
         return -1;
     return ((cols + weights - 1) / weights) * bytes;
 }
@@ -293,8 +310,23 @@ static void dequant_row_q6_k(const uint8_t* row, int64_t cols, float* out)
     }
 }
 
+/* Split row: scale of block b at bytes 2b, 2b+1; code i at scale region + i. */
+static void dequant_row_q8_0_split(const uint8_t* row, int64_t cols, float* out)
+{
+    int64_t nb = (cols + O_Q8_0_WEIGHTS - 1) / O_Q8_0_WEIGHTS;
+    const uint8_t* codes = row + split_scale_bytes(nb);
+    for (int64_t c = 0; c < cols; c++) {
+        float d = gqo_f16_to_f32(read_u16le(row + 2 * (c / O_Q8_0_WEIGHTS)));
+        out[c] = d * (float)(int8_t)codes[c];
+    }
+}
+
 static int dequant_row(int type, const uint8_t* row, int64_t cols, float* out)
 {
+    if (type == GQO_TYPE_Q8_0_SPLIT) {
+        dequant_row_q8_0_split(row, cols, out);
+        return 0;
+    }
     if (type == GQO_TYPE_Q5_0) {
         dequant_row_q5_0(row, cols, out);
         return 0;
@@ -426,6 +458,31 @@ int gqo_matvec(int type, const void* W, int64_t rows, int64_t cols,
                const float* x, double* y, double* S, int nthreads)
 {
     return gqo_matmul(type, W, rows, cols, x, 1, y, S, nthreads);
+}
+
+/* ------------------------------------------------ split Q8_0 repack */
+
+int gqo_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out)
+{
+    int64_t rb = gqo_row_bytes(GQO_TYPE_Q8_0, cols);
+    int64_t rs = gqo_row_bytes(GQO_TYPE_Q8_0_SPLIT, cols);
+    if (rb < 0 || rows < 0 || cols <= 0 || !W || !out)
+        return -1;
+    int64_t nb = (cols + O_Q8_0_WEIGHTS - 1) / O_Q8_0_WEIGHTS;
+    int64_t sb = split_scale_bytes(nb);
+    const uint8_t* src = (const uint8_t*)W;
+    uint8_t* dst = (uint8_t*)out;
+    for (int64_t r = 0; r < rows; r++) {
+        const uint8_t* in = src + r * rb;
+        uint8_t* o = dst + r * rs;
+        memset(o, 0, (size_t)sb);
+        for (int64_t b = 0; b < nb; b++) {
+            o[2 * b] = in[b * O_Q8_0_BYTES];
+            o[2 * b + 1] = in[b * O_Q8_0_BYTES + 1];
+            memcpy(o + sb + b * O_Q8_0_WEIGHTS, in + b * O_Q8_0_BYTES + 2, O_Q8_0_WEIGHTS);
+        }
+    }
+    return 0;
 }
 
 /* --------------------------------------------- test-only quantisers */

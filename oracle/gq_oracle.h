@@ -40,6 +40,10 @@ extern "C" {
 #define GQO_TYPE_Q5_0 6
 #define GQO_TYPE_Q5_K 13
 #define GQO_TYPE_Q6_K 14
+/* Q8_0 repacked into the split per-row layout (not a ggml id): per row the
+ * nb fp16 scales, zero padding to a multiple of 16 bytes, then the nb * 32
+ * int8 codes in block order. */
+#define GQO_TYPE_Q8_0_SPLIT 1008
 
 /* Bytes of one row of `cols` input features, or -1 for an unknown type. */
 int64_t gqo_row_bytes(int type, int64_t cols);
@@ -68,6 +72,10 @@ int gqo_matvec(int type, const void* W, int64_t rows, int64_t cols,
 /* Y[m*rows + r] = sum_c w(r,c) * X[m*cols + c] (f64), S likewise. */
 int gqo_matmul(int type, const void* W, int64_t rows, int64_t cols,
                const float* X, int64_t M, double* Y, double* S, int nthreads);
+
+/* Repack rows of Q8_0 blocks into the split per-row layout (row stride
+ * gqo_row_bytes(GQO_TYPE_Q8_0_SPLIT, cols)); padding bytes are zero. */
+int gqo_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out);
 
 /* Test-only reference quantisers (the pages print none for Q4_K). */
 int gqo_quantize_q8_0(const float* w, int64_t rows, int64_t cols, uint8_t* out);
