@@ -369,6 +369,36 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
         warm_us_per_call=round(ms_warm * 1e3, 2))
     log(f"lm_head: {out['qwen05b_lm_head_q8_0']}")
 
+    # the same lm_head repacked into the split per-row layout (scales apart
+    # from the codes), cold over 4 copies like the packed one
+    srb = gq.gq_row_bytes(gq.FMT_Q8_0_SPLIT, cols)
+    split = [gq.gq_q8_0_split_repack(c, rows, cols) for c in copies]
+    torch.cuda.synchronize()
+    sbytes = gemv_bytes(srb, rows, cols)
+
+    def lm_split(cs):
+        sp = stream_ptr()
+        for c in cs:
+            lib.gq_matvec(gq.FMT_Q8_0_SPLIT, c.data_ptr(), rows, cols, xd.data_ptr(), yd.data_ptr(), sp)
+
+    ms_cold = timer.time(lambda: lm_split(split), iters, warmup=2) / len(split)
+    ms_warm = timer.time(lambda: lm_split(split[:1] * 4), iters, warmup=2) / 4
+    out["qwen05b_lm_head_q8_0_split"] = dict(
+        shape=[rows, cols], us_per_call=round(ms_cold * 1e3, 2),
+        GBps=round(sbytes / (ms_cold * 1e-3) / 1e9, 1),
+        pct_hbm=round(100 * sbytes / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+        warm_us_per_call=round(ms_warm * 1e3, 2))
+    log(f"lm_head split layout: {out['qwen05b_lm_head_q8_0_split']}")
+
+    def repack():
+        st = lib.gq_q8_0_split_repack(copies[0].data_ptr(), rows, cols, split[0].data_ptr(), stream_ptr())
+        assert st == 0
+
+    ms = timer.time(repack, 5, warmup=1)
+    out["q8_0_split_repack_lm_head"] = dict(us_per_call=round(ms * 1e3, 1),
+                                            GBps=round(rows * (rb + srb) / (ms * 1e-3) / 1e9, 1))
+    del split
+
     # gq_dequant of the lm_head (bit-exact expansion, 545 MB written)
     dq = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
 

@@ -9,6 +9,7 @@ is no CPU fallback: if the library is not built, loading raises.
     gq_matvec(fmt, W, rows, cols, x, y=None)           -> y [rows] fp32
     gq_matvec_acc(fmt, W, rows, cols, x, y)            -> y += W x
     gq_matvec_swiglu(fmt, W, rows, cols, x, y=None)    -> y = silu(W_gate x) * (W_up x)
+    gq_q8_0_split_repack(W, rows, cols, out=None)      -> W in the split Q8_0 layout
     gq_matvec_experts(fmt, W, n_expert, rows, cols, X, xk, expid, Y=None)
                                                        -> Y[a] = W[expid[a]] X[a // xk]
     gq_matmul(fmt, W, rows, cols, X, Y=None)           -> Y [M, rows] fp32
@@ -30,6 +31,7 @@ FMT_Q4_K = 12
 FMT_Q5_0 = 6
 FMT_Q5_K = 13
 FMT_Q6_K = 14
+FMT_Q8_0_SPLIT = 1008  # Q8_0 repacked by gq_q8_0_split_repack (scales apart from codes)
 
 GQ_OK = 0
 GQ_ERR_NULL = 1
@@ -40,7 +42,7 @@ GQ_ERR_DEVICE = 5
 GQ_ERR_OVERLAP = 6
 
 EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matvec_acc",
-           "gq_matvec_swiglu", "gq_matvec_experts", "gq_matmul")
+           "gq_matvec_swiglu", "gq_matvec_experts", "gq_q8_0_split_repack", "gq_matmul")
 
 _lib = None
 
@@ -70,6 +72,8 @@ def load_library():
     for name in ("gq_matvec", "gq_matvec_acc", "gq_matvec_swiglu"):
         getattr(lib, name).argtypes = [i32, vp, i64, i64, vp, vp, vp]
         getattr(lib, name).restype = i32
+    lib.gq_q8_0_split_repack.argtypes = [vp, i64, i64, vp, vp]
+    lib.gq_q8_0_split_repack.restype = i32
     lib.gq_matvec_experts.argtypes = [i32, vp, i64, i64, i64, vp, i64, vp, i64, vp, vp]
     lib.gq_matvec_experts.restype = i32
     lib.gq_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
@@ -194,6 +198,24 @@ def gq_matvec_experts(fmt: int, W, n_expert: int, rows: int, cols: int, X, xk: i
     if st != GQ_OK:
         raise GQError(st, "gq_matvec_experts")
     return Y
+
+
+def gq_q8_0_split_repack(W, rows: int, cols: int, out=None, stream=None):
+    """Q8_0 rows -> the split per-row layout (uint8 tensor of
+    rows * gq_row_bytes(FMT_Q8_0_SPLIT, cols) bytes), asynchronous."""
+    torch = _torch()
+    _check_w(FMT_Q8_0, W, rows, cols)
+    need = rows * gq_row_bytes(FMT_Q8_0_SPLIT, cols)
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=W.device)
+    _check_dev(out, "out", torch.uint8)
+    if out.numel() < need:
+        raise ValueError("out is too small")
+    st = load_library().gq_q8_0_split_repack(_ptr(W), int(rows), int(cols), _ptr(out),
+                                             _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_q8_0_split_repack")
+    return out
 
 
 def gq_matmul(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):

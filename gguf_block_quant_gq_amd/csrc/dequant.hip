@@ -160,11 +160,67 @@ __global__ __launch_bounds__(kThreads) void dequant_q6_k_kernel(DequantArgs a) {
   }
 }
 
+// Split Q8_0 rows: wave item = (row, 8-block group) as for Q8_0; lane l's four
+// codes are one aligned dword of the code region.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void dequant_q8_0_split_kernel(DequantArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int groups = (a.units + 7) / 8;
+  const int64_t items = a.rows * (int64_t)groups;
+  for (int64_t it = blockIdx.x * (int64_t)kWaves + (threadIdx.x >> 6); it < items;
+       it += (int64_t)gridDim.x * kWaves) {
+    const int64_t row = it / groups;
+    const int gi = (int)(it - row * groups);
+    const int c0 = 256 * gi + 4 * lane;
+    if (c0 >= a.cols) continue;
+    float v[4];
+    Q8SplitQuad::get(a.W + row * a.row_bytes, c0, a.cols, v);
+    float* o = a.out + row * a.cols + c0;
+    store_quad<VEC>(o, c0, a.cols, v[0], v[1], v[2], v[3]);
+  }
+}
+
+// One thread per (row, block): the block's scale to bytes 2b of the output
+// row, its codes to the code region, and (block 0) zeros over the padding.
+__global__ __launch_bounds__(kThreads) void q8_0_split_repack_kernel(const uint8_t* W, int64_t rows,
+                                                                     int nb, int64_t rb, uint8_t* out,
+                                                                     int64_t orb) {
+  const int sb = split_scale_bytes(nb);
+  const int64_t total = rows * (int64_t)nb;
+  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = t / nb;
+    const int b = (int)(t - row * nb);
+    Q8Raw raw;
+    q8_load(W + row * rb + (int64_t)b * kQ8Bytes, raw);
+    uint32_t q[8];
+    q8_codes(raw, q);
+    uint8_t* o = out + row * orb;
+    *(uint16_t*)(o + 2 * b) = (uint16_t)raw.d16;
+    u32x4* c = (u32x4*)(o + sb + 32 * b);
+    c[0] = u32x4{q[0], q[1], q[2], q[3]};
+    c[1] = u32x4{q[4], q[5], q[6], q[7]};
+    if (b == 0)
+      for (int p = 2 * nb; p < sb; p += 2) *(uint16_t*)(o + p) = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_q8_0_split_repack(const uint8_t* W, int64_t rows, int cols, int64_t row_bytes,
+                                    uint8_t* out, int64_t out_row_bytes, hipStream_t s) {
+  const int nb = (cols + 31) / 32;
+  int64_t blocks = (rows * (int64_t)nb + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(q8_0_split_repack_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, W, rows, nb,
+                     row_bytes, out, out_row_bytes);
+  return hipGetLastError();
+}
 
 hipError_t launch_dequant(int fmt, DequantArgs a, hipStream_t s) {
   // units per row: blocks (Q8_0, Q5_0; a wave takes 8) or super-blocks
-  const bool small_blocks = fmt == kFmtQ8_0 || fmt == kFmtQ5_0;
+  const bool small_blocks = fmt == kFmtQ8_0 || fmt == kFmtQ5_0 || fmt == kFmtQ8_0Split;
   a.units = small_blocks ? (a.cols + 31) / 32 : (a.cols + 255) / 256;
   const int64_t items = a.rows * (int64_t)(small_blocks ? (a.units + 7) / 8 : a.units);
   int64_t blocks = (items + kWaves - 1) / kWaves;
@@ -183,6 +239,7 @@ hipError_t launch_dequant(int fmt, DequantArgs a, hipStream_t s) {
     case kFmtQ5_0: GQ_DQ_LAUNCH(dequant_q5_0_kernel); break;
     case kFmtQ5_K: GQ_DQ_LAUNCH(dequant_q5_k_kernel); break;
     case kFmtQ6_K: GQ_DQ_LAUNCH(dequant_q6_k_kernel); break;
+    case kFmtQ8_0Split: GQ_DQ_LAUNCH(dequant_q8_0_split_kernel); break;
     default: return hipErrorInvalidValue;
   }
 #undef GQ_DQ_LAUNCH

@@ -1,5 +1,5 @@
-// gemm_f32.hip -- Y = X W^T on the fp32 matrix cores for Q8_0, Q5_0, Q5_K
-// and Q6_K weights (the prompt-chunk product, "nurllama 0.18.1 API",
+// gemm_f32.hip -- Y = X W^T on the fp32 matrix cores for Q8_0 (packed or
+// split per row), Q5_0, Q5_K and Q6_K weights (the prompt-chunk product, "nurllama 0.18.1 API",
 // model.nu section; the Loom inventory's prefill GEMMs per format).
 //
 // These formats scale every 16 or 32 weights, and scale * code needs up to
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(F32Args a) {
     for (int j = 0; j < 8; ++j) {  // 64 rows x 128 k = 2048 quads, 32 threads per row
       const int qd = tid + 256 * j;
       const int row = r0 + (qd >> 5), k = k0 + 4 * (qd & 31);
-      if (row < a.rows && k < a.cols) Q::load(wr[j], a.W + (int64_t)row * a.row_bytes, k);
+      if (row < a.rows && k < a.cols) Q::load(wr[j], a.W + (int64_t)row * a.row_bytes, k, a.cols);
     }
 #pragma unroll
     for (int j = 0; j < 2 * WM; ++j) {  // 16*WM rows x 128 k, zero past M and cols
@@ -168,7 +168,7 @@ hipError_t launch_wm(const F32Args& a, int WM, int gx, int gy, int ks, hipStream
 }  // namespace
 
 hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s) {
-  if (fmt != kFmtQ8_0 && fmt != kFmtQ5_0 && fmt != kFmtQ5_K && fmt != kFmtQ6_K)
+  if (fmt != kFmtQ8_0 && fmt != kFmtQ5_0 && fmt != kFmtQ5_K && fmt != kFmtQ6_K && fmt != kFmtQ8_0Split)
     return hipErrorInvalidValue;
   const int mtiles = (a.M + 15) / 16;
   const int WM = mtiles >= 4 ? 4 : mtiles >= 2 ? 2 : 1;
@@ -195,6 +195,7 @@ hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s) {
     case kFmtQ8_0: e = launch_wm<Q8Quad>(fa, WM, gx, gy, ks, s); break;
     case kFmtQ5_0: e = launch_wm<Q5_0Quad>(fa, WM, gx, gy, ks, s); break;
     case kFmtQ5_K: e = launch_wm<Q5KQuad>(fa, WM, gx, gy, ks, s); break;
+    case kFmtQ8_0Split: e = launch_wm<Q8SplitQuad>(fa, WM, gx, gy, ks, s); break;
     default: e = launch_wm<Q6KQuad>(fa, WM, gx, gy, ks, s); break;
   }
   if (ks > 1) {

@@ -68,9 +68,34 @@ constexpr int kThreads = 256;
 #define GQ_GEMV_K56_WG_PER_CU GQ_GEMV_WG_PER_CU_RBN
 #endif
 
+// Unit traits: kWantsCols (lane() takes the column count and load() the lane
+// constants) and kQ8Like (scheduled like the Q8_0 units); false if absent.
+template <class F, class = void>
+struct wants_cols : std::false_type {};
+template <class F>
+struct wants_cols<F, std::void_t<decltype(F::kWantsCols)>> : std::integral_constant<bool, F::kWantsCols> {};
+template <class F, class = void>
+struct q8_like : std::false_type {};
+template <class F>
+struct q8_like<F, std::void_t<decltype(F::kQ8Like)>> : std::integral_constant<bool, F::kQ8Like> {};
+
 template <class F>
 constexpr bool is_q8() {
-  return std::is_same<typename F::Base, Q8Unit>::value || std::is_same<typename F::Base, Q8PairUnit>::value;
+  return std::is_same<typename F::Base, Q8Unit>::value || std::is_same<typename F::Base, Q8PairUnit>::value ||
+         q8_like<F>::value;
+}
+
+template <class F>
+__device__ __forceinline__ typename F::Lane make_lane(int gl, const GemvArgs& a) {
+  if constexpr (wants_cols<F>::value) return F::lane(gl, a.cols);
+  else return F::lane(gl);
+}
+
+template <class F>
+__device__ __forceinline__ void load_unit(typename F::Raw& raw, const uint8_t* row, int unit,
+                                          const typename F::Lane& ln) {
+  if constexpr (wants_cols<F>::value) F::load(raw, row, unit, ln);
+  else F::load(raw, row, unit);
 }
 
 template <class F>
@@ -89,7 +114,7 @@ constexpr int out_rows() {
 // the last row: a batch past the end re-reads it and discards the result).
 template <class F, int RB, int EPI>
 __device__ __forceinline__ void load_rows(typename F::Raw (&raw)[RB], const GemvArgs& a,
-                                          int obase, int unit_ld) {
+                                          int obase, int unit_ld, const typename F::Lane& ln) {
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     int row;
@@ -99,7 +124,7 @@ __device__ __forceinline__ void load_rows(typename F::Raw (&raw)[RB], const Gemv
       row = obase + i;
       row = row < a.rows ? row : a.rows - 1;
     }
-    F::load(raw[i], a.W + (int64_t)row * a.row_bytes, unit_ld);
+    load_unit<F>(raw[i], a.W + (int64_t)row * a.row_bytes, unit_ld, ln);
   }
 }
 
@@ -278,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(KernelArgs<EXPERTS> args
   const int tid = threadIdx.x;
   const int grp = tid / G;
   const int gl = tid % G;
-  const typename F::Lane ln = F::lane(gl);
+  const typename F::Lane ln = make_lane<F>(gl, a);
   const int unit = gl;
   const int unit_ld = unit < a.units ? unit : a.units - 1;
 
@@ -293,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(KernelArgs<EXPERTS> args
   XStage<F, G> st;
   issue_x<F, G>(st, a.x, a.cols, 0);
   typename F::Raw buf[RB];
-  load_rows<F, RB, EPI>(buf, a, it0 * kRowsPerIter + grp * kOut, unit_ld);
+  load_rows<F, RB, EPI>(buf, a, it0 * kRowsPerIter + grp * kOut, unit_ld, ln);
   commit_x<F, G>(xs, st);
   __syncthreads();
   typename F::X xr;
@@ -344,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(KernelArgs<EXPERTS> args
     // more, smaller batches) after it: each order measured faster for its
     // format.
     const int nx = it + stride < iters ? it + stride : iters - 1;
-    if constexpr (!kQ8) load_rows<F, RB, EPI>(buf, a, nx * kRowsPerIter + grp * kOut, unit_ld);
+    if constexpr (!kQ8) load_rows<F, RB, EPI>(buf, a, nx * kRowsPerIter + grp * kOut, unit_ld, ln);
     if constexpr (G <= 64) {
 #pragma unroll
       for (int i = 0; i < RB; ++i) acc[i] = group_sum_last<G>(acc[i]);
@@ -359,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(KernelArgs<EXPERTS> args
       }
       if (slot == kSlots - 1) flush(n - (kSlots - 1), kSlots);
     }
-    if constexpr (kQ8) load_rows<F, RB, EPI>(buf, a, nx * kRowsPerIter + grp * kOut, unit_ld);
+    if constexpr (kQ8) load_rows<F, RB, EPI>(buf, a, nx * kRowsPerIter + grp * kOut, unit_ld, ln);
   }
   if constexpr (G > 64) {
     const int used = n % kSlots;
@@ -383,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void gemv_seg_kernel(KernelArgs<EXPERTS> 
   const int tid = threadIdx.x;
   const int grp = tid / G;
   const int gl = tid % G;
-  const typename F::Lane ln = F::lane(gl);
+  const typename F::Lane ln = make_lane<F>(gl, a);
   const int nseg = (a.units + G - 1) / G;
   const int iters = (a.rows + kRowsPerIter - 1) / kRowsPerIter;
 
@@ -396,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void gemv_seg_kernel(KernelArgs<EXPERTS> 
       const int unit = seg * G + gl;
       const int unit_ld = unit < a.units ? unit : a.units - 1;
       typename F::Raw raw[RB];
-      load_rows<F, RB, EPI>(raw, a, obase, unit_ld);
+      load_rows<F, RB, EPI>(raw, a, obase, unit_ld, ln);
       typename F::X xr;
       if (F::valid(unit, a.units, a.cols)) F::load_x(xr, a.x, unit, a.cols);
       else F::zero_x(xr);
@@ -478,6 +503,40 @@ hipError_t dispatch_g(const GemvArgs& a, int cus, hipStream_t s, const ExpertArg
   return with_g<F, 256, EPI>(a, cus, s, ex);
 }
 
+// The split-layout unit's column map depends on the group width: in each
+// pass of G lanes, lane g takes chunks g, g + G, g + 2G, g + 3G, so the chunks
+// of a pass are shared by all G lanes, not by the first `units` of them. The
+// unit count is rounded up to whole passes, so that no lane is folded onto
+// another lane's unit; the unit's own clamp keeps chunks past the row's end
+// in bounds (their x is zero).
+template <int G, int EPI>
+hipError_t split_with_g(GemvArgs a, int cus, hipStream_t s, const ExpertArgs* ex) {
+  a.units = (a.units + G - 1) / G * G;
+  return with_g<Q8SplitUnit<G>, G, EPI>(a, cus, s, ex);
+}
+
+template <int EPI>
+hipError_t dispatch_g_split(const GemvArgs& a, int cus, hipStream_t s, const ExpertArgs* ex) {
+  const int n = a.units;
+  if (n <= 4) return split_with_g<4, EPI>(a, cus, s, ex);
+  if (n <= 8) return split_with_g<8, EPI>(a, cus, s, ex);
+  if (n <= 16) return split_with_g<16, EPI>(a, cus, s, ex);
+  if (n <= 32) return split_with_g<32, EPI>(a, cus, s, ex);
+  if (n <= 64) return split_with_g<64, EPI>(a, cus, s, ex);
+  if (n <= 128) return split_with_g<128, EPI>(a, cus, s, ex);
+  return split_with_g<256, EPI>(a, cus, s, ex);
+}
+
+hipError_t dispatch_split(const GemvArgs& a, int cus, hipStream_t s, int epi, const ExpertArgs* ex) {
+  if (ex && epi != kEpiStore) return hipErrorInvalidValue;
+  switch (epi) {
+    case kEpiStore: return dispatch_g_split<kEpiStore>(a, cus, s, ex);
+    case kEpiAcc: return dispatch_g_split<kEpiAcc>(a, cus, s, nullptr);
+    case kEpiSwiglu: return dispatch_g_split<kEpiSwiglu>(a, cus, s, nullptr);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <class F>
 hipError_t dispatch(const GemvArgs& a, int cus, hipStream_t s, int epi, const ExpertArgs* ex) {
   if (ex && epi != kEpiStore) return hipErrorInvalidValue;
@@ -506,6 +565,10 @@ hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi,
   if (fmt == kFmtQ5_0) {
     a.units = (a.cols + 31) / 32;
     return dispatch<Q5_0Unit>(a, cus, s, epi, ex);
+  }
+  if (fmt == kFmtQ8_0Split) {
+    a.units = ((a.cols + 31) / 32 + 1) / 2;  // four 16-code chunks per lane
+    return dispatch_split(a, cus, s, epi, ex);
   }
   // K-quants: four units per 256-weight super-block
   a.units = 4 * ((a.cols + 255) / 256);

@@ -54,7 +54,8 @@ int check_shape(int fmt, int64_t rows, int64_t cols, int64_t M, int64_t* rb, int
 
 // Formats whose block size is not a multiple of 4 bytes (Q8_0 34, Q5_0 22,
 // Q6_K 210) take 2-byte aligned W, so that a row range starting at any
-// block boundary is accepted; Q4_K and Q5_K blocks (144, 176 B) take 4.
+// block boundary is accepted; Q4_K and Q5_K blocks (144, 176 B) and the
+// split Q8_0 layout (rows of whole 16-byte chunks) take 4.
 int check_align(int fmt, const void* W) {
   const bool two = fmt == GQ_FMT_Q8_0 || fmt == GQ_FMT_Q5_0 || fmt == GQ_FMT_Q6_K;
   const uintptr_t need = two ? 2 : 4;
@@ -75,6 +76,7 @@ int finish(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_DEVICE; }
 #define GQ_F32_MIN_M_BLOCK32 8
 #endif
 int64_t f32_matrix_core_min_m(int fmt) {
+  if (fmt == GQ_FMT_Q8_0_SPLIT) return 2;  // the few-row kernel has no split-layout unit
   return (fmt == GQ_FMT_Q5_K || fmt == GQ_FMT_Q6_K) ? GQ_F32_MIN_M_KQUANT : GQ_F32_MIN_M_BLOCK32;
 }
 
@@ -88,6 +90,10 @@ extern "C" int64_t gq_row_bytes(int fmt, int64_t cols) {
     case GQ_FMT_Q4_K: return ((cols + 255) / 256) * 144;
     case GQ_FMT_Q5_K: return ((cols + 255) / 256) * 176;
     case GQ_FMT_Q6_K: return ((cols + 255) / 256) * 210;
+    case GQ_FMT_Q8_0_SPLIT: {
+      const int64_t nb = (cols + 31) / 32;
+      return ((2 * nb + 15) / 16) * 16 + 32 * nb;
+    }
     default: return -1;
   }
 }
@@ -193,6 +199,22 @@ extern "C" int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64
   gq::GemvArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
   const gq::ExpertArgs ex{expid, ebytes, (int)n_expert, (int)xk, (int)n_assign};
   return finish(gq::launch_gemv(fmt, a, cus, (hipStream_t)stream, gq::kEpiStore, &ex));
+}
+
+extern "C" int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out,
+                                    void* stream) {
+  int64_t rb = 0, wbytes = 0, orb = 0, obytes = 0;
+  int st = check_shape(GQ_FMT_Q8_0, rows, cols, 1, &rb, &wbytes);
+  if (st != GQ_OK) return st;
+  if ((st = check_shape(GQ_FMT_Q8_0_SPLIT, rows, cols, 1, &orb, &obytes)) != GQ_OK) return st;
+  if (rows == 0) return GQ_OK;
+  if (!W || !out) return GQ_ERR_NULL;
+  if ((st = check_align(GQ_FMT_Q8_0, W)) != GQ_OK) return st;
+  if ((st = check_align(GQ_FMT_Q8_0_SPLIT, out)) != GQ_OK) return st;
+  if (overlaps(out, obytes, W, wbytes)) return GQ_ERR_OVERLAP;
+  (void)hipGetLastError();
+  return finish(gq::launch_q8_0_split_repack((const uint8_t*)W, rows, (int)cols, rb, (uint8_t*)out,
+                                             orb, (hipStream_t)stream));
 }
 
 extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,

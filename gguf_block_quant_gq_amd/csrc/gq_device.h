@@ -37,6 +37,10 @@ constexpr int kQ5KBytes = 176;
 constexpr int kQ6KWeights = 256;
 constexpr int kQ6KBytes = 210;
 
+// Q8_0 split per-row layout: the nb fp16 scales, zero padding to a multiple
+// of 16 bytes, then the nb * 32 codes in block order.
+__host__ __device__ constexpr int split_scale_bytes(int nb) { return ((2 * nb + 15) / 16) * 16; }
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

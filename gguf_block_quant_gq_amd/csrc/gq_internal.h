@@ -12,6 +12,7 @@ constexpr int kFmtQ4_K = 12;
 constexpr int kFmtQ5_0 = 6;
 constexpr int kFmtQ5_K = 13;
 constexpr int kFmtQ6_K = 14;
+constexpr int kFmtQ8_0Split = 1008;  // Q8_0 repacked: scales first, then codes
 
 struct GemvArgs {
   const uint8_t* W;
@@ -61,6 +62,10 @@ struct GemmArgs {
   int M;
   int units;
 };
+
+// Q8_0 rows -> the split per-row layout (gq_q8_0_split_repack).
+hipError_t launch_q8_0_split_repack(const uint8_t* W, int64_t rows, int cols, int64_t row_bytes,
+                                    uint8_t* out, int64_t out_row_bytes, hipStream_t s);
 
 // All launchers enqueue on `s` and return the launch status.
 // `units` is filled in by the launcher; `cus` is the device's CU count.

@@ -39,6 +39,7 @@ struct Q8Quad {
     load(r, row, i0);
     decode(r, i0, v);
   }
+  __device__ static void load(Raw& r, const uint8_t* row, int i0, int) { load(r, row, i0); }
 };
 
 // Q5_0: block i0 / 32, t = i0 % 32: nibble bytes (t % 16) .. +3 (low nibbles
@@ -71,6 +72,7 @@ struct Q5_0Quad {
     load(r, row, i0);
     decode(r, i0, v);
   }
+  __device__ static void load(Raw& r, const uint8_t* row, int i0, int) { load(r, row, i0); }
 };
 
 // Q5_K: super-block i0 / 256, i = i0 % 256 in sub-block j = i / 32 (g = j / 2,
@@ -102,6 +104,7 @@ struct Q5KQuad {
     load(r, row, i0);
     decode(r, i0, v);
   }
+  __device__ static void load(Raw& r, const uint8_t* row, int i0, int) { load(r, row, i0); }
 };
 
 // Q6_K: super-block i0 / 256, i = i0 % 256 = 128 n + 32 k + l0: nibble k / 2
@@ -132,6 +135,29 @@ struct Q6KQuad {
   __device__ static void get(const uint8_t* row, int i0, float v[4]) {
     Raw r;
     load(r, row, i0);
+    decode(r, i0, v);
+  }
+  __device__ static void load(Raw& r, const uint8_t* row, int i0, int) { load(r, row, i0); }
+};
+
+// Q8_0 split per-row layout: code i0 .. i0+3 at the code region + i0 (4-byte
+// aligned), the scale of block i0 / 32 at bytes 2 (i0 / 32).
+struct Q8SplitQuad {
+  struct Raw {
+    uint32_t d16, q;
+  };
+  __device__ static void load(Raw& r, const uint8_t* row, int i0, int cols) {
+    r.d16 = load_u16(row + 2 * (i0 >> 5));
+    r.q = load_u32(row + split_scale_bytes((cols + 31) / 32) + i0);
+  }
+  __device__ static void decode(const Raw& r, int, float v[4]) {
+    const float d = half_bits_to_float(r.d16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = d * i8_at(r.q, e);
+  }
+  __device__ static void get(const uint8_t* row, int i0, int cols, float v[4]) {
+    Raw r;
+    load(r, row, i0, cols);
     decode(r, i0, v);
   }
 };

@@ -763,4 +763,112 @@ struct Q6KUnit {
   }
 };
 
+// ------------------------------------------------ Q8_0 split-layout unit
+// Rows repacked so that the fp16 scales come first (split_scale_bytes(nb))
+// and the codes follow in block order. Lane gl of a G-lane row group owns the
+// 16-code chunks c_j = 4G * segment + gl + j G (j < 4): every 16-byte load of
+// a wave reads one contiguous run of the row's codes. Chunk c holds columns
+// 16c .. 16c + 15 and uses the scale of block c / 2. The scale region's size
+// depends on the row length, so the kernels pass the column count to lane().
+template <int G>
+struct Q8SplitUnit {
+  using Base = Q8SplitUnit<G>;
+  static constexpr bool kWantsCols = true;
+  static constexpr bool kQ8Like = true;
+  static constexpr int kPerUnitCols = 64;
+  struct X {
+    float v[64];  // chunk j's 16 values at v[16 j ..]
+  };
+  struct Raw {
+    u32x4 c[4];
+    uint32_t d16[4];
+  };
+  struct Lane {
+    int scale_bytes;  // offset of the codes in a row
+    int nchunk;       // 16-code chunks per row
+  };
+
+  __device__ static Lane lane(int, int cols) {
+    const int nb = (cols + 31) / 32;
+    return Lane{split_scale_bytes(nb), 2 * nb};
+  }
+
+  __device__ static int chunk0(int unit) { return (unit / G) * 4 * G + unit % G; }
+
+  __device__ static bool valid(int unit, int units, int cols) {
+    return unit < units && 16 * chunk0(unit) < cols;
+  }
+
+  __device__ static void load_x(X& x, const float* xv, int unit, int cols) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c0 = 16 * (chunk0(unit) + j * G);
+      if (c0 + 16 <= cols) {
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+          const f32x4 t = load_f32x4(xv + c0 + i);
+          x.v[16 * j + i] = t.x; x.v[16 * j + i + 1] = t.y; x.v[16 * j + i + 2] = t.z; x.v[16 * j + i + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x.v[16 * j + i] = (c0 + i < cols) ? xv[c0 + i] : 0.f;
+      }
+    }
+  }
+
+  __device__ static void zero_x(X& x) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x.v[i] = 0.f;
+  }
+
+  __device__ static void finish_x(X&) {}
+
+  static constexpr int kChunks = 16;
+  __device__ static int x_chunk(int gl, int k) { return 4 * (gl + (k >> 2) * G) + (k & 3); }
+  __device__ static void set_x(X& x, const f32x4 (&c)[kChunks]) {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      x.v[4 * k] = c[k].x; x.v[4 * k + 1] = c[k].y; x.v[4 * k + 2] = c[k].z; x.v[4 * k + 3] = c[k].w;
+    }
+  }
+
+  // Chunks past the row's end read its last chunk (their x is zero).
+  __device__ static void load(Raw& raw, const uint8_t* row, int unit, const Lane& ln) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int c = chunk0(unit) + j * G;
+      c = c < ln.nchunk ? c : ln.nchunk - 1;
+      raw.c[j] = load_u32x4(row + ln.scale_bytes + 16 * c);
+      raw.d16[j] = load_u16(row + 2 * (c >> 1));
+    }
+  }
+
+  __device__ static void zero(Raw& raw) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      raw.c[j] = u32x4{0, 0, 0, 0};
+      raw.d16[j] = 0u;
+    }
+  }
+
+  __device__ static float dot(const Raw& raw, const X& x, const Lane&) {
+    float r = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w[4] = {raw.c[j].x, raw.c[j].y, raw.c[j].z, raw.c[j].w};
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; k += 2) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          s0 = __builtin_fmaf(i8_at(w[k], b), x.v[16 * j + 4 * k + b], s0);
+          s1 = __builtin_fmaf(i8_at(w[k + 1], b), x.v[16 * j + 4 * k + 4 + b], s1);
+        }
+      }
+      r = __builtin_fmaf(half_bits_to_float(raw.d16[j]), s0 + s1, r);
+    }
+    return r;
+  }
+};
+
 }  // namespace gq

@@ -34,6 +34,13 @@
  *     ql[64n + 32(k&1) + l] as its low four bits and bits 2k, 2k+1 of
  *     qh[32n + l] as its top two, scale number i/16 for weight i;
  *     w = (d*scale)*(code - 32).
+ *   Q8_0 split (fmt 1008): the same Q8_0 data repacked per row with the
+ *     scales apart from the codes ("nurllama 0.18.1 API", kernels.nu section:
+ *     an uploaded q8_0 tensor is repacked into a split per-row layout; the
+ *     layout is not printed there, this is the one taken): the ceil(cols/32)
+ *     fp16 scales, zero padding to a multiple of 16 bytes, then the codes of
+ *     the blocks in order. Made by gq_q8_0_split_repack; the matvec reads its
+ *     codes as one contiguous, 16-byte aligned stream.
  *   Q5_0, Q5_K and Q6_K appear next to Q4_K in the model files the pages run
  *   ("nurllama" README, "What it runs"; their per-format matvec kernels are
  *   listed in "nurllama 0.18.1 API", kernels.nu section). The byte layouts
@@ -56,7 +63,7 @@
  * Alignment
  *   Q8_0, Q5_0 and Q6_K W: 2-byte aligned (a row range of such a tensor
  *   starts on any block boundary, and their blocks are 34, 22 and 210 bytes).
- *   Q4_K and Q5_K W: 4-byte aligned. x, y, X, Y, out: 4-byte
+ *   Q4_K, Q5_K and split Q8_0 W: 4-byte aligned. x, y, X, Y, out: 4-byte
  *   aligned. An output that overlaps an input is rejected (GQ_ERR_OVERLAP).
  *
  * Errors
@@ -86,6 +93,7 @@ enum gq_fmt {
     GQ_FMT_Q4_K = 12,
     GQ_FMT_Q5_K = 13,
     GQ_FMT_Q6_K = 14,
+    GQ_FMT_Q8_0_SPLIT = 1008, /* Q8_0 in the split per-row layout (not a ggml id) */
 };
 
 enum gq_status {
@@ -177,13 +185,23 @@ int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, in
                       float* Y, void* stream);
 
 /*
+ * Repack `rows` rows of Q8_0 blocks (W, rows * gq_row_bytes(GQ_FMT_Q8_0,
+ * cols) bytes, 2-byte aligned) into the split per-row layout at `out`
+ * (rows * gq_row_bytes(GQ_FMT_Q8_0_SPLIT, cols) bytes, 4-byte aligned, must
+ * not overlap W); padding bytes are written as zero. A one-time step after
+ * upload ("nurllama 0.18.1 API", kernels.nu section, the q8_0 repack);
+ * every entry point then accepts GQ_FMT_Q8_0_SPLIT. Asynchronous on `stream`.
+ */
+int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out, void* stream);
+
+/*
  * Y[m*rows + r] = sum_{c < cols} w(r, c) * X[m*cols + c], for m < M, r < rows;
  * Y is overwritten. X: [M, cols] row-major fp32; Y: [M, rows] row-major fp32.
  * The batched form used for prompt chunks ("nurllama 0.18.1 API", model.nu
  * section: the matmuls run over up to 64 positions at once, each weight read
  * once per chunk). M == 1 runs the gq_matvec kernel. Q4_K with M >= 2 runs
  * on the fp16 matrix cores with exact operands (workspace described above).
- * Q5_K and Q6_K with M >= 2, and Q8_0 and Q5_0 with M >= 8, run on the fp32
+ * Q5_K, Q6_K and split Q8_0 with M >= 2, and Q8_0 and Q5_0 with M >= 8, run on the fp32
  * matrix cores: each k-chunk of W is dequantised exactly to fp32 and
  * multiplied with the fp32 activations (a workspace of 4 * M * rows bytes per
  * extra split when the k range is split over workgroups). Q8_0 and Q5_0 with

@@ -156,3 +156,18 @@ def test_validation_experts(lib):
     # Y overlapping the expert ids, or the last expert's weights
     assert _mx(lib, expid=Y_OK + 16) == gq.GQ_ERR_OVERLAP
     assert _mx(lib, Y=W_OK + 4 * 4 * 144 - 4) == gq.GQ_ERR_OVERLAP
+
+
+def test_split_layout_row_bytes_and_repack_validation(lib, oracle):
+    for cols in (1, 31, 32, 33, 896, 4096, 14336):
+        assert gq.gq_row_bytes(1008, cols) == oracle.row_bytes(1008, cols)
+    rp = lib.gq_q8_0_split_repack
+    assert rp(W_OK, 4, 896, Y_OK, None) != gq.GQ_ERR_ALIGN           # passes the host checks
+    assert rp(W_OK + 1, 4, 896, Y_OK, None) == gq.GQ_ERR_ALIGN       # W: 2-byte aligned
+    assert rp(W_OK, 4, 896, Y_OK + 2, None) == gq.GQ_ERR_ALIGN       # out: 4-byte aligned
+    assert rp(None, 4, 896, Y_OK, None) == gq.GQ_ERR_NULL
+    assert rp(W_OK, -1, 896, Y_OK, None) == gq.GQ_ERR_SHAPE
+    assert rp(W_OK, 0, 896, None, None) == gq.GQ_OK
+    assert rp(W_OK, 4, 896, W_OK + 8, None) == gq.GQ_ERR_OVERLAP
+    # the split layout needs 4-byte aligned W in every entry point
+    assert _mv(lib, fmt=1008, W=W_OK + 2) == gq.GQ_ERR_ALIGN
