@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
-SMALL_M = (4, 8)               # few activation rows (padded to 16 on the matrix cores)
+SMALL_M = (2, 4, 8)            # few activation rows (batched matvec or matrix cores)
 
 
 def log(msg: str) -> None:

@@ -42,7 +42,8 @@ GQ_ERR_DEVICE = 5
 GQ_ERR_OVERLAP = 6
 
 EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matvec_acc",
-           "gq_matvec_swiglu", "gq_matvec_experts", "gq_q8_0_split_repack", "gq_matmul")
+           "gq_matvec_swiglu", "gq_matvec_experts", "gq_matvec_batch", "gq_q8_0_split_repack",
+           "gq_matmul")
 
 _lib = None
 
@@ -76,8 +77,9 @@ def load_library():
     lib.gq_q8_0_split_repack.restype = i32
     lib.gq_matvec_experts.argtypes = [i32, vp, i64, i64, i64, vp, i64, vp, i64, vp, vp]
     lib.gq_matvec_experts.restype = i32
-    lib.gq_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
-    lib.gq_matmul.restype = i32
+    for name in ("gq_matmul", "gq_matvec_batch"):
+        getattr(lib, name).argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
+        getattr(lib, name).restype = i32
     _lib = lib
     return lib
 
@@ -218,8 +220,7 @@ def gq_q8_0_split_repack(W, rows: int, cols: int, out=None, stream=None):
     return out
 
 
-def gq_matmul(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):
-    """Y[M, rows] = X[M, cols] W^T on `stream`, asynchronous."""
+def _rows_product(name: str, fmt: int, W, rows: int, cols: int, X, Y, stream):
     torch = _torch()
     _check_w(fmt, W, rows, cols)
     _check_dev(X, "X", torch.float32)
@@ -231,8 +232,19 @@ def gq_matmul(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):
     _check_dev(Y, "Y", torch.float32)
     if Y.numel() < M * rows:
         raise ValueError("Y is too small")
-    st = load_library().gq_matmul(int(fmt), _ptr(W), int(rows), int(cols), _ptr(X), int(M),
-                                  _ptr(Y), _stream_handle(stream))
+    st = getattr(load_library(), name)(int(fmt), _ptr(W), int(rows), int(cols), _ptr(X), int(M),
+                                       _ptr(Y), _stream_handle(stream))
     if st != GQ_OK:
-        raise GQError(st, "gq_matmul")
+        raise GQError(st, name)
     return Y
+
+
+def gq_matmul(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):
+    """Y[M, rows] = X[M, cols] W^T on `stream`, asynchronous."""
+    return _rows_product("gq_matmul", fmt, W, rows, cols, X, Y, stream)
+
+
+def gq_matvec_batch(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):
+    """Y[b] = W @ X[b] for every row b of X, each row bit-identical to
+    gq_matvec of that row, asynchronous."""
+    return _rows_product("gq_matvec_batch", fmt, W, rows, cols, X, Y, stream)

@@ -264,11 +264,12 @@ __device__ __forceinline__ GemvArgs base_args(const GemvExpertArgs& a) { return 
 // Expert-batched calls: point a (the workgroup's copy of the arguments) at
 // the expert, activation row and output row of assignment blockIdx.y. An
 // expert id outside [0, n_expert) reads no weights: the assignment's output
-// row is filled with NaN instead. Returns false when there is nothing more
+// row is filled with NaN instead. Without an id table (the batched matvec)
+// every assignment uses W itself. Returns false when there is nothing more
 // to do.
 __device__ __forceinline__ bool bind_assignment(GemvArgs& a, const ExpertArgs& ex) {
   const int as = blockIdx.y;
-  const int e = ex.expid[as];
+  const int e = ex.expid ? ex.expid[as] : 0;
   a.x += (int64_t)(as / ex.xk) * a.cols;
   a.y += (int64_t)as * a.rows;
   if (e < 0 || e >= ex.n_expert) {

@@ -75,6 +75,13 @@ int finish(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_DEVICE; }
 #ifndef GQ_F32_MIN_M_BLOCK32
 #define GQ_F32_MIN_M_BLOCK32 8
 #endif
+// Products of a few activation rows (M < 16) with M * rows * cols at most
+// this many weight-rows run as the batched matvec.
+#ifndef GQ_BATCH_MAX_WORK
+#define GQ_BATCH_MAX_WORK (int64_t(1) << 28)
+#endif
+constexpr int64_t kBatchMaxWork = GQ_BATCH_MAX_WORK;
+
 int64_t f32_matrix_core_min_m(int fmt) {
   if (fmt == GQ_FMT_Q8_0_SPLIT) return 2;  // the few-row kernel has no split-layout unit
   return (fmt == GQ_FMT_Q5_K || fmt == GQ_FMT_Q6_K) ? GQ_F32_MIN_M_KQUANT : GQ_F32_MIN_M_BLOCK32;
@@ -201,6 +208,39 @@ extern "C" int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64
   return finish(gq::launch_gemv(fmt, a, cus, (hipStream_t)stream, gq::kEpiStore, &ex));
 }
 
+namespace {
+
+// Shared by gq_matvec_batch and the few-row routing of gq_matmul (arguments
+// already checked): one launch of the matvec kernels over `batch` activation
+// rows, each row a grid slice of its own.
+int batch_launch(int fmt, const void* W, int64_t rb, int64_t rows, int64_t cols, const float* X,
+                 int64_t batch, float* Y, void* stream, int cus) {
+  gq::GemvArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
+  const gq::ExpertArgs ex{nullptr, 0, 1, 1, (int)batch};
+  return finish(gq::launch_gemv(fmt, a, cus, (hipStream_t)stream, gq::kEpiStore, &ex));
+}
+
+}  // namespace
+
+extern "C" int gq_matvec_batch(int fmt, const void* W, int64_t rows, int64_t cols,
+                               const float* X, int64_t batch, float* Y, void* stream) {
+  int64_t rb = 0, wbytes = 0;
+  int st = check_shape(fmt, rows, cols, batch, &rb, &wbytes);
+  if (st != GQ_OK) return st;
+  if (batch > 65535) return GQ_ERR_SHAPE;  // the grid's second dimension
+  if (rows == 0 || batch == 0) return GQ_OK;
+  if (rows > INT64_MAX / 4 / batch || cols > INT64_MAX / 4 / batch) return GQ_ERR_SHAPE;
+  if (!W || !X || !Y) return GQ_ERR_NULL;
+  if ((st = check_align(fmt, W)) != GQ_OK) return st;
+  if ((uintptr_t)X % 4 || (uintptr_t)Y % 4) return GQ_ERR_ALIGN;
+  if (overlaps(Y, batch * rows * 4, W, wbytes) || overlaps(Y, batch * rows * 4, X, batch * cols * 4))
+    return GQ_ERR_OVERLAP;
+  const int cus = current_cus();
+  if (cus <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  return batch_launch(fmt, W, rb, rows, cols, X, batch, Y, stream, cus);
+}
+
 extern "C" int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out,
                                     void* stream) {
   int64_t rb = 0, wbytes = 0, orb = 0, obytes = 0;
@@ -233,15 +273,19 @@ extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, con
   const int cus = current_cus();
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
-  // One activation row is the matvec (same rounding, its kernel). Q4_K with
-  // two or more rows runs on the fp16 matrix cores (exact operands): padded
-  // to 16 rows it was measured faster than the fp32 few-row kernel from M = 2
-  // on (the latter re-reads each activation row per weight-row batch). The
-  // other formats run on the fp32 matrix cores from a per-format M.
+  // One activation row is the matvec (same rounding, its kernel). A few rows
+  // over a small enough product run as the batched matvec, so each row again
+  // rounds exactly as the matvec does (its cost grows with M * rows * cols:
+  // every row repeats the decode; measured faster than the matrix cores up
+  // to about 2^28 weight-rows for every format). Larger Q4_K products run on
+  // the fp16 matrix cores (exact operands), the other formats on the fp32
+  // matrix cores from a per-format M, else on the fp32 few-row kernel.
   if (M == 1) {
     gq::GemvArgs v{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
     return finish(gq::launch_gemv(fmt, v, cus, (hipStream_t)stream));
   }
+  if (M < 16 && rows * cols <= kBatchMaxWork / M)
+    return batch_launch(fmt, W, rb, rows, cols, X, M, Y, stream, cus);
   gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
   if (fmt == GQ_FMT_Q4_K) return finish(gq::launch_gemm_mfma(fmt, a, cus, (hipStream_t)stream));
   if (M >= f32_matrix_core_min_m(fmt))

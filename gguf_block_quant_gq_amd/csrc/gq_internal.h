@@ -26,7 +26,8 @@ struct GemvArgs {
 
 // The expert-batched form (gq_matvec_experts): assignment a = blockIdx.y
 // multiplies expert expid[a] (at W + expid[a] * expert_bytes) by activation
-// row a / xk of x and writes row a of y (rows floats each). Kept out of
+// row a / xk of x and writes row a of y (rows floats each). With expid null
+// (gq_matvec_batch) every assignment multiplies W itself. Kept out of
 // GemvArgs so that the plain matvec's kernel arguments stay small.
 struct ExpertArgs {
   const int32_t* expid;

@@ -185,6 +185,25 @@ int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, in
                       float* Y, void* stream);
 
 /*
+ * Batched matvec: `batch` activation rows against one weight matrix, each
+ * rounded exactly as a lone gq_matvec call rounds it:
+ *   Y[b*rows + r] = sum_{c < cols} w(r, c) * X[b*cols + c],  b < batch, r < rows,
+ * and Y's row b equals gq_matvec(fmt, W, rows, cols, X + b*cols, ...) bit for
+ * bit, whatever the batch size. The pages' matvec takes a batch count
+ * ("nurllama 0.18.1 API", kernels.nu section); a chunked prompt must
+ * continue exactly as the unbatched reference does ("nurllama" README, "How
+ * it is checked"), and a kernel variant is a dispatch choice, never a change
+ * of results (same README, "What it runs"). One launch: every batch row is a slice of the matvec grid, and
+ * the slices walk the same rows together, so W is streamed from HBM about
+ * once. X: [batch, cols] row-major fp32 (4-byte aligned); Y: [batch, rows],
+ * overwritten, must not overlap W or X. batch is at most 65535 (GQ_ERR_SHAPE
+ * beyond); batch == 0 or rows == 0 is a no-op. No workspace. Asynchronous
+ * on `stream`.
+ */
+int gq_matvec_batch(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,
+                    int64_t batch, float* Y, void* stream);
+
+/*
  * Repack `rows` rows of Q8_0 blocks (W, rows * gq_row_bytes(GQ_FMT_Q8_0,
  * cols) bytes, 2-byte aligned) into the split per-row layout at `out`
  * (rows * gq_row_bytes(GQ_FMT_Q8_0_SPLIT, cols) bytes, 4-byte aligned, must
@@ -199,15 +218,17 @@ int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out, v
  * Y is overwritten. X: [M, cols] row-major fp32; Y: [M, rows] row-major fp32.
  * The batched form used for prompt chunks ("nurllama 0.18.1 API", model.nu
  * section: the matmuls run over up to 64 positions at once, each weight read
- * once per chunk). M == 1 runs the gq_matvec kernel. Q4_K with M >= 2 runs
- * on the fp16 matrix cores with exact operands (workspace described above).
- * Q5_K, Q6_K and split Q8_0 with M >= 2, and Q8_0 and Q5_0 with M >= 8, run on the fp32
- * matrix cores: each k-chunk of W is dequantised exactly to fp32 and
- * multiplied with the fp32 activations (a workspace of 4 * M * rows bytes per
- * extra split when the k range is split over workgroups). Q8_0 and Q5_0 with
- * 2 <= M < 8 stream W once per 15 activation rows on the fp32 vector units. Same
- * accuracy bound as gq_matvec; repeated calls give bit-identical results.
- * Asynchronous on `stream`.
+ * once per chunk). M == 1 runs the gq_matvec kernel. With M < 16 and
+ * M * rows * cols <= 2^28 the call is gq_matvec_batch, so every row of Y
+ * equals gq_matvec of its activation row bit for bit. Otherwise Q4_K runs on
+ * the fp16 matrix cores with exact operands (workspace described above);
+ * Q5_K, Q6_K and split Q8_0 with M >= 2, and Q8_0 and Q5_0 with M >= 8, run
+ * on the fp32 matrix cores: each k-chunk of W is dequantised exactly to fp32
+ * and multiplied with the fp32 activations (a workspace of 4 * M * rows bytes
+ * per extra split when the k range is split over workgroups); Q8_0 and Q5_0
+ * with 2 <= M < 8 stream W once per 15 activation rows on the fp32 vector
+ * units. Same accuracy bound as gq_matvec; repeated calls give bit-identical
+ * results. Asynchronous on `stream`.
  */
 int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
               const float* X, int64_t M, float* Y, void* stream);

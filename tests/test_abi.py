@@ -82,11 +82,15 @@ def _mm(lib, fmt=12, W=W_OK, rows=4, cols=256, X=X_OK, M=2, Y=Y_OK):
     return lib.gq_matmul(fmt, W, rows, cols, X, M, Y, None)
 
 
+def _mb(lib, fmt=12, W=W_OK, rows=4, cols=256, X=X_OK, M=2, Y=Y_OK):
+    return lib.gq_matvec_batch(fmt, W, rows, cols, X, M, Y, None)
+
+
 def _dq(lib, fmt=12, W=W_OK, rows=4, cols=256, out=Y_OK):
     return lib.gq_dequant(fmt, W, rows, cols, out)
 
 
-@pytest.mark.parametrize("call", [_mv, _mva, _mvs, _mm, _dq])
+@pytest.mark.parametrize("call", [_mv, _mva, _mvs, _mm, _mb, _dq])
 def test_validation_before_any_device_call(lib, call):
     for bad in (0, 7, 10, 11, 15, -1):   # Q5_1, Q2_K, Q3_K, IQ... have no kernels
         assert call(lib, fmt=bad) == gq.GQ_ERR_FMT
@@ -132,6 +136,20 @@ def test_validation_vectors(lib):
     # likewise Q5_0 (22-byte blocks) and Q6_K (210-byte super-blocks)
     assert _mv(lib, fmt=6, W=W_OK + 22, y=W_OK + 24) == gq.GQ_ERR_OVERLAP
     assert _mv(lib, fmt=14, W=W_OK + 210, y=W_OK + 212) == gq.GQ_ERR_OVERLAP
+
+
+def test_validation_batch(lib):
+    assert _mb(lib, M=-1) == gq.GQ_ERR_SHAPE
+    assert _mb(lib, M=65536) == gq.GQ_ERR_SHAPE     # the grid's second dimension
+    assert _mb(lib, M=65535, Y=None) == gq.GQ_ERR_NULL
+    assert _mb(lib, M=0, X=None, Y=None) == gq.GQ_OK
+    assert _mb(lib, X=None) == gq.GQ_ERR_NULL
+    assert _mb(lib, Y=None) == gq.GQ_ERR_NULL
+    assert _mb(lib, X=X_OK + 2) == gq.GQ_ERR_ALIGN
+    assert _mb(lib, Y=Y_OK + 1) == gq.GQ_ERR_ALIGN
+    # Y is [M, rows]: the second output row overlapping X's second row
+    assert _mb(lib, Y=X_OK + 256 * 4 + 4) == gq.GQ_ERR_OVERLAP
+    assert _mb(lib, Y=W_OK + 4 * 144 - 4) == gq.GQ_ERR_OVERLAP
 
 
 def _mx(lib, fmt=12, W=W_OK, n_expert=4, rows=4, cols=256, X=X_OK, xk=2, expid=0x40000,

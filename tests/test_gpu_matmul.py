@@ -75,3 +75,39 @@ def test_rows_agree_with_matvec_and_empty(gq, oracle):
     e = torch.empty(0, dtype=torch.float32, device="cuda")
     gq.gq_matmul(12, Wd, rows, cols, torch.empty((0, cols), device="cuda"), Y=e)
     gq.gq_matmul(12, Wd, 0, cols, to_dev(X), Y=e)
+
+
+@pytest.mark.parametrize("fmt,rows,cols,M", [
+    (12, 4096, 4096, 4), (12, 896, 896, 15), (8, 4096, 4096, 7), (14, 2048, 768, 3),
+    (13, 300, 4096, 2), (6, 4864, 896, 9),
+])
+def test_few_rows_round_like_matvec(gq, fmt, rows, cols, M):
+    """Few activation rows over a small product are the batched matvec: every
+    row of Y equals gq_matvec of its activation row bit for bit."""
+    rng = synth.rng_for(610, fmt * 100000 + rows + M)
+    W = to_dev(synth.weights(fmt, rows, cols, rng))
+    X = to_dev(synth.activations((M, cols), rng))
+    print(f"[matmul] few rows fmt={fmt} rows={rows} cols={cols} M={M}", flush=True)
+    Y = to_host(gq.gq_matmul(fmt, W, rows, cols, X))
+    for m in range(M):
+        y = to_host(gq.gq_matvec(fmt, W, rows, cols, X[m]))
+        assert np.array_equal(y.view(np.uint32), Y[m].view(np.uint32)), m
+
+
+@pytest.mark.parametrize("fmt,rows,cols,M", [
+    (12, 14336, 4096, 5),     # Q4_K past the batched-matvec bound: fp16 matrix cores
+    (8, 151936, 896, 2),      # Q8_0 lm_head, two rows: the fp32 few-row kernel
+    (14, 4096, 14336, 5),     # Q6_K: fp32 matrix cores
+])
+def test_few_rows_large_products(gq, oracle, fmt, rows, cols, M):
+    """A few activation rows over products larger than 2^28 weight-rows run
+    on the other kernels; the oracle checks a sample of output rows."""
+    rng = synth.rng_for(611, fmt * 100000 + M)
+    W = synth.weights(fmt, rows, cols, rng)
+    X = synth.activations((M, cols), rng)
+    print(f"[matmul] large few-row product fmt={fmt} rows={rows} cols={cols} M={M}", flush=True)
+    Y = _run(gq, fmt, W, rows, cols, X)
+    idx = np.unique(np.concatenate([np.arange(0, rows, 131), [1, 31, 32, 63, 64, rows - 1]]))
+    Ws = oracle.select_rows(fmt, W, cols, idx)
+    ref, S = oracle.matmul(fmt, Ws, idx.size, cols, X, nthreads=oracle_threads())
+    assert_within_tolerance(Y[:, idx], ref, S, f"large few-row fmt={fmt} M={M}")
