@@ -16,7 +16,9 @@ pytestmark = pytest.mark.gpu
 SPLIT = 1008
 
 SHAPES = [(1, 32), (63, 64), (65, 96), (3, 70), (5, 33), (64, 1024), (7, 1053), (130, 4096),
-          (17, 40000), (1000, 160), (151936, 896)]
+          (17, 40000), (1000, 160), (151936, 896),
+          # more row lengths: 28 to 1792 chunks, one ragged
+          (5, 448), (9, 1792), (300, 3584), (64, 14336), (33, 890), (3, 28672)]
 
 
 def _repack(gq, oracle, W, rows, cols):
