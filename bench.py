@@ -490,7 +490,28 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
         out[name] = dict(us_per_call=round(ms * 1e3, 2), expert_bytes_per_call=int(b),
                          GBps=round(b / (ms * 1e-3) / 1e9, 1),
                          pct_hbm=round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1))
-        del g, Wd
+        del g
+        if n_expert == 8:
+            # the prefill of the same layer: 512 tokens, top 2, bucketed by
+            # expert (a skewed split of the 1024 rows), one grouped call
+            counts = [230, 190, 150, 130, 110, 90, 74, 50]
+            Xg = torch.from_numpy(synth.activations((sum(counts), c), rng)).cuda()
+            Yg = torch.empty((sum(counts), r), dtype=torch.float32, device="cuda")
+            import ctypes
+            carr = (ctypes.c_int64 * n_expert)(*counts)
+
+            def grouped(f=f, r=r, c=c, Wd=Wd, Xg=Xg, Yg=Yg, carr=carr):
+                st = lib.gq_matmul_experts(f, Wd.data_ptr(), n_expert, r, c, Xg.data_ptr(), carr,
+                                           Yg.data_ptr(), stream_ptr())
+                assert st == 0
+
+            ms = timer.time(grouped, 5, warmup=1)
+            tf = 2.0 * sum(counts) * r * c / (ms * 1e-3) / 1e12
+            out["moe_prefill_512x2_of_8_14336x4096_q4_k"] = dict(
+                rows_per_expert=counts, us_per_call=round(ms * 1e3, 1), TFLOPs=round(tf, 2),
+                pct_mfma_f16_peak=round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2))
+            del Xg, Yg
+        del Wd
     log(f"moe: { {k: v for k, v in out.items() if k.startswith('moe')} }")
 
     # prefill products of the other formats on the fp32 matrix cores (the

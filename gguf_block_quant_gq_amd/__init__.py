@@ -43,7 +43,7 @@ GQ_ERR_OVERLAP = 6
 
 EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matvec_acc",
            "gq_matvec_swiglu", "gq_matvec_experts", "gq_matvec_batch", "gq_q8_0_split_repack",
-           "gq_matmul")
+           "gq_matmul", "gq_matmul_experts")
 
 _lib = None
 
@@ -77,6 +77,8 @@ def load_library():
     lib.gq_q8_0_split_repack.restype = i32
     lib.gq_matvec_experts.argtypes = [i32, vp, i64, i64, i64, vp, i64, vp, i64, vp, vp]
     lib.gq_matvec_experts.restype = i32
+    lib.gq_matmul_experts.argtypes = [i32, vp, i64, i64, i64, vp, ctypes.POINTER(i64), vp, vp]
+    lib.gq_matmul_experts.restype = i32
     for name in ("gq_matmul", "gq_matvec_batch"):
         getattr(lib, name).argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
         getattr(lib, name).restype = i32
@@ -248,3 +250,30 @@ def gq_matvec_batch(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):
     """Y[b] = W @ X[b] for every row b of X, each row bit-identical to
     gq_matvec of that row, asynchronous."""
     return _rows_product("gq_matvec_batch", fmt, W, rows, cols, X, Y, stream)
+
+
+def gq_matmul_experts(fmt: int, W, n_expert: int, rows: int, cols: int, X, m_per_expert,
+                      Y=None, stream=None):
+    """Y = the per-expert products of activation rows bucketed by expert:
+    X [sum(m_per_expert), cols] holds expert 0's rows first, then expert 1's,
+    ...; m_per_expert is a host sequence of n_expert counts. Asynchronous."""
+    torch = _torch()
+    counts = [int(m) for m in m_per_expert]
+    if len(counts) != n_expert:
+        raise ValueError("m_per_expert must hold n_expert counts")
+    total = sum(counts)
+    _check_w(fmt, W, n_expert * rows, cols)
+    _check_dev(X, "X", torch.float32)
+    if X.numel() < total * cols:
+        raise ValueError("X is too small")
+    if Y is None:
+        Y = torch.empty((total, rows), dtype=torch.float32, device=W.device)
+    _check_dev(Y, "Y", torch.float32)
+    if Y.numel() < total * rows:
+        raise ValueError("Y is too small")
+    arr = (ctypes.c_int64 * max(1, n_expert))(*counts)
+    st = load_library().gq_matmul_experts(int(fmt), _ptr(W), int(n_expert), int(rows), int(cols),
+                                          _ptr(X), arr, _ptr(Y), _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_matmul_experts")
+    return Y

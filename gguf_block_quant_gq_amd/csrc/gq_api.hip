@@ -257,22 +257,11 @@ extern "C" int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, v
                                              orb, (hipStream_t)stream));
 }
 
-extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,
-                         int64_t M, float* Y, void* stream) {
-  int64_t rb = 0, wbytes = 0;
-  int st = check_shape(fmt, rows, cols, M, &rb, &wbytes);
-  if (st != GQ_OK) return st;
-  if (M > 0 && (rows > INT64_MAX / 4 / M || cols > INT64_MAX / 4 / M)) return GQ_ERR_SHAPE;
-  if (rows == 0 || M == 0) return GQ_OK;
-  if (!W || !X || !Y) return GQ_ERR_NULL;
-  if ((st = check_align(fmt, W)) != GQ_OK) return st;
-  if ((uintptr_t)X % 4 || (uintptr_t)Y % 4) return GQ_ERR_ALIGN;
-  if (overlaps(Y, M * rows * 4, W, wbytes) || overlaps(Y, M * rows * 4, X, M * cols * 4))
-    return GQ_ERR_OVERLAP;
+namespace {
 
-  const int cus = current_cus();
-  if (cus <= 0) return GQ_ERR_DEVICE;
-  (void)hipGetLastError();
+// gq_matmul after its checks: the kernel route for M activation rows.
+int matmul_route(int fmt, const void* W, int64_t rb, int64_t rows, int64_t cols, const float* X,
+                 int64_t M, float* Y, void* stream, int cus) {
   // One activation row is the matvec (same rounding, its kernel). A few rows
   // over a small enough product run as the batched matvec, so each row again
   // rounds exactly as the matvec does (its cost grows with M * rows * cols:
@@ -291,4 +280,66 @@ extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, con
   if (M >= f32_matrix_core_min_m(fmt))
     return finish(gq::launch_gemm_f32(fmt, a, cus, (hipStream_t)stream));
   return finish(gq::launch_gemm_small(fmt, a, cus, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,
+                         int64_t M, float* Y, void* stream) {
+  int64_t rb = 0, wbytes = 0;
+  int st = check_shape(fmt, rows, cols, M, &rb, &wbytes);
+  if (st != GQ_OK) return st;
+  if (M > 0 && (rows > INT64_MAX / 4 / M || cols > INT64_MAX / 4 / M)) return GQ_ERR_SHAPE;
+  if (rows == 0 || M == 0) return GQ_OK;
+  if (!W || !X || !Y) return GQ_ERR_NULL;
+  if ((st = check_align(fmt, W)) != GQ_OK) return st;
+  if ((uintptr_t)X % 4 || (uintptr_t)Y % 4) return GQ_ERR_ALIGN;
+  if (overlaps(Y, M * rows * 4, W, wbytes) || overlaps(Y, M * rows * 4, X, M * cols * 4))
+    return GQ_ERR_OVERLAP;
+
+  const int cus = current_cus();
+  if (cus <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  return matmul_route(fmt, W, rb, rows, cols, X, M, Y, stream, cus);
+}
+
+extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64_t rows,
+                                 int64_t cols, const float* X, const int64_t* m_per_expert,
+                                 float* Y, void* stream) {
+  int64_t rb = 0, ebytes = 0;
+  int st = check_shape(fmt, rows, cols, 1, &rb, &ebytes);
+  if (st != GQ_OK) return st;
+  if (n_expert < 0 || n_expert > INT_MAX) return GQ_ERR_SHAPE;
+  if (n_expert == 0 || rows == 0) return GQ_OK;
+  if (!m_per_expert) return GQ_ERR_NULL;
+  // total activation rows, with every count checked before any launch
+  int64_t total = 0;
+  for (int64_t e = 0; e < n_expert; ++e) {
+    const int64_t m = m_per_expert[e];
+    if (m < 0 || m > INT_MAX || total > INT64_MAX - m) return GQ_ERR_SHAPE;
+    total += m;
+  }
+  if (total == 0) return GQ_OK;
+  if (ebytes > INT64_MAX / n_expert) return GQ_ERR_SHAPE;
+  if (rows > INT64_MAX / 4 / total || cols > INT64_MAX / 4 / total) return GQ_ERR_SHAPE;
+  const int64_t wbytes = ebytes * n_expert, xbytes = total * cols * 4, ybytes = total * rows * 4;
+  if (!W || !X || !Y) return GQ_ERR_NULL;
+  if ((st = check_align(fmt, W)) != GQ_OK) return st;
+  if ((uintptr_t)X % 4 || (uintptr_t)Y % 4) return GQ_ERR_ALIGN;
+  if (overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, X, xbytes)) return GQ_ERR_OVERLAP;
+
+  const int cus = current_cus();
+  if (cus <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  // one gq_matmul per expert with rows, in expert order on the caller's stream
+  int64_t m0 = 0;
+  for (int64_t e = 0; e < n_expert; ++e) {
+    const int64_t m = m_per_expert[e];
+    if (m == 0) continue;
+    st = matmul_route(fmt, (const uint8_t*)W + e * ebytes, rb, rows, cols, X + m0 * cols, m,
+                      Y + m0 * rows, stream, cus);
+    if (st != GQ_OK) return st;
+    m0 += m;
+  }
+  return GQ_OK;
 }

@@ -50,6 +50,15 @@ hipError_t device_pool(hipMemPool_t* out) {
 }  // namespace
 
 hipError_t ws_alloc(size_t bytes, hipStream_t s, void** p) {
+  // Requests are rounded up to a power of two (at least 1 MiB): measured on
+  // MI355X, consecutive requests of different sizes (prompt chunks of
+  // different lengths, the groups of gq_matmul_experts) were not served
+  // from the pool's freed blocks and cost hundreds of microseconds each
+  // (eight Q4_K products of 50..230 rows: 2.8 ms, against 0.69 ms rounded).
+  size_t b = (size_t)1 << 20;
+  while (b < bytes && b <= (SIZE_MAX >> 1)) b <<= 1;
+  if (b < bytes) return hipErrorOutOfMemory;
+  bytes = b;
   hipMemPool_t pool;
   hipError_t e = device_pool(&pool);
   if (e != hipSuccess) return e;

@@ -54,7 +54,8 @@
  *   device, created on first use, memory kept until the process ends):
  *   Q4_K 17472 * ceil(M/16) * ceil(cols/256) bytes of prepared activations,
  *   and for every format 4 * M * rows bytes per split when the K range is
- *   split over workgroups. It is allocated and released on the caller's stream, so the
+ *   split over workgroups, each request rounded up to a power of two (at
+ *   least 1 MiB) so that calls of different sizes reuse the pool's blocks. It is allocated and released on the caller's stream, so the
  *   call stays asynchronous and calls on different streams never share it;
  *   an allocation failure returns GQ_ERR_DEVICE. Global state: that pool and
  *   a per-device cache of device properties, each filled once. Calls on
@@ -232,6 +233,29 @@ int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out, v
  */
 int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
               const float* X, int64_t M, float* Y, void* stream);
+
+/*
+ * Grouped product for the prefill of a mixture-of-experts layer: activation
+ * rows already bucketed by expert (the Loom porting skill, "Beyond the
+ * starter": tokens bucketed by expert, then one grouped GEMM per expert for
+ * prefill; per-assignment matvecs serve decode, gq_matvec_experts). W holds
+ * the n_expert matrices back to back as in gq_matvec_experts (expert e's
+ * rows start at byte e * rows * gq_row_bytes(fmt, cols)). m_per_expert is a
+ * HOST array of n_expert row counts; X is [sum m_e, cols] with expert 0's
+ * m_0 rows first, then expert 1's, ...; Y is [sum m_e, rows] in the same
+ * order, overwritten:
+ *   Y[(o_e + i)*rows + r] = sum_c w_e(r, c) * X[(o_e + i)*cols + c],
+ *   o_e = m_0 + ... + m_{e-1}, i < m_e.
+ * Each expert's block is exactly gq_matmul of that expert's matrix and rows
+ * (same kernels, same bits): the batched matvec for small groups, the
+ * matrix cores for large ones, with gq_matmul's workspace per group.
+ * Experts with no rows are skipped. All counts are checked (>= 0, sums
+ * without overflow) before the first launch; n_expert == 0, rows == 0 or no
+ * rows at all is a no-op. Asynchronous on `stream` (the counts are read
+ * during the call and not kept).
+ */
+int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, int64_t cols,
+                      const float* X, const int64_t* m_per_expert, float* Y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -152,6 +152,33 @@ def test_validation_batch(lib):
     assert _mb(lib, Y=W_OK + 4 * 144 - 4) == gq.GQ_ERR_OVERLAP
 
 
+def _mge(lib, counts=(2, 0, 3), fmt=12, W=W_OK, rows=4, cols=256, X=X_OK, Y=Y_OK, n_expert=None):
+    import ctypes
+    arr = (ctypes.c_int64 * max(1, len(counts)))(*counts) if counts is not None else None
+    n = n_expert if n_expert is not None else len(counts)
+    return lib.gq_matmul_experts(fmt, W, n, rows, cols, X, arr, Y, None)
+
+
+def test_validation_grouped_experts(lib):
+    for bad in (0, 7, 15):
+        assert _mge(lib, fmt=bad) == gq.GQ_ERR_FMT
+    assert _mge(lib, n_expert=-1) == gq.GQ_ERR_SHAPE
+    assert _mge(lib, cols=0) == gq.GQ_ERR_SHAPE
+    assert _mge(lib, counts=(2, -1, 3)) == gq.GQ_ERR_SHAPE        # every count checked first
+    assert _mge(lib, counts=(1 << 62, 1 << 62)) == gq.GQ_ERR_SHAPE
+    assert _mge(lib, counts=None, n_expert=3) == gq.GQ_ERR_NULL
+    assert _mge(lib, counts=(), W=None, X=None, Y=None) == gq.GQ_OK   # no experts
+    assert _mge(lib, counts=(0, 0), W=None, X=None, Y=None) == gq.GQ_OK  # no rows
+    assert _mge(lib, rows=0, W=None) == gq.GQ_OK
+    assert _mge(lib, X=None) == gq.GQ_ERR_NULL
+    assert _mge(lib, Y=None) == gq.GQ_ERR_NULL
+    assert _mge(lib, W=W_OK + 2) == gq.GQ_ERR_ALIGN
+    assert _mge(lib, X=X_OK + 2) == gq.GQ_ERR_ALIGN
+    # Y is [5, rows]: overlapping X's last row, or the last expert's weights
+    assert _mge(lib, Y=X_OK + 4 * 256 * 4) == gq.GQ_ERR_OVERLAP
+    assert _mge(lib, Y=W_OK + 3 * 4 * 144 - 4) == gq.GQ_ERR_OVERLAP
+
+
 def _mx(lib, fmt=12, W=W_OK, n_expert=4, rows=4, cols=256, X=X_OK, xk=2, expid=0x40000,
         n_assign=8, Y=Y_OK):
     return lib.gq_matvec_experts(fmt, W, n_expert, rows, cols, X, xk, expid, n_assign, Y, None)

@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import assert_within_tolerance, oracle_threads, to_dev, to_host
+from helpers import (assert_pad_untouched, assert_within_tolerance, oracle_threads,
+                     sentinel_buffer, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,3 +74,40 @@ def test_invalid_ids_and_empty(gq, oracle):
     gq.gq_matvec_experts(fmt, Wd, n_expert, rows, cols, Xd, 2,
                          torch.empty(0, dtype=torch.int32, device="cuda"), Y=Y0)
     assert (to_host(Y0) == 7.0).all()
+
+
+# (fmt, rows, cols, rows per expert): groups that take the matvec (1), the
+# batched matvec (3, 5), and the matrix cores (17 and up), with empty experts
+GROUPED = [
+    (12, 512, 2048, [0, 1, 3, 17, 40, 70, 5, 120]),
+    (14, 256, 768, [33, 0, 2, 64]),          # Q6_K: fp32 matrix cores for the large groups
+    (8, 300, 896, [9, 16, 0, 1]),            # Q8_0: few-row kernel / fp32 matrix cores
+    (12, 64, 300, [0, 0, 7]),                # ragged rows, one expert with all the rows
+]
+
+
+@pytest.mark.parametrize("fmt,rows,cols,counts", GROUPED)
+def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
+    """Each expert's block of gq_matmul_experts equals gq_matmul of that
+    expert's matrix and rows bit for bit, and the oracle within tolerance."""
+    n_expert, total = len(counts), sum(counts)
+    rng = synth.rng_for(962, fmt * 1000 + rows)
+    W = synth.weights(fmt, n_expert * rows, cols, rng)
+    X = synth.activations((total, cols), rng)
+    print(f"[grouped] fmt={fmt} rows={rows} cols={cols} counts={counts}", flush=True)
+    Wd, Xd = to_dev(W), to_dev(X)
+    Y = sentinel_buffer(total * rows)
+    gq.gq_matmul_experts(fmt, Wd, n_expert, rows, cols, Xd, counts, Y=Y[:total * rows])
+    assert_pad_untouched(Y, total * rows)
+    got = to_host(Y)[:total * rows].reshape(total, rows)
+    rb = gq.gq_row_bytes(fmt, cols)
+    o = 0
+    for e, m in enumerate(counts):
+        if m == 0:
+            continue
+        We = W[e * rows * rb:(e + 1) * rows * rb]
+        ref, S = oracle.matmul(fmt, We, rows, cols, X[o:o + m], nthreads=oracle_threads())
+        assert_within_tolerance(got[o:o + m], ref, S, f"expert {e}")
+        one = to_host(gq.gq_matmul(fmt, Wd[e * rows * rb:(e + 1) * rows * rb], rows, cols, Xd[o:o + m]))
+        assert np.array_equal(one.view(np.uint32), got[o:o + m].view(np.uint32)), e
+        o += m
