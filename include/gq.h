@@ -252,7 +252,9 @@ int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
  * Experts with no rows are skipped. All counts are checked (>= 0, sums
  * without overflow) before the first launch; n_expert == 0, rows == 0 or no
  * rows at all is a no-op. Asynchronous on `stream` (the counts are read
- * during the call and not kept).
+ * during the call and not kept). The groups are enqueued in expert order;
+ * if a launch fails (GQ_ERR_DEVICE) the groups before it have been enqueued
+ * and Y's later blocks are unspecified.
  */
 int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, int64_t cols,
                       const float* X, const int64_t* m_per_expert, float* Y, void* stream);
