@@ -109,21 +109,24 @@ def traffic_probe(torch, gq, lib, mats, stream_ptr):
                       / len(dominant_launches(mats))}), flush=True)
 
 
-def prefill_probe(torch, gq, lib, synth, stream_ptr):
-    """One call of each prefill product at M = 512 (after one warm-up call):
-    Q4_K gate and down on the fp16 matrix cores, Q6_K down and Q5_K gate on
-    the fp32 matrix cores; for rocprofv3 --pmc runs (MFMA busy cycles and
-    executed matrix ops per dispatch)."""
-    M = 512
+def prefill_probe(torch, gq, lib, synth, stream_ptr, ms=(512,)):
+    """One call of each prefill product per M (after one warm-up call):
+    Q4_K gate and down on the fp16 matrix cores and, at M = 512, Q6_K down
+    and Q5_K gate on the fp32 matrix cores; for rocprofv3 --pmc runs (MFMA
+    busy cycles, executed matrix ops, waits and cache requests per
+    dispatch)."""
     cases = []
-    for which in ("gate", "down"):
-        W, X, rows, cols = synth.prefill_inputs(which, M)
-        cases.append((f"q4_k_{which}", 12, W, X, rows, cols))
-    for i in (1, 3):
-        name, f, r, c, W, _ = synth.mixed_format_weight_and_x(i)
-        cases.append((name, f, W, synth.activations((M, c), synth.rng_for(911, M)), r, c))
+    for M in ms:
+        for which in ("gate", "down"):
+            W, X, rows, cols = synth.prefill_inputs(which, M)
+            cases.append((f"q4_k_{which}_M{M}", 12, W, X, rows, cols))
+        if M == 512:
+            for i in (1, 3):
+                name, f, r, c, W, _ = synth.mixed_format_weight_and_x(i)
+                cases.append((name, f, W, synth.activations((M, c), synth.rng_for(911, M)), r, c))
     out = {}
     for name, f, W, X, rows, cols in cases:
+        M = X.shape[0]
         Wd, Xd = torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda()
         Yd = torch.empty((M, rows), dtype=torch.float32, device="cuda")
         for _ in range(2):
@@ -145,7 +148,9 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--prefill-probe", action="store_true",
-                    help="run each prefill product at M = 512 twice (for counter runs) and exit")
+                    help="run each prefill product twice (M from --prefill-probe-m; for counter runs) and exit")
+    ap.add_argument("--prefill-probe-m", default="512",
+                    help="activation rows for --prefill-probe, comma separated")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 256 MiB copy and one pass of the dominant kernel, then exit")
     args = ap.parse_args()
@@ -166,7 +171,8 @@ def main() -> int:
     stream_ptr = lambda: int(torch.cuda.current_stream().cuda_stream)  # noqa: E731
 
     if args.prefill_probe:
-        prefill_probe(torch, gq, lib, synth, stream_ptr)
+        prefill_probe(torch, gq, lib, synth, stream_ptr,
+                      tuple(int(m) for m in args.prefill_probe_m.split(",")))
         return 0
 
     # ------------------------------------------------ decode step workload
