@@ -543,7 +543,7 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
         del Wd
     log(f"mixed-format prefill: { {k: v for k, v in out.items() if k.startswith('matmul_llama3')} }")
 
-    # Q4_K products with a few (M = 4, 8) and many activation rows at the
+    # Q4_K products with a few (M = 2, 4, 8) and many activation rows at the
     # Llama-3-8B prefill shapes (matrix cores)
     for which in ("gate", "down"):
         for M in SMALL_M + synth.PREFILL_M:
