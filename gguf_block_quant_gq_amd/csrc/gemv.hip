@@ -60,6 +60,13 @@ constexpr int kThreads = 256;
 #ifndef GQ_GEMV_RB1_WAVES_PER_CU
 #define GQ_GEMV_RB1_WAVES_PER_CU 8
 #endif
+// Q8_0 units (packed and split layouts) take one row per group up to
+// 12 waves' worth of rows per CU: measured on MI355X, Q8_0 4096 x 4096
+// 6.24 -> 5.55 us and 4096 x 14336 15.21 -> 14.57 us against the threshold
+// of 8; the Q4_K projections of the same shapes are faster at 8.
+#ifndef GQ_GEMV_Q8_RB1_WAVES_PER_CU
+#define GQ_GEMV_Q8_RB1_WAVES_PER_CU 12
+#endif
 // Q5_K and Q6_K (more registers and ALU work per weight)
 #ifndef GQ_GEMV_K56_RBN
 #define GQ_GEMV_K56_RBN GQ_GEMV_RBN
@@ -478,7 +485,8 @@ hipError_t with_g(const GemvArgs& a, int cus, hipStream_t s, const ExpertArgs* e
   if constexpr (EPI == kEpiSwiglu) {
     return launch_one<F, G, 2, EPI>(a, cus, s, ex);
   } else {
-    const int64_t groups_needed = (int64_t)cus * GQ_GEMV_RB1_WAVES_PER_CU * (G >= 64 ? 1 : 64 / G);
+    constexpr int kWaves = is_q8<F>() ? GQ_GEMV_Q8_RB1_WAVES_PER_CU : GQ_GEMV_RB1_WAVES_PER_CU;
+    const int64_t groups_needed = (int64_t)cus * kWaves * (G >= 64 ? 1 : 64 / G);
     if ((int64_t)a.rows < 2 * groups_needed) return launch_one<F, G, 1, EPI>(a, cus, s, ex);
     // Q5_K / Q6_K on tall matrices (an lm_head, 14336-row projections): one
     // row per group at more workgroups per CU measured faster (more waves to
