@@ -92,9 +92,16 @@ def dominant_launches(mats):
     return [m for m in mats if m["cols"] == 4096 and m["rows"] >= 4096]
 
 
-def traffic_probe(torch, gq, lib, mats, stream_ptr):
-    """One plain device copy of 256 MiB (the counter calibration), then one
-    pass over the dominant kernel's launches; for rocprofv3 --pmc runs."""
+def traffic_probe(torch, gq, lib, synth, mats, stream_ptr):
+    """One plain device copy of 256 MiB (the counter calibration), one pass
+    over the dominant kernel's launches, then the Qwen2.5-0.5B Q8_0 lm_head
+    once packed and once in the split layout (cold: fresh copies, repacked
+    before the copy that flushes the caches); for rocprofv3 --pmc runs."""
+    fmt, rows, cols = synth.QWEN05_LM_HEAD
+    W, x = synth.matrix_and_x(fmt, rows, cols, 2, 0)
+    Wd, xd = torch.from_numpy(W).cuda(), torch.from_numpy(x).cuda()
+    Sd = gq.gq_q8_0_split_repack(Wd, rows, cols)
+    yd = torch.empty(rows, dtype=torch.float32, device="cuda")
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -104,9 +111,17 @@ def traffic_probe(torch, gq, lib, mats, stream_ptr):
     for m in dominant_launches(mats):
         lib.gq_matvec(*m["args"], sp)
     torch.cuda.synchronize()
+    for f, w in ((fmt, Wd), (gq.FMT_Q8_0_SPLIT, Sd)):
+        dst.copy_(src)  # evicts the lm_head from the caches
+        torch.cuda.synchronize()
+        assert lib.gq_matvec(f, w.data_ptr(), rows, cols, xd.data_ptr(), yd.data_ptr(), sp) == 0
+        torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": src.numel(),
                       "dominant_bytes_per_launch": sum(m["bytes"] for m in dominant_launches(mats))
-                      / len(dominant_launches(mats))}), flush=True)
+                      / len(dominant_launches(mats)),
+                      "lm_head_bytes": {"packed": gemv_bytes(gq.gq_row_bytes(fmt, cols), rows, cols),
+                                        "split": gemv_bytes(gq.gq_row_bytes(gq.FMT_Q8_0_SPLIT, cols),
+                                                            rows, cols)}}), flush=True)
 
 
 def prefill_probe(torch, gq, lib, synth, stream_ptr, ms=(512,)):
@@ -197,7 +212,7 @@ def main() -> int:
         f"{time.time() - t0:.1f}s")
 
     if args.traffic_probe:
-        traffic_probe(torch, gq, lib, mats, stream_ptr)
+        traffic_probe(torch, gq, lib, synth, mats, stream_ptr)
         return 0
 
     def step(subset=None):
