@@ -550,7 +550,7 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
                                    stream_ptr())
                 assert st == 0
 
-            ms = timer.time(mmf, 10 if M < 512 else 5, warmup=1)
+            ms = float(np.median([timer.time(mmf, 10 if M < 512 else 5, warmup=1) for _ in range(3)]))
             tf = 2.0 * M * r * c / (ms * 1e-3) / 1e12
             out[f"matmul_{name}_M{M}"] = dict(
                 us_per_call=round(ms * 1e3, 1), TFLOPs=round(tf, 2),
@@ -571,7 +571,9 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
                                    Yd.data_ptr(), stream_ptr())
                 assert st == 0
 
-            ms = timer.time(mm, 10 if M < 512 else 5, warmup=1)
+            # median of three timed loops (a single loop of these short
+            # calls is at the mercy of one slow launch)
+            ms = float(np.median([timer.time(mm, 10 if M < 512 else 5, warmup=1) for _ in range(3)]))
             flops = 2.0 * M * rows * cols
             wb = rows * gq.gq_row_bytes(12, cols) + 4 * M * (rows + cols)
             tf = flops / (ms * 1e-3) / 1e12
