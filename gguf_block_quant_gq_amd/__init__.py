@@ -60,8 +60,8 @@ def load_library():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                           "(or python gguf_block_quant_gq_amd/_build.py)")
+        raise RuntimeError(f"{LIB_PATH} is not built; run "
+                           "python gguf_block_quant_gq_amd/_build.py")
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     lib.gq_row_bytes.argtypes = [i32, i64]
