@@ -56,6 +56,12 @@
 #ifndef GQ_MM_WG_PER_CU
 #define GQ_MM_WG_PER_CU 2  // split-K target for the one-m-tile tiles (M <= 16)
 #endif
+#ifndef GQ_MM_TILE1_WR
+// weight row tiles per wave for one m-tile (M <= 16): 1 measured faster than
+// 2 on MI355X (Q4_K gate / down at M = 16: 32.5 / 28.7 us against 34.5 /
+// 32.2 us, interleaved A/B); at M = 32 and 64 two stay ahead
+#define GQ_MM_TILE1_WR 1
+#endif
 #ifndef GQ_MM_WG_PER_CU_WM
 #define GQ_MM_WG_PER_CU_WM 1  // split-K target for 2 and 4 m-tiles (16 < M <= 64)
 #endif
@@ -508,8 +514,8 @@ hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s) {
   const int mtiles = (a.M + 15) / 16;
 
   // tile shape by activation rows: WM m-tiles of 16, 64*WR weight rows
-  int WR = 2, WM = 1;
-  if (a.M > 16) WM = 2;
+  int WR = GQ_MM_TILE1_WR, WM = 1;
+  if (a.M > 16) WR = 2, WM = 2;
   if (a.M > 32) WM = 4;
   if (a.M > GQ_MM_BIG_M) {
     WR = GQ_MM_BIG_WR;
@@ -543,7 +549,7 @@ hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s) {
     if (big) e = launch_main<GQ_MM_BIG_WR, GQ_MM_BIG_WM>(m, gx, gy, s);
     else if (WM == 4) e = launch_main<2, 4>(m, gx, gy, s);
     else if (WM == 2) e = launch_main<2, 2>(m, gx, gy, s);
-    else e = launch_main<2, 1>(m, gx, gy, s);
+    else e = launch_main<GQ_MM_TILE1_WR, 1>(m, gx, gy, s);
   }
   if (e == hipSuccess && ks > 1) {
     const int64_t n = (int64_t)a.M * a.rows;
