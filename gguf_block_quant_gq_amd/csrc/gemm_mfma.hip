@@ -54,16 +54,16 @@
 #define GQ_MM_BIG_WM 4  // activation m-tiles per wave for the large tile
 #endif
 #ifndef GQ_MM_WG_PER_CU
-#define GQ_MM_WG_PER_CU 2  // split-K target for the one-m-tile tiles (M <= 16)
+// split-K target: workgroups per CU. One measured faster than two for every
+// tile (Q4_K gate / down, interleaved A/B: M = 16 34.9 / 32.1 -> 31.1 /
+// 30.0 us, M = 64 46.6 / 41.9 -> 39.2 / 36.9 us)
+#define GQ_MM_WG_PER_CU 1
 #endif
 #ifndef GQ_MM_TILE1_WR
 // weight row tiles per wave for one m-tile (M <= 16): 1 measured faster than
 // 2 on MI355X (Q4_K gate / down at M = 16: 32.5 / 28.7 us against 34.5 /
 // 32.2 us, interleaved A/B); at M = 32 and 64 two stay ahead
 #define GQ_MM_TILE1_WR 1
-#endif
-#ifndef GQ_MM_WG_PER_CU_WM
-#define GQ_MM_WG_PER_CU_WM 1  // split-K target for 2 and 4 m-tiles (16 < M <= 64)
 #endif
 
 namespace gq {
@@ -524,11 +524,9 @@ hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s) {
   const int gx = (a.rows + 64 * WR - 1) / (64 * WR);
   const int gy = (mtiles + WM - 1) / WM;
   // split the super-blocks until the grid covers the GPU (>= 2 super-blocks
-  // each). Fewer splits measured faster once a tile holds 2 or 4 m-tiles
-  // (Llama-3-8B gate / down at M = 64: 46.6 / 41.9 us with two workgroups
-  // per CU, 39.2 / 36.9 us with one); at M <= 16 two per CU stay ahead.
+  // each)
   const bool big = a.M > GQ_MM_BIG_M;
-  const int64_t target = (int64_t)cus * (big ? 1 : WM > 1 ? GQ_MM_WG_PER_CU_WM : GQ_MM_WG_PER_CU);
+  const int64_t target = (int64_t)cus * GQ_MM_WG_PER_CU;
   int ks = 1;
   while ((int64_t)gx * gy * ks < target && nsb / (2 * ks) >= 2) ks *= 2;
 
