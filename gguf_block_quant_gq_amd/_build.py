@@ -29,8 +29,19 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _stale(src: str, obj: str) -> bool:
+    """True when obj is missing or older than src or any header under csrc/."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [src, *glob.glob(os.path.join(CSRC, "*.h")), os.path.join(ROOT, "include", "gq.h")]
+    return any(os.path.getmtime(d) > t for d in deps if os.path.exists(d))
+
+
+def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    if incremental and not _stale(src, obj):
+        return obj
     cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -44,11 +55,13 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every HIP source and link libgq.so. With incremental=True,
+    objects newer than their source and every header are reused."""
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, incremental), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
@@ -59,4 +72,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

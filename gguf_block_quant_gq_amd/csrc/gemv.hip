@@ -29,6 +29,7 @@
 // reduction folds the partials), re-shaped for 64-wide wavefronts.
 #include <type_traits>
 
+#include "gemv_common.h"
 #include "gq_device.h"
 #include "gq_internal.h"
 #include "gq_units.h"
@@ -133,12 +134,6 @@ __device__ __forceinline__ void load_rows(typename F::Raw (&raw)[RB], const Gemv
     }
     load_unit<F>(raw[i], a.W + (int64_t)row * a.row_bytes, unit_ld, ln);
   }
-}
-
-// silu(g) * u = g / (1 + e^-g) * u, in fp32 (e^-g overflows to inf for very
-// negative g, giving -0 * u).
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.f + expf(-g)) * u;
 }
 
 // Write the finished sums of output rows obase.. (v[i] for weight row i of
@@ -252,40 +247,6 @@ __device__ __forceinline__ void fetch_x(typename F::X& xr, const f32x4* xs, int 
   for (int k = 0; k < C; ++k) c[k] = xs[x_slot<F, G>(F::x_chunk(gl, k))];
   F::set_x(xr, c);
   F::finish_x(xr);
-}
-
-// Rows fit in one segment: x stays in registers for the whole kernel.
-// Kernel arguments: the plain form, or the expert-batched form with the
-// expert table appended.
-struct GemvExpertArgs {
-  GemvArgs g;
-  ExpertArgs e;
-};
-
-template <bool EXPERTS>
-using KernelArgs = typename std::conditional<EXPERTS, GemvExpertArgs, GemvArgs>::type;
-
-__device__ __forceinline__ GemvArgs base_args(const GemvArgs& a) { return a; }
-__device__ __forceinline__ GemvArgs base_args(const GemvExpertArgs& a) { return a.g; }
-
-// Expert-batched calls: point a (the workgroup's copy of the arguments) at
-// the expert, activation row and output row of assignment blockIdx.y. An
-// expert id outside [0, n_expert) reads no weights: the assignment's output
-// row is filled with NaN instead. Without an id table (the batched matvec)
-// every assignment uses W itself. Returns false when there is nothing more
-// to do.
-__device__ __forceinline__ bool bind_assignment(GemvArgs& a, const ExpertArgs& ex) {
-  const int as = blockIdx.y;
-  const int e = ex.expid ? ex.expid[as] : 0;
-  a.x += (int64_t)(as / ex.xk) * a.cols;
-  a.y += (int64_t)as * a.rows;
-  if (e < 0 || e >= ex.n_expert) {
-    for (int r = blockIdx.x * kThreads + threadIdx.x; r < a.rows; r += gridDim.x * kThreads)
-      a.y[r] = __builtin_nanf("");
-    return false;
-  }
-  a.W += (int64_t)e * ex.expert_bytes;
-  return true;
 }
 
 // Row groups wider than a wave (G > 64) would need a barrier per batch to add
@@ -580,6 +541,9 @@ hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi,
     return dispatch_split(a, cus, s, epi, ex);
   }
   // K-quants: four units per 256-weight super-block
+#ifndef GQ_Q4K_OFF
+  if (fmt == kFmtQ4_K && gemv_q4k_supports(a, cus, ex)) return launch_gemv_q4k(a, cus, s, epi, ex);
+#endif
   a.units = 4 * ((a.cols + 255) / 256);
   if (fmt == kFmtQ5_K) return dispatch<Q5KUnit>(a, cus, s, epi, ex);
   if (fmt == kFmtQ6_K) return dispatch<Q6KUnit>(a, cus, s, epi, ex);

@@ -189,6 +189,41 @@ __device__ __forceinline__ void q4k_scales(const Q4KScaleSel& s, uint32_t h1, ui
   }
 }
 
+// Lane constants for the scale fields of sub-blocks 2g and 2g + 1 (see
+// q4_scales).
+struct Q4Sel {
+  uint32_t sel;  // v_perm_b32 selector: bytes a, a + 1 of each source
+  uint32_t sh;   // 0 (g < 2) or 2 (g >= 2)
+  uint32_t mt;   // mask of the P bits kept
+  uint32_t mq;   // mask of the Q bits kept
+};
+
+__device__ __forceinline__ Q4Sel q4_sel(int g) {
+  const uint32_t a = 2u * (uint32_t)(g & 1);
+  Q4Sel s;
+  s.sel = a | ((a + 1) << 8) | ((a + 4) << 16) | ((a + 5) << 24);
+  s.sh = g < 2 ? 0u : 2u;
+  s.mt = g < 2 ? 0x3F3F3F3Fu : 0x30303030u;
+  s.mq = g < 2 ? 0u : 0x0F0F0F0Fu;
+  return s;
+}
+
+// The codes sc_2g, sc_2g+1, m_2g, m_2g+1 as the four bytes of one dword.
+// With h1, h2, h3 = scale bytes 0..3, 4..7, 8..11 and a = 2(g & 1):
+//   g < 2 : sc_j = s[j] & 63, m_j = s[j + 4] & 63 (j = a, a + 1), i.e.
+//           bytes a, a + 1 of h1 and of h2, masked to six bits;
+//   g >= 2: low four bits from bytes a, a + 1 of h3 (sc: low nibble, m: high
+//           nibble), top two bits from bits 6-7 of the same bytes of h1 (sc)
+//           and h2 (m).
+// P = [h1.a, h1.a+1, h2.a, h2.a+1] and Q = [h3.a, h3.a+1, (h3>>4).a, (h3>>4).a+1]
+// give both cases as (Q & mq) | ((P >> sh) & mt).
+__device__ __forceinline__ uint32_t q4_scales(const u32x4& h, const Q4Sel& s) {
+  const uint32_t p = __builtin_amdgcn_perm(h.z, h.y, s.sel);
+  const uint32_t q = __builtin_amdgcn_perm(h.w >> 4, h.w, s.sel);
+  const uint32_t t = (p >> s.sh) & s.mt;
+  return (q & s.mq) | t;
+}
+
 // The 32 codes of one 16-byte chunk as fp32 values code * 2^-9:
 // lo[l] = low nibble of byte l (sub-block 2g), hi[l] = high nibble (2g + 1).
 __device__ __forceinline__ void q4k_chunk_codes(u32x4 v, float lo[16], float hi[16]) {

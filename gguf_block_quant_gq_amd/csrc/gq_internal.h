@@ -73,6 +73,10 @@ hipError_t launch_q8_0_split_repack(const uint8_t* W, int64_t rows, int cols, in
 hipError_t launch_dequant(int fmt, DequantArgs a, hipStream_t s);
 hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi = kEpiStore,
                        const ExpertArgs* ex = nullptr);
+// The Q4_K matvec for rows of 33..256 units (gemv_q4k.hip): whether a call
+// fits it, and its launch (same epilogues and batched form as launch_gemv).
+bool gemv_q4k_supports(const GemvArgs& a, int cus, const ExpertArgs* ex);
+hipError_t launch_gemv_q4k(GemvArgs a, int cus, hipStream_t s, int epi, const ExpertArgs* ex);
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
 hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s);
 hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s);

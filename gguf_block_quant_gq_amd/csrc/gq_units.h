@@ -195,27 +195,17 @@ struct Q4KUnit {
     u32x4 q0, q1, h;
   };
   // Per-lane constants: the lane's group g is fixed (G is a multiple of 4),
-  // so the bit positions of its two scale and min codes are too.
+  // so the selectors and masks that gather its two scale and min codes are
+  // too (q4_scales).
   struct Lane {
     int g;
-    bool high;          // g >= 2: sub-blocks 4..7
-    uint32_t o_sc[2];   // bit offset of the low 4 bits of sc_j
-    uint32_t o_m[2];    // bit offset of the low 4 bits of m_j
-    uint32_t o_top[2];  // bit offset of the top 2 bits of sc_j (in s[0..3]) / m_j (in s[4..7])
+    Q4Sel sel;
   };
 
   __device__ static Lane lane(int gl) {
     Lane l;
     l.g = gl & 3;
-    l.high = l.g >= 2;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const uint32_t j = 2u * l.g + e;
-      const uint32_t i = j & 3u;
-      l.o_sc[e] = 8u * i;
-      l.o_m[e] = l.high ? 8u * i + 4u : 8u * i;
-      l.o_top[e] = l.high ? 8u * i + 6u : 8u * i + 4u;
-    }
+    l.sel = q4_sel(l.g);
     return l;
   }
 
@@ -290,21 +280,14 @@ struct Q4KUnit {
     raw.q0 = raw.q1 = raw.h = u32x4{0, 0, 0, 0};
   }
 
-  // sc_j = low 4 bits | top 2 bits << 4, both read with lane-constant
-  // offsets; only the register holding the low bits depends on the lane.
+  // sc_2g, sc_2g+1, m_2g, m_2g+1 gathered into one dword (q4_scales), one
+  // v_cvt_f32_ubyte each.
   __device__ static void scales(const Raw& raw, const Lane& ln, float sc[2], float m[2]) {
-    const uint32_t h1 = raw.h.y, h2 = raw.h.z, h3 = raw.h.w;
-    const uint32_t src_sc = ln.high ? h3 : h1;
-    const uint32_t src_m = ln.high ? h3 : h2;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const uint32_t s = __builtin_amdgcn_ubfe(src_sc, ln.o_sc[e], 4) |
-                         (__builtin_amdgcn_ubfe(h1, ln.o_top[e], 2) << 4);
-      const uint32_t mm = __builtin_amdgcn_ubfe(src_m, ln.o_m[e], 4) |
-                          (__builtin_amdgcn_ubfe(h2, ln.o_top[e], 2) << 4);
-      sc[e] = (float)s;
-      m[e] = (float)mm;
-    }
+    const uint32_t scm = q4_scales(raw.h, ln.sel);
+    sc[0] = (float)(scm & 0xFFu);
+    sc[1] = (float)((scm >> 8) & 0xFFu);
+    m[0] = (float)((scm >> 16) & 0xFFu);
+    m[1] = (float)(scm >> 24);
   }
 
   __device__ static float dot(const Raw& raw, const X& x, const Lane& ln) {
