@@ -4,21 +4,25 @@
 //
 // These formats scale every 16 or 32 weights, and scale * code needs up to
 // 18 significant bits (Q8_0 d*q), so no exact fp16 operand exists (the Q4_K
-// path in gemm_mfma.hip relies on sc*code <= 945). Here each k-chunk of the
+// path in gemm_q4k.hip relies on sc*code <= 945). Here each k-chunk of the
 // weight tile is dequantised exactly to fp32 in LDS (gq_quads.h, the same
 // values gq_dequant writes) and multiplied with fp32 activations by
 // v_mfma_f32_16x16x4f32, accumulating in fp32.
 //
-// A workgroup (4 waves) owns 64 weight rows x 16*WM activation rows and a
-// range of k-chunks (split over blockIdx.z when the tiles alone cannot fill
-// the GPU; the split partial products are added in split order afterwards).
-// Per chunk of 128 k: every thread decodes 8 quads of weights into the W
-// tile and stores its share of the X tile (both requested into registers
-// during the previous chunk); then wave w multiplies weight rows
-// 16w..16w+15 by all activation rows. Within each group of 16 k, lane
-// (i, q) = (lane & 15, lane >> 4) supplies k = 4q + s at MFMA step s for both
-// operands (the same permutation of k on both sides leaves the sum
-// unchanged), so each operand is one 16-byte LDS read per 16 k.
+// A workgroup of KS groups of RW waves owns 16 RW weight rows x 16 WM
+// activation rows; group g takes the k-chunks g, g + KS, ... and the groups'
+// products are added in group order at the end (deterministic; no memory
+// beyond the arguments). Per chunk of 128 k: every thread of a group decodes
+// 8 quads of weights into the group's W tile and stores its share of the X
+// tile (both requested into registers during the previous chunk); then wave
+// w of the group multiplies weight rows 16w..16w+15 by all activation rows.
+// Within each group of 16 k, lane (i, q) = (lane & 15, lane >> 4) supplies
+// k = 4q + s at MFMA step s for both operands (the same permutation of k on
+// both sides leaves the sum unchanged), so each operand is one 16-byte LDS
+// read per 16 k.
+//
+// Q4_K runs here only for rows whose length is not a multiple of 4 (the
+// fp16 matrix-core kernel reads activations four at a time).
 #include "gq_device.h"
 #include "gq_internal.h"
 #include "gq_quads.h"
@@ -27,35 +31,42 @@ namespace gq {
 
 namespace {
 
-constexpr int kKC = 128;        // k per chunk
-constexpr int kLD = kKC + 4;    // LDS row stride in floats (keeps 16-byte rows, spreads banks)
-constexpr int kRowsWG = 64;     // weight rows per workgroup
 
 struct F32Args {
   const uint8_t* W;
   const float* X;
-  float* out;            // Y, or the split partials
+  float* Y;
   int64_t row_bytes;
-  int64_t split_stride;  // floats between the partials of two splits
   int rows, cols, M;
-  int nchunk;            // k-chunks in a row
-  int per_split;         // k-chunks per split
-  int xvec;              // X rows are 16-byte aligned and cols % 4 == 0
+  int nchunk;  // k-chunks in a row (of the kernel's chunk size)
+  int xvec;    // X rows are 16-byte aligned and cols % 4 == 0
 };
 
-template <class Q, int WM>
-__global__ __launch_bounds__(256, 2) void gemm_f32_kernel(F32Args a) {
-  __shared__ __attribute__((aligned(16))) float Wl[kRowsWG * kLD];
-  __shared__ __attribute__((aligned(16))) float Xl[16 * WM * kLD];
+template <class Q, int WM, int RW, int KS, int PF, int KC>
+__global__ __launch_bounds__(64 * RW * KS) void gemm_f32_kernel(F32Args a) {
+  static_assert(PF == 1 || PF == 2, "prefetch depth");
+  static_assert(KC == 64 || KC == 128, "chunk");
+  constexpr int kLD = KC + 4;               // LDS row stride in floats (16-byte rows, banks spread)
+  constexpr int kQR = KC / 4;               // quads per tile row
+  constexpr int kGT = 64 * RW;              // threads per group
+  constexpr int kWQ = 16 * RW * kQR / kGT;  // W quads per thread and chunk
+  constexpr int kXQ = 16 * WM * kQR / kGT;  // X quads per thread and chunk
+  constexpr int kTile = (16 * RW + 16 * WM) * kLD;
+  static_assert(kXQ >= 1 && (16 * WM * kQR) % kGT == 0, "X share");
+  __shared__ __attribute__((aligned(16))) float lds[KS * kTile];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x % kGT;
+  const int grp = threadIdx.x / kGT;
   const int wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, q = lane >> 4;
-  const int r0 = blockIdx.x * kRowsWG;
+  const int r0 = blockIdx.x * 16 * RW;
   const int m0 = blockIdx.y * 16 * WM;
-  const int z = blockIdx.z;
-  const int c_begin = z * a.per_split;
-  const int c_end = min(a.nchunk, c_begin + a.per_split);
+  float* Wl = lds + grp * kTile;
+  float* Xl = Wl + 16 * RW * kLD;
+  // this group's chunks grp, grp + KS, ... (n of them); every group takes
+  // the workgroup's step count so that the barriers match
+  const int n = a.nchunk > grp ? (a.nchunk - grp + KS - 1) / KS : 0;
+  const int steps = (a.nchunk + KS - 1) / KS;
 
   f32x4 acc[WM];
 #pragma unroll
@@ -64,20 +75,22 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(F32Args a) {
   // The next chunk's raw weight bytes and activations are requested into
   // registers before the current chunk is multiplied, so their latency hides
   // behind the matrix-core work; they are decoded into LDS after it.
-  typename Q::Raw wr[8];
-  f32x4 xr[2 * WM];
-  auto fetch = [&](int c) {
-    const int k0 = c * kKC;
+  typename Q::Raw wr_[2][kWQ];
+  f32x4 xr_[2][kXQ];
+  auto fetch = [&](int c, int st) {
+    typename Q::Raw (&wr)[kWQ] = wr_[st];
+    f32x4 (&xr)[kXQ] = xr_[st];
+    const int k0 = c * KC;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {  // 64 rows x 128 k = 2048 quads, 32 threads per row
-      const int qd = tid + 256 * j;
-      const int row = r0 + (qd >> 5), k = k0 + 4 * (qd & 31);
+    for (int j = 0; j < kWQ; ++j) {  // 16 RW rows x KC k
+      const int qd = tid + kGT * j;
+      const int row = r0 + qd / kQR, k = k0 + 4 * (qd % kQR);
       if (row < a.rows && k < a.cols) Q::load(wr[j], a.W + (int64_t)row * a.row_bytes, k, a.cols);
     }
 #pragma unroll
-    for (int j = 0; j < 2 * WM; ++j) {  // 16*WM rows x 128 k, zero past M and cols
-      const int qd = tid + 256 * j;
-      const int m = m0 + (qd >> 5), k = k0 + 4 * (qd & 31);
+    for (int j = 0; j < kXQ; ++j) {  // 16*WM rows x KC k, zero past M and cols
+      const int qd = tid + kGT * j;
+      const int m = m0 + qd / kQR, k = k0 + 4 * (qd % kQR);
       f32x4 xv = {0.f, 0.f, 0.f, 0.f};
       if (m < a.M) {
         const float* xp = a.X + (int64_t)m * a.cols + k;
@@ -93,12 +106,14 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(F32Args a) {
       xr[j] = xv;
     }
   };
-  auto commit = [&](int c) {
-    const int k0 = c * kKC;
+  auto commit = [&](int c, int st) {
+    const typename Q::Raw (&wr)[kWQ] = wr_[st];
+    const f32x4 (&xr)[kXQ] = xr_[st];
+    const int k0 = c * KC;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int qd = tid + 256 * j;
-      const int rl = qd >> 5, kk = 4 * (qd & 31);
+    for (int j = 0; j < kWQ; ++j) {
+      const int qd = tid + kGT * j;
+      const int rl = qd / kQR, kk = 4 * (qd % kQR);
       const int row = r0 + rl, k = k0 + kk;
       float v[4] = {0.f, 0.f, 0.f, 0.f};
       if (row < a.rows && k < a.cols) {
@@ -110,19 +125,15 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(F32Args a) {
       *(f32x4*)&Wl[rl * kLD + kk] = f32x4{v[0], v[1], v[2], v[3]};
     }
 #pragma unroll
-    for (int j = 0; j < 2 * WM; ++j) {
-      const int qd = tid + 256 * j;
-      *(f32x4*)&Xl[(qd >> 5) * kLD + 4 * (qd & 31)] = xr[j];
+    for (int j = 0; j < kXQ; ++j) {
+      const int qd = tid + kGT * j;
+      *(f32x4*)&Xl[(qd / kQR) * kLD + 4 * (qd % kQR)] = xr[j];
     }
   };
 
-  if (c_begin < c_end) fetch(c_begin);
-  for (int c = c_begin; c < c_end; ++c) {
-    commit(c);
-    __syncthreads();
-    if (c + 1 < c_end) fetch(c + 1);
+  auto multiply = [&]() {
 #pragma unroll 4
-    for (int k16 = 0; k16 < kKC; k16 += 16) {
+    for (int k16 = 0; k16 < KC; k16 += 16) {
       const f32x4 wf = *(const f32x4*)&Wl[(16 * wave + i) * kLD + k16 + 4 * q];
       f32x4 xf[WM];
 #pragma unroll
@@ -135,75 +146,104 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(F32Args a) {
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[t].w, wf.w, acc[t], 0, 0, 0);
       }
     }
+  };
+  // step s: decode chunk s (its requests were made PF steps earlier) into
+  // the tiles, then request chunk s + PF into the freed registers, then
+  // multiply
+  auto step = [&](int s, int st) {
+    if (s < n) commit(grp + KS * s, st);
     __syncthreads();
+    if (s + PF < n) fetch(grp + KS * (s + PF), st);
+    if (s < n) multiply();
+    __syncthreads();
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < n) fetch(grp + KS * p, p);
+  for (int s = 0; s < steps; s += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (s + p < steps) step(s + p, p);
+  }
+
+  // groups 1.. park their sums in LDS (the tiles are free now); group 0 adds
+  // them in group order
+  if constexpr (KS > 1) {
+    f32x4* red = (f32x4*)lds;  // [KS - 1][RW][WM][64]
+    if (grp > 0) {
+#pragma unroll
+      for (int t = 0; t < WM; ++t) red[(((grp - 1) * RW + wave) * WM + t) * 64 + lane] = acc[t];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < KS; ++g)
+#pragma unroll
+      for (int t = 0; t < WM; ++t) {
+        const f32x4 o = red[(((g - 1) * RW + wave) * WM + t) * 64 + lane];
+        acc[t] = f32x4{acc[t].x + o.x, acc[t].y + o.y, acc[t].z + o.z, acc[t].w + o.w};
+      }
   }
 
   // D lane layout: column (weight row) i, activation rows 4q..4q+3
   const int r = r0 + 16 * wave + i;
   if (r >= a.rows) return;
-  float* out = a.out + (int64_t)z * a.split_stride;
 #pragma unroll
   for (int t = 0; t < WM; ++t) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = m0 + 16 * t + 4 * q + e;
-      if (m < a.M) out[(int64_t)m * a.rows + r] = acc[t][e];
+      if (m < a.M) a.Y[(int64_t)m * a.rows + r] = acc[t][e];
     }
   }
 }
 
-template <class Q, int WM>
-hipError_t launch(const F32Args& a, int gx, int gy, int ks, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_f32_kernel<Q, WM>), dim3(gx, gy, ks), dim3(256), 0, s, a);
+template <class Q, int WM, int RW, int KS, int PF, int KC>
+hipError_t launch(F32Args a, int gy, hipStream_t s) {
+  const int gx = (a.rows + 16 * RW - 1) / (16 * RW);
+  a.nchunk = (a.cols + KC - 1) / KC;
+  hipLaunchKernelGGL((gemm_f32_kernel<Q, WM, RW, KS, PF, KC>), dim3(gx, gy), dim3(64 * RW * KS), 0, s, a);
   return hipGetLastError();
 }
 
+// Tiles, measured on MI355X (Q6_K 4096 x 14336, Q5_K 14336 x 4096, Q8_0
+// 4096 x 14336): 64 weight rows per workgroup (four waves sharing the
+// tiles) when that grid gives two workgroups per CU, or about one per CU
+// with two or four m-tiles; otherwise 16 rows per workgroup with its waves
+// splitting k (each decoding its own 16-row tile): eight waves for one
+// m-tile (Q6_K M = 16: 58 us against 127 with four), six or eight with 64-k
+// chunks (so that their tiles fit the LDS) for four or two (Q6_K M = 64:
+// 158 us against 232 with four).
 template <class Q>
-hipError_t launch_wm(const F32Args& a, int WM, int gx, int gy, int ks, hipStream_t s) {
-  if (WM == 4) return launch<Q, 4>(a, gx, gy, ks, s);
-  if (WM == 2) return launch<Q, 2>(a, gx, gy, ks, s);
-  return launch<Q, 1>(a, gx, gy, ks, s);
+hipError_t launch_wm(const F32Args& a, int cus, hipStream_t s) {
+  const int mtiles = (a.M + 15) / 16;
+  const int WM = mtiles >= 4 ? 4 : mtiles >= 2 ? 2 : 1;
+  const int gy = (mtiles + WM - 1) / WM;
+  const int64_t grid = (int64_t)((a.rows + 63) / 64) * gy;
+  if (grid >= 2LL * cus || (WM > 1 && grid >= (int64_t)cus * 7 / 8)) {
+    if (WM == 4) return launch<Q, 4, 4, 1, 1, 128>(a, gy, s);
+    if (WM == 2) return launch<Q, 2, 4, 1, 1, 128>(a, gy, s);
+    return launch<Q, 1, 4, 1, 1, 128>(a, gy, s);
+  }
+  if (WM == 4) return launch<Q, 4, 1, 6, 1, 64>(a, gy, s);
+  if (WM == 2) return launch<Q, 2, 1, 8, 1, 64>(a, gy, s);
+  return launch<Q, 1, 1, 8, 1, 128>(a, mtiles, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s) {
-  if (fmt != kFmtQ8_0 && fmt != kFmtQ5_0 && fmt != kFmtQ5_K && fmt != kFmtQ6_K && fmt != kFmtQ8_0Split)
-    return hipErrorInvalidValue;
-  const int mtiles = (a.M + 15) / 16;
-  const int WM = mtiles >= 4 ? 4 : mtiles >= 2 ? 2 : 1;
-  const int gx = (a.rows + kRowsWG - 1) / kRowsWG;
-  const int gy = (mtiles + WM - 1) / WM;
-  const int nchunk = (a.cols + kKC - 1) / kKC;
-  // split the k-chunks until two workgroups per CU are busy (>= 2 chunks each)
-  int ks = 1;
-  while ((int64_t)gx * gy * ks < 2LL * cus && nchunk / (2 * ks) >= 2) ks *= 2;
-  const int per_split = (nchunk + ks - 1) / ks;
-  ks = (nchunk + per_split - 1) / per_split;
-
-  void* ws = nullptr;
-  const int64_t n = (int64_t)a.M * a.rows;
-  if (ks > 1) {
-    const hipError_t e = ws_alloc((size_t)ks * n * sizeof(float), s, &ws);
-    if (e != hipSuccess) return e;
-  }
   const int xvec = (a.cols % 4 == 0) && (((uintptr_t)a.X & 15) == 0);
-  const F32Args fa{a.W, a.X, ks > 1 ? (float*)ws : a.Y, a.row_bytes, n,
-                   a.rows, a.cols, a.M, nchunk, per_split, xvec};
-  hipError_t e;
+  const F32Args fa{a.W, a.X, a.Y, a.row_bytes, a.rows, a.cols, a.M, 0, xvec};
   switch (fmt) {
-    case kFmtQ8_0: e = launch_wm<Q8Quad>(fa, WM, gx, gy, ks, s); break;
-    case kFmtQ5_0: e = launch_wm<Q5_0Quad>(fa, WM, gx, gy, ks, s); break;
-    case kFmtQ5_K: e = launch_wm<Q5KQuad>(fa, WM, gx, gy, ks, s); break;
-    case kFmtQ8_0Split: e = launch_wm<Q8SplitQuad>(fa, WM, gx, gy, ks, s); break;
-    default: e = launch_wm<Q6KQuad>(fa, WM, gx, gy, ks, s); break;
+    case kFmtQ8_0: return launch_wm<Q8Quad>(fa, cus, s);
+    case kFmtQ5_0: return launch_wm<Q5_0Quad>(fa, cus, s);
+    case kFmtQ4_K: return launch_wm<Q4KQuad>(fa, cus, s);
+    case kFmtQ5_K: return launch_wm<Q5KQuad>(fa, cus, s);
+    case kFmtQ6_K: return launch_wm<Q6KQuad>(fa, cus, s);
+    case kFmtQ8_0Split: return launch_wm<Q8SplitQuad>(fa, cus, s);
+    default: return hipErrorInvalidValue;
   }
-  if (ks > 1) {
-    if (e == hipSuccess) e = launch_split_sum((const float*)ws, a.Y, n, ks, s);
-    const hipError_t ef = ws_free(ws, s);
-    if (e == hipSuccess) e = ef;
-  }
-  return e;
 }
 
 }  // namespace gq

@@ -1,0 +1,755 @@
+// gemm_q4k.hip -- Y = X W^T for Q4_K weights and two or more activation rows,
+// on the gfx950 matrix cores (v_mfma_f32_16x16x32_f16). One launch; the
+// kernel uses no memory beyond its arguments.
+//
+// The prompt-chunk product ("nurllama 0.18.1 API", model.nu section: the
+// matmuls run over a chunk of positions at once, each weight read once per
+// chunk) is a real dense contraction once M >= 16.
+//
+// Exact operands. A Q4_K super-block contributes, per output,
+//   d * sum_j sc_j * sum_{c in j} code_c * x_c  -  dmin * sum_j m_j * X_j
+// with X_j the sum of x over sub-block j:
+//   * the weight operand is sc_j * code_c, an integer <= 945, exact in fp16;
+//   * the 256 x of one activation row and super-block are scaled by 2^e so
+//     that the largest magnitude lies in [2^9, 2^10), and split into fp16
+//     parts hi = fp16(x 2^e) and lo = fp16(x 2^e - hi) (v_fma_mix: one
+//     rounding each), so x 2^e = hi + lo to about 2^-22 relative; both parts
+//     are multiplied, so the products are exact and the sums are fp32;
+//   * the min term is one more product per super-block: each lane's partial
+//     sums of x over its 8 columns of every sub-block (hi and lo parts, side
+//     by side along k) against m_j repeated for every lane;
+//   * d, dmin and 2^-e are applied per super-block in fp32.
+// The fp16 parts keep this accuracy for every activation whose magnitude is
+// at least 2^-14 of the largest one in its row and super-block (and for any
+// row whose largest magnitude lies in [2^-117, 2^126)); smaller ones reach
+// the fp16 subnormal range and are represented only to an absolute 2^-34 of
+// that largest magnitude.
+//
+// Decomposition. A workgroup of four waves owns 16 WR weight rows and 16 WM
+// activation rows; its waves take the super-blocks in turn (wave w: w, w + 4,
+// ...) and each builds its own operands in registers:
+//   * the weight rows' bytes arrive by buffer loads -- lane (i, q) reads the
+//     header and bytes 8q..8q+7 of each 32-byte code group of its row i, which
+//     is exactly the k range its operand needs -- and become sc * code with
+//     one v_perm_b32 (code under the exponent of 1024) and one packed fp16
+//     fma per code pair;
+//   * lane (i, q) reads columns 8q..8q+7 of every sub-block of activation row
+//     i, takes the row's largest magnitude with two lane exchanges, and
+//     splits its values into the hi and lo operands.
+// The four waves' products are added in LDS in wave order (deterministic).
+#include "gq_device.h"
+#include "gq_internal.h"
+
+namespace gq {
+
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+
+__device__ __forceinline__ h8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(h8, v);
+}
+
+// Codes of 8 consecutive bytes (w0 = bytes 0-3, w1 = bytes 4-7), low (H = 0)
+// or high (H = 1) nibbles, as the fp16 values sc * code in byte order:
+// v_perm_b32 puts each code byte under the exponent byte 0x64 of 1024, and
+// fma((1024 + c), sc, -1024 sc) = c * sc is exact (one rounding of an exactly
+// representable value).
+template <int H>
+__device__ __forceinline__ h8 weight_operand(uint32_t w0, uint32_t w1, h2 sc, h2 nsc) {
+  constexpr uint32_t kMagic = 0x64646464u;
+  const uint32_t n0 = (H ? w0 >> 4 : w0) & 0x0F0F0F0Fu;
+  const uint32_t n1 = (H ? w1 >> 4 : w1) & 0x0F0F0F0Fu;
+  // selector bytes 0..3 take bytes of the second source, 4..7 of the first
+  uint32_t p[4];
+  p[0] = __builtin_amdgcn_perm(kMagic, n0, 0x04010400u);  // codes 0, 1
+  p[1] = __builtin_amdgcn_perm(kMagic, n0, 0x04030402u);  // codes 2, 3
+  p[2] = __builtin_amdgcn_perm(kMagic, n1, 0x04010400u);  // codes 4, 5
+  p[3] = __builtin_amdgcn_perm(kMagic, n1, 0x04030402u);  // codes 6, 7
+  uint32_t r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    r[k] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(h2, p[k]), sc, nsc));
+  return as_h8(r[0], r[1], r[2], r[3]);
+}
+
+// Two six-bit fields (bits 0-5 and 16-21) as an exact fp16 pair.
+__device__ __forceinline__ h2 pair_f16(uint32_t two_fields) {
+  const h2 v = __builtin_bit_cast(h2, two_fields | 0x64006400u);
+  const h2 k = {(_Float16)1024.f, (_Float16)1024.f};
+  return v - k;
+}
+
+// The header of one row's super-block, decoded for the operands: the eight
+// scale codes as fp16 (sc) and times -1024 (nsc), the min-term operand
+// (m_0..m_7), d and dmin.
+struct RowHead {
+  float d, dmin;
+  h8 sc, nsc, mop;
+};
+
+__device__ __forceinline__ RowHead decode_head(u32x4 hd) {
+  RowHead h;
+  h.d = half_bits_to_float(hd.x & 0xFFFFu);
+  h.dmin = half_bits_to_float(hd.x >> 16);
+  // pairs (field j, field j + 2) from the 12 scale bytes s[0..11]:
+  // j < 4: sc = s[j] & 63, m = s[j + 4] & 63; j >= 4: low 4 bits from s[j + 4],
+  // top 2 bits from bits 6-7 of s[j - 4] (sc) or s[j] (m)
+  constexpr uint32_t L6 = 0x003F003Fu, L4 = 0x000F000Fu, H2 = 0x00300030u;
+  const h2 s02 = pair_f16(hd.y & L6), s13 = pair_f16((hd.y >> 8) & L6);
+  const h2 s46 = pair_f16((hd.w & L4) | ((hd.y >> 2) & H2));
+  const h2 s57 = pair_f16(((hd.w >> 8) & L4) | ((hd.y >> 10) & H2));
+  const h2 m02 = pair_f16(hd.z & L6), m13 = pair_f16((hd.z >> 8) & L6);
+  const h2 m46 = pair_f16(((hd.w >> 4) & L4) | ((hd.z >> 2) & H2));
+  const h2 m57 = pair_f16(((hd.w >> 12) & L4) | ((hd.z >> 10) & H2));
+  h.sc = h8{s02[0], s13[0], s02[1], s13[1], s46[0], s57[0], s46[1], s57[1]};
+  const _Float16 k = (_Float16)-1024.f;
+  h.nsc = h.sc * h8{k, k, k, k, k, k, k, k};
+  h.mop = h8{m02[0], m13[0], m02[1], m13[1], m46[0], m57[0], m46[1], m57[1]};
+  return h;
+}
+
+// fp16 parts of a * s and b * s: hi = fp16(v), lo = fp16(v - hi), each one
+// rounding of the exact value (v_fma_mix), packed (a in the low half).
+__device__ __forceinline__ void split2(float a, float b, float s, uint32_t& hi, uint32_t& lo) {
+  __asm__("v_fma_mixlo_f16 %0, %2, %4, 0\n\t"
+          "v_fma_mixhi_f16 %0, %3, %4, 0\n\t"
+          "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[0,0,1]\n\t"
+          "v_fma_mixhi_f16 %1, %3, %4, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+          : "=&v"(hi), "=&v"(lo)
+          : "v"(a), "v"(b), "v"(s));
+}
+
+__device__ __forceinline__ float lane_xor(float v, int mask) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+      (int)(((threadIdx.x & 63) ^ mask) << 2), __builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ float lane_read(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ u32x4 buf_b128(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+}
+
+__device__ __forceinline__ u32x2 buf_b64(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0));
+}
+
+__device__ __forceinline__ float buf_b32f(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+}
+
+// One product (or one group of a grouped product): W rows, X rows, Y rows.
+struct MmTile {
+  int64_t w_off;   // byte offset of the group's weight tensor from W
+  int m_begin;     // first activation row of the group (in X and Y)
+  int m_count;     // activation rows in the group
+  int mtile0;      // first blockIdx.y of the group
+};
+
+constexpr int kMaxGroups = 64;
+
+struct MmArgs {
+  const uint8_t* W;
+  const float* X;
+  float* Y;
+  int64_t row_bytes;
+  int rows, cols, nsb;
+  int n_groups;
+  MmTile g[kMaxGroups];
+};
+
+// The weight bytes a wave needs for one super-block (its rows' headers and
+// code bytes); the activation tile goes to LDS.
+template <int WR>
+struct Stage {
+  u32x4 hd[WR];
+  u32x2 cw[WR][4];
+};
+
+// An activation tile (16 rows x the 256 columns of one super-block) in LDS:
+// row r at r * kXRow bytes. The 16-byte pad makes the lane reads of the
+// operand layout (16 rows at the same column) hit 16 different bank groups.
+constexpr int kXRow = 1024 + 16;
+constexpr int kXTile = 16 * kXRow;
+
+// KW waves per workgroup take the super-blocks in turn; each keeps the next
+// super-block's bytes in flight (two stages) while it multiplies the current
+// one. The activation tile is moved by direct global-to-LDS loads, one row
+// (1 KB, contiguous) per wave instruction: reading the operand layout
+// straight from memory would make every instruction touch 16 rows whose
+// stride (cols * 4 bytes, a multiple of 4 KB for 4096 or 14336 columns)
+// maps them all to one L2 channel.
+template <int WR, int KW>
+__global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
+  __shared__ f32x4 red[KW][WR][64];
+  __shared__ __attribute__((aligned(16))) uint8_t xbuf[KW][2][kXTile];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, q = lane >> 4;
+
+  // the group of this m-tile (groups are few; a linear scan on scalars)
+  int gidx = 0;
+  for (int g = 1; g < a.n_groups; ++g)
+    if ((int)blockIdx.y >= a.g[g].mtile0) gidx = g;
+  const MmTile grp = a.g[gidx];
+  const int m0 = grp.m_begin + ((int)blockIdx.y - grp.mtile0) * 16;  // first activation row
+  const int m_end = grp.m_begin + grp.m_count;
+  const int r0 = blockIdx.x * 16 * WR;
+
+  // buffers over this workgroup's weight rows and activation rows (loads past
+  // them return zero); per-lane offsets are fixed, super-block offsets scalar
+  const int wrows = min(16 * WR, a.rows - r0);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.W + grp.w_off + (int64_t)r0 * a.row_bytes), (short)0, (int)(wrows * a.row_bytes), 0x00020000);
+  const int xrows = min(16, m_end - m0);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.X + (int64_t)m0 * a.cols), (short)0, (int)(xrows * a.cols * 4), 0x00020000);
+  int wv[WR];
+#pragma unroll
+  for (int t = 0; t < WR; ++t) wv[t] = min(16 * t + i, wrows - 1) * (int)a.row_bytes;
+  const bool ragged = (a.cols & 255) != 0;
+
+  // this wave's super-blocks: wave, wave + KW, ... (n of them); requests past
+  // the last one re-read it (their results are never used)
+  const int n = a.nsb > wave ? (a.nsb - wave + KW - 1) / KW : 0;
+  auto fetch = [&](Stage<WR>& st, int slot, int k) {
+    const int sb = wave + KW * (k < n ? k : n - 1);
+    // every offset in the per-lane part (the buffer's range check covers it);
+    // a ragged row's tail is clamped to the next row's start (cleared later)
+    const int col = min(256 * sb + 4 * lane, a.cols) * 4;
+    issue_fence();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) load_lds16(xrs, &xbuf[wave][slot][r * kXRow], r * a.cols * 4 + col, 0);
+#pragma unroll
+    for (int t = 0; t < WR; ++t) {
+      st.hd[t] = buf_b128(wrs, wv[t], sb * kQ4KBytes);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) st.cw[t][g] = buf_b64(wrs, wv[t] + 16 + 32 * g + 8 * q, sb * kQ4KBytes);
+    }
+    issue_fence();
+  };
+  // vector-memory operations of one fetch (they retire in order)
+  constexpr int kFetchOps = 16 + 5 * WR;
+
+  f32x4 acc[WR];
+#pragma unroll
+  for (int t = 0; t < WR; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Stage<WR>& st, int slot, int k) {
+    const int sb = wave + KW * k;
+    // this stage's loads (one fetch was issued after them)
+    wait_vmcnt<kFetchOps>();
+    // lane (i, q): columns 8q..8q+7 of each sub-block of activation row i
+    f32x4 xr[16];
+    const uint8_t* xt = &xbuf[wave][slot][i * kXRow + 32 * q];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xr[2 * j] = *(const f32x4*)(xt + 128 * j);
+      xr[2 * j + 1] = *(const f32x4*)(xt + 128 * j + 16);
+    }
+    if (ragged && sb == a.nsb - 1) {
+      // columns past cols read the next row (or zero): clear them
+      const int cbase = 256 * sb + 8 * q;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (cbase + 32 * j + e >= a.cols) xr[2 * j + e / 4][e % 4] = 0.f;
+    }
+    // the row's largest magnitude over the super-block (lanes i, i+16, i+32, i+48)
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xr[c].x), fabsf(xr[c].y)), fmaxf(fabsf(xr[c].z), fabsf(xr[c].w))));
+    mx = fmaxf(mx, lane_xor(mx, 16));
+    mx = fmaxf(mx, lane_xor(mx, 32));
+    // 2^e with the largest magnitude in [2^9, 2^10): e = 136 - biased exponent
+    int e = 0;
+    if (mx > 0.f) {
+      const int be = (int)((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFF);
+      e = 136 - be;
+      e = e > 126 ? 126 : (e < -126 ? -126 : e);
+    }
+    const float s = __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);
+    const float sinv = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);
+    // 2^-e of the four activation rows whose outputs this lane holds (4q..4q+3)
+    float sv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sv[c] = lane_read(sinv, 4 * q + c);
+
+    RowHead h[WR];
+#pragma unroll
+    for (int t = 0; t < WR; ++t) h[t] = decode_head(st.hd[t]);
+    f32x4 p1[WR];
+#pragma unroll
+    for (int t = 0; t < WR; ++t) p1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float ps[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f32x4 a0 = xr[2 * j], a1 = xr[2 * j + 1];
+      uint32_t hi[4], lo[4];
+      split2(a0.x, a0.y, s, hi[0], lo[0]);
+      split2(a0.z, a0.w, s, hi[1], lo[1]);
+      split2(a1.x, a1.y, s, hi[2], lo[2]);
+      split2(a1.z, a1.w, s, hi[3], lo[3]);
+      const h8 xh = as_h8(hi[0], hi[1], hi[2], hi[3]);
+      const h8 xl = as_h8(lo[0], lo[1], lo[2], lo[3]);
+      ps[j] = ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w));
+#pragma unroll
+      for (int t = 0; t < WR; ++t) {
+        const u32x2 c = st.cw[t][j >> 1];
+        const h2 sc = {h[t].sc[j], h[t].sc[j]}, nsc = {h[t].nsc[j], h[t].nsc[j]};
+        const h8 wop = (j & 1) ? weight_operand<1>(c.x, c.y, sc, nsc) : weight_operand<0>(c.x, c.y, sc, nsc);
+        p1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, wop, p1[t], 0, 0, 0);
+        p1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, wop, p1[t], 0, 0, 0);
+      }
+    }
+    uint32_t mh[4], ml[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) split2(ps[2 * c], ps[2 * c + 1], s, mh[c], ml[c]);
+    const h8 mhi = as_h8(mh[0], mh[1], mh[2], mh[3]);
+    const h8 mlo = as_h8(ml[0], ml[1], ml[2], ml[3]);
+#pragma unroll
+    for (int t = 0; t < WR; ++t) {
+      f32x4 p2 = {0.f, 0.f, 0.f, 0.f};
+      p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(mhi, h[t].mop, p2, 0, 0, 0);
+      p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(mlo, h[t].mop, p2, 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float v = __builtin_fmaf(h[t].d, p1[t][c], -(h[t].dmin * p2[c]));
+        acc[t][c] = __builtin_fmaf(v, sv[c], acc[t][c]);
+      }
+    }
+  };
+
+  Stage<WR> sa, sbuf;
+  if (n > 0) {
+    fetch(sa, 0, 0);
+    for (int k = 0; k < n; k += 2) {
+      fetch(sbuf, 1, k + 1);
+      compute(sa, 0, k);
+      fetch(sa, 0, k + 2);
+      if (k + 1 < n) compute(sbuf, 1, k + 1);
+    }
+    wait_vmcnt<0>();  // the last (unused) requests land before the LDS is left
+  }
+
+  // add the waves' products in wave order and store: lane (i, q) of row
+  // tile t holds Y[m0 + 4q + c][r0 + 16t + i]
+#pragma unroll
+  for (int t = 0; t < WR; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  for (int t = wave; t < WR; t += KW) {
+    f32x4 v = red[0][t][lane];
+#pragma unroll
+    for (int w = 1; w < KW; ++w) {
+      const f32x4 o = red[w][t][lane];
+      v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+    }
+    const int r = r0 + 16 * t + i;
+    if (r < a.rows) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int m = m0 + 4 * q + c;
+        if (m < m_end) a.Y[(int64_t)m * a.rows + r] = v[c];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared-activation kernel: a workgroup of four waves owns 64 R weight rows
+// (wave w: rows 16 R w .. 16 R w + 16 R - 1) and 16 C activation rows, over
+// every super-block. Each super-block's activation tile is converted once,
+// by all four waves together, into the fp16 operand fragments in LDS, and
+// every wave multiplies it against its own weight rows; so the conversion is
+// paid once per 64 R weight rows instead of once per 16 WR.
+//
+// Pipeline, per super-block k: the raw activation rows and the weight bytes
+// of super-block k + D are requested (register rings; D super-blocks in
+// flight), super-block k is multiplied (LDS buffer k % 2), super-block k + 1
+// is converted into the other LDS buffer, and one barrier ends the step.
+
+// One operand fragment (64 lanes x 16 bytes): lane L's 16 bytes sit at
+// (L / 16) * 272 + (L % 16) * 16. The 16-byte gap after each group of 16
+// lanes spreads the conversion's writes (one activation row at a time) over
+// all bank groups; the operand reads stay conflict-free.
+constexpr int kFragGroup = 272;
+constexpr int kFragBytes = 4 * kFragGroup;
+constexpr int kMinFrag = 16;  // fragments 0-7: hi parts of sub-blocks 0-7, 8-15: lo parts,
+                              // 16, 17: the min-term hi and lo parts
+constexpr int kTileBytes = 18 * kFragBytes;  // one 16-row m-tile of one super-block
+
+// fp16 parts of a * s: hi = fp16(a s), lo = fp16(a s - hi), in the low halves.
+__device__ __forceinline__ void split1(float a, float s, uint32_t& hi, uint32_t& lo) {
+  __asm__("v_fma_mixlo_f16 %0, %2, %3, 0\n\t"
+          "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel_hi:[0,0,1]"
+          : "=&v"(hi), "=&v"(lo)
+          : "v"(a), "v"(s));
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+template <int R>
+struct WStage {
+  u32x4 hd[R];
+  u32x2 cw[R][4];
+};
+
+__device__ __forceinline__ f32x4 buf_f32x4(__amdgpu_buffer_rsrc_t rs, int voff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+}
+
+template <int R, int C, int D, int KS, int RS>
+__global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
+  static_assert(RS == 4 || (RS == 8 && C % 2 == 0), "row groups");
+  constexpr int CW = C * 4 / RS;          // m-tiles each wave converts
+  constexpr int SW = D + 1;               // weight ring slots
+  constexpr int SX = D == 1 ? 1 : D + 1;  // activation ring slots (divides SW)
+  // hi and lo products in separate accumulators when there are too few
+  // independent MFMA chains to cover the dependent-issue latency
+  constexpr bool kSplitAcc = R * C < 4;
+  constexpr int kStage = C * kTileBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[KS][2][kStage];
+  __shared__ __attribute__((aligned(16))) float xsv[KS][2][16 * C];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave % RS;  // weight-row group
+  const int wk = wave / RS;  // super-block group: super-blocks wk, wk + KS, ...
+  const int i = lane & 15, q = lane >> 4;
+
+  int gidx = 0;
+  for (int g = 1; g < a.n_groups; ++g)
+    if ((int)blockIdx.y >= a.g[g].mtile0) gidx = g;
+  const MmTile grp = a.g[gidx];
+  const int m0 = grp.m_begin + ((int)blockIdx.y - grp.mtile0) * 16 * C;
+  const int m_end = grp.m_begin + grp.m_count;
+  const int r0 = blockIdx.x * 16 * RS * R;
+
+  // weight rows of the workgroup (each lane's row clamped to a real one) and
+  // activation rows of the tile (rows past the group read as zero)
+  const int wrows = min(16 * RS * R, a.rows - r0);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.W + grp.w_off + (int64_t)r0 * a.row_bytes), (short)0, (int)(wrows * a.row_bytes), 0x00020000);
+  const int xrows = min(16 * C, m_end - m0);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.X + (int64_t)m0 * a.cols), (short)0, (int)(xrows * a.cols * 4), 0x00020000);
+  int wv[R];
+#pragma unroll
+  for (int t = 0; t < R; ++t) wv[t] = min(16 * (wr * R + t) + i, wrows - 1) * (int)a.row_bytes;
+  const int n = a.nsb;
+  const int nk = n > wk ? (n - wk + KS - 1) / KS : 0;  // this group's super-blocks
+  const int nsteps = (n + KS - 1) / KS;                // the workgroup's steps (every group)
+
+  // conversion: wave wr of a group converts rows w, w + 4, w + 8, w + 12
+  // (w = wr % 4) of m-tiles wr / 4, wr / 4 + RS / 4, ..., one per 16-lane
+  // row of the wave (r = lane / 16); in request v (0..3) lane l = lane % 16
+  // holds columns 64 v + 4 l .. + 3, which are half of operand lane
+  // (row, (l % 8) / 2) of sub-block 2 v + l / 8
+  const int cr = lane >> 4, cl = lane & 15;
+  const int ci = (wr & 3) + 4 * cr;  // the lane's row within each m-tile
+  const int cb = wr >> 2;            // the first m-tile it converts
+  const int cv_off = (cl >> 3) * kFragBytes + ((cl >> 1) & 3) * kFragGroup + ci * 16 + (cl & 1) * 8;
+  const int cm_off = kMinFrag * kFragBytes + ((cl >> 1) & 3) * kFragGroup + ci * 16 + 2 * (cl >> 3);
+  int xv[CW];  // byte offset of the lane's activation row of each m-tile it converts
+#pragma unroll
+  for (int c = 0; c < CW; ++c) xv[c] = (16 * (cb + c * RS / 4) + ci) * a.cols * 4;
+  // operand reads: lane (i, q)
+  const int rd_off = q * kFragGroup + i * 16;
+
+  f32x4 xr[SX][CW][4];
+  WStage<R> ws[SW];
+
+  // the group's k-th super-block (k past the last re-reads the last)
+  auto sb_of = [&](int k) { return wk + KS * (k < nk ? k : nk - 1); };
+
+  // requests for super-block sb (the column offset is clamped so that a
+  // ragged row's tail stays inside the buffer)
+  auto fetch = [&](int sb, int xslot, int wslot) {
+    int col[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) col[v] = min(256 * sb + 64 * v + 4 * cl, a.cols) * 4;
+    issue_fence();
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) xr[xslot][c][v] = buf_f32x4(xrs, xv[c] + col[v]);
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      ws[wslot].hd[t] = buf_b128(wrs, wv[t], sb * kQ4KBytes);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) ws[wslot].cw[t][g] = buf_b64(wrs, wv[t] + 16 + 32 * g + 8 * q, sb * kQ4KBytes);
+    }
+    issue_fence();
+  };
+
+  // super-block sb's activation rows -> the group's LDS buffer buf
+  auto convert = [&](int sb, int xslot, int buf) {
+    uint8_t* base = &xs[wk][buf][0];
+    if ((a.cols & 255) != 0 && sb == n - 1) {  // ragged last super-block: clear columns past the row
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (256 * sb + 64 * v + 4 * cl >= a.cols)
+#pragma unroll
+          for (int c = 0; c < CW; ++c) xr[xslot][c][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+      const int ct = cb + c * RS / 4;  // the m-tile
+      // the row's largest magnitude: 16 values per lane, then its 16 lanes
+      float m = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const f32x4 x = xr[xslot][c][v];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+      }
+      uint32_t mb = __builtin_bit_cast(uint32_t, m);
+      mb = max(mb, dpp_u32<0xB1>(mb));   // quad_perm [1,0,3,2]
+      mb = max(mb, dpp_u32<0x4E>(mb));   // quad_perm [2,3,0,1]
+      mb = max(mb, dpp_u32<0x141>(mb));  // row_half_mirror
+      mb = max(mb, dpp_u32<0x140>(mb));  // row_mirror
+      // 2^e with the row's largest magnitude in [2^9, 2^10)
+      int e = mb != 0 ? 136 - (int)(mb >> 23) : 0;
+      e = e > 126 ? 126 : (e < -126 ? -126 : e);
+      const float s = __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);
+      uint8_t* tile = base + ct * kTileBytes;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const f32x4 x = xr[xslot][c][v];
+        uint32_t h0, l0, h1, l1;
+        split2(x.x, x.y, s, h0, l0);
+        split2(x.z, x.w, s, h1, l1);
+        *(u32x2*)(tile + 2 * v * kFragBytes + cv_off) = u32x2{h0, h1};
+        *(u32x2*)(tile + (8 + 2 * v) * kFragBytes + cv_off) = u32x2{l0, l1};
+        // this lane pair's 8 columns summed, for the min term
+        const float s4 = (x.x + x.y) + (x.z + x.w);
+        const float s8 = s4 + __builtin_bit_cast(float, dpp_u32<0xB1>(__builtin_bit_cast(uint32_t, s4)));
+        if ((cl & 1) == 0) {
+          uint32_t mh, ml;
+          split1(s8, s, mh, ml);
+          *(uint16_t*)(tile + cm_off + 4 * v) = (uint16_t)mh;
+          *(uint16_t*)(tile + cm_off + 4 * v + kFragBytes) = (uint16_t)ml;
+        }
+      }
+      if (cl == 0) xsv[wk][buf][16 * ct + ci] = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);
+    }
+  };
+
+  f32x4 acc[R][C];
+#pragma unroll
+  for (int t = 0; t < R; ++t)
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int wslot, int buf) {
+    const uint8_t* base = &xs[wk][buf][0];
+    RowHead h[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) h[t] = decode_head(ws[wslot].hd[t]);
+    f32x4 ph[R][C], pl[R][C];
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+      for (int c = 0; c < C; ++c) ph[t][c] = pl[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h8 xh[C], xl[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        xh[c] = *(const h8*)(base + c * kTileBytes + j * kFragBytes + rd_off);
+        xl[c] = *(const h8*)(base + c * kTileBytes + (8 + j) * kFragBytes + rd_off);
+      }
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const u32x2 cw = ws[wslot].cw[t][j >> 1];
+        const h2 sc = {h[t].sc[j], h[t].sc[j]}, nsc = {h[t].nsc[j], h[t].nsc[j]};
+        const h8 wop = (j & 1) ? weight_operand<1>(cw.x, cw.y, sc, nsc) : weight_operand<0>(cw.x, cw.y, sc, nsc);
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          ph[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[c], wop, ph[t][c], 0, 0, 0);
+          if constexpr (kSplitAcc)
+            pl[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[c], wop, pl[t][c], 0, 0, 0);
+          else
+            ph[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[c], wop, ph[t][c], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const h8 mh = *(const h8*)(base + c * kTileBytes + kMinFrag * kFragBytes + rd_off);
+      const h8 ml = *(const h8*)(base + c * kTileBytes + (kMinFrag + 1) * kFragBytes + rd_off);
+      const f32x4 sv = *(const f32x4*)&xsv[wk][buf][16 * c + 4 * q];
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        f32x4 p2 = {0.f, 0.f, 0.f, 0.f};
+        p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(mh, h[t].mop, p2, 0, 0, 0);
+        p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ml, h[t].mop, p2, 0, 0, 0);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const float p1 = kSplitAcc ? ph[t][c][cc] + pl[t][c][cc] : ph[t][c][cc];
+          const float v = __builtin_fmaf(h[t].d, p1, -(h[t].dmin * p2[cc]));
+          acc[t][c][cc] = __builtin_fmaf(v, sv[cc], acc[t][c][cc]);
+        }
+      }
+    }
+  };
+
+  // LDS writes done, then the workgroup barrier (no wait on the requests)
+  auto step_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    bare_barrier();
+  };
+
+  // every group takes the same number of steps (a group with fewer
+  // super-blocks idles through its last one), so the barriers match
+#pragma unroll
+  for (int d = 0; d < D; ++d) fetch(sb_of(d), d % SX, d % SW);
+  if (nk > 0) convert(sb_of(0), 0, 0);
+  step_barrier();
+  for (int k0 = 0; k0 < nsteps; k0 += SW) {
+#pragma unroll
+    for (int u = 0; u < SW; ++u) {
+      const int k = k0 + u;
+      if (k < nsteps) {
+        fetch(sb_of(k + D), (u + D) % SX, (u + D) % SW);
+        if (k < nk) compute(u, k & 1);
+        if (k + 1 < nk) convert(sb_of(k + 1), (u + 1) % SX, (k + 1) & 1);
+        step_barrier();
+      }
+    }
+  }
+
+  // groups 1.. park their sums in LDS; group 0 adds them in group order
+  if constexpr (KS > 1) {
+    f32x4* red = (f32x4*)&xs[0][0][0];  // [KS - 1][RS][R][C][64]
+    if (wk > 0) {
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+#pragma unroll
+        for (int c = 0; c < C; ++c) red[((((wk - 1) * RS + wr) * R + t) * C + c) * 64 + lane] = acc[t][c];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    bare_barrier();
+    if (wk > 0) return;
+#pragma unroll
+    for (int g = 1; g < KS; ++g)
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const f32x4 o = red[((((g - 1) * RS + wr) * R + t) * C + c) * 64 + lane];
+          acc[t][c] = f32x4{acc[t][c].x + o.x, acc[t][c].y + o.y, acc[t][c].z + o.z, acc[t][c].w + o.w};
+        }
+  }
+
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    const int r = r0 + 16 * (wr * R + t) + i;
+    if (r < a.rows) {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int m = m0 + 16 * c + 4 * q + cc;
+          if (m < m_end) a.Y[(int64_t)m * a.rows + r] = acc[t][c][cc];
+        }
+    }
+  }
+}
+
+#ifndef GQ_MM_KW
+#define GQ_MM_KW 4  // waves per workgroup (splitting the super-blocks)
+#endif
+
+template <int WR>
+hipError_t launch(const MmArgs& a, int gx, int gy, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_q4k_kernel<WR, GQ_MM_KW>), dim3(gx, gy), dim3(GQ_MM_KW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int R, int C, int D, int KS, int RS>
+hipError_t launch_xs(const MmArgs& a, int gy, hipStream_t s) {
+  const int gx = (a.rows + 16 * RS * R - 1) / (16 * RS * R);
+  hipLaunchKernelGGL((gemm_q4k_xs_kernel<R, C, D, KS, RS>), dim3(gx, gy), dim3(64 * RS * KS), 0, s, a);
+  return hipGetLastError();
+}
+
+// m-tiles of tm activation rows over the groups (the grid's y).
+int64_t count_mtiles(const int64_t* group_m, int n_groups, int tm) {
+  int64_t gy = 0;
+  for (int g = 0; g < n_groups; ++g) gy += (group_m[g] + tm - 1) / tm;
+  return gy;
+}
+
+// The group table for m-tiles of tm activation rows; returns the number of
+// m-tiles (the grid's y), or -1 when the groups exceed the table.
+int build_groups(MmArgs& m, const int64_t* group_m, const int64_t* group_off, int n_groups,
+                 int64_t group_w_bytes, int tm) {
+  int gy = 0, ng = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    if (group_m[g] == 0) continue;
+    if (ng == kMaxGroups) return -1;
+    m.g[ng] = MmTile{group_w_bytes * g, (int)group_off[g], (int)group_m[g], gy};
+    gy += (int)((group_m[g] + tm - 1) / tm);
+    ++ng;
+  }
+  m.n_groups = ng;
+  return gy;
+}
+
+}  // namespace
+
+bool gemm_q4k_fits(int64_t rows, int64_t cols, int64_t row_bytes) {
+  // 31-bit buffer offsets: 256 weight rows and 64 activation rows of a tile
+  return 256 * row_bytes < ((int64_t)1 << 31) && 64 * cols * 4 < ((int64_t)1 << 31) && rows <= INT32_MAX;
+}
+
+// Tile choice, measured on MI355X (Q4_K 14336 x 4096 gate / 4096 x 14336
+// down): the largest shared-activation tile whose grid still fills about
+// every CU -- 256 x 64 (gate M = 512: 191 us), 256 x 32 (down M = 512:
+// 213 us), 128 x 32 split in two along k (gate M = 64: 38 us), 64 x 16 split
+// in four (gate M = 16: 19 us, down M = 64: 56 us) -- else the per-wave
+// kernel with as many weight-row tiles per workgroup as still fill the GPU
+// (down M = 16: 30 us).
+hipError_t launch_gemm_q4k(const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
+                           int n_groups, int64_t group_w_bytes, int cus, hipStream_t s) {
+  MmArgs m{};
+  m.W = a.W;
+  m.X = a.X;
+  m.Y = a.Y;
+  m.row_bytes = a.row_bytes;
+  m.rows = a.rows;
+  m.cols = a.cols;
+  m.nsb = (a.cols + 255) / 256;
+  const int64_t fill = (int64_t)cus * 7 / 8;
+  auto grid = [&](int tr, int tm) { return ((a.rows + tr - 1) / tr) * count_mtiles(group_m, n_groups, tm); };
+  auto run_xs = [&](auto launch, int tm) {
+    const int gy = build_groups(m, group_m, group_off, n_groups, group_w_bytes, tm);
+    if (gy < 0) return hipErrorInvalidValue;
+    if (gy == 0) return hipSuccess;
+    return launch(m, gy, s);
+  };
+  if (grid(256, 64) >= fill) return run_xs(launch_xs<2, 4, 1, 1, 8>, 64);
+  if (grid(256, 32) >= fill) return run_xs(launch_xs<2, 2, 2, 1, 8>, 32);
+  if (grid(128, 32) >= fill) return run_xs(launch_xs<1, 2, 1, 2, 8>, 32);
+  if (grid(64, 16) >= fill) return run_xs(launch_xs<1, 1, 1, 4, 4>, 16);
+  const int gy = build_groups(m, group_m, group_off, n_groups, group_w_bytes, 16);
+  if (gy < 0) return hipErrorInvalidValue;
+  if (gy == 0) return hipSuccess;
+  if (grid(32, 16) >= fill) return launch<2>(m, (a.rows + 31) / 32, gy, s);
+  return launch<1>(m, (a.rows + 15) / 16, gy, s);
+}
+
+}  // namespace gq

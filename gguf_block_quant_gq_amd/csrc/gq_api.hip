@@ -259,6 +259,22 @@ extern "C" int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, v
 
 namespace {
 
+// Q4_K products run on the fp16 matrix cores when rows are whole groups of
+// four floats, else on the fp32 matrix cores.
+bool q4k_matrix_cores(int fmt, int64_t cols) { return fmt == GQ_FMT_Q4_K && cols % 4 == 0; }
+
+bool batched_matvec(int64_t M, int64_t rows, int64_t cols) {
+  return M > 1 && M < 16 && rows * cols <= kBatchMaxWork / M;
+}
+
+// Whether the kernel that gq_matmul picks for this shape can address it
+// (its tiles use 31-bit buffer offsets); checked before any HIP call.
+bool matmul_addressable(int fmt, int64_t rows, int64_t cols, int64_t M, int64_t rb) {
+  if (q4k_matrix_cores(fmt, cols) && M > 1 && !batched_matvec(M, rows, cols))
+    return gq::gemm_q4k_fits(rows, cols, rb);
+  return true;
+}
+
 // gq_matmul after its checks: the kernel route for M activation rows.
 int matmul_route(int fmt, const void* W, int64_t rb, int64_t rows, int64_t cols, const float* X,
                  int64_t M, float* Y, void* stream, int cus) {
@@ -273,11 +289,13 @@ int matmul_route(int fmt, const void* W, int64_t rb, int64_t rows, int64_t cols,
     gq::GemvArgs v{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
     return finish(gq::launch_gemv(fmt, v, cus, (hipStream_t)stream));
   }
-  if (M < 16 && rows * cols <= kBatchMaxWork / M)
-    return batch_launch(fmt, W, rb, rows, cols, X, M, Y, stream, cus);
+  if (batched_matvec(M, rows, cols)) return batch_launch(fmt, W, rb, rows, cols, X, M, Y, stream, cus);
   gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
-  if (fmt == GQ_FMT_Q4_K) return finish(gq::launch_gemm_mfma(fmt, a, cus, (hipStream_t)stream));
-  if (M >= f32_matrix_core_min_m(fmt))
+  if (q4k_matrix_cores(fmt, cols)) {
+    const int64_t off = 0;
+    return finish(gq::launch_gemm_q4k(a, &M, &off, 1, 0, cus, (hipStream_t)stream));
+  }
+  if (fmt == GQ_FMT_Q4_K || M >= f32_matrix_core_min_m(fmt))
     return finish(gq::launch_gemm_f32(fmt, a, cus, (hipStream_t)stream));
   return finish(gq::launch_gemm_small(fmt, a, cus, (hipStream_t)stream));
 }
@@ -296,6 +314,7 @@ extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, con
   if ((uintptr_t)X % 4 || (uintptr_t)Y % 4) return GQ_ERR_ALIGN;
   if (overlaps(Y, M * rows * 4, W, wbytes) || overlaps(Y, M * rows * 4, X, M * cols * 4))
     return GQ_ERR_OVERLAP;
+  if (!matmul_addressable(fmt, rows, cols, M, rb)) return GQ_ERR_SHAPE;
 
   const int cus = current_cus();
   if (cus <= 0) return GQ_ERR_DEVICE;
@@ -327,10 +346,30 @@ extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64
   if ((st = check_align(fmt, W)) != GQ_OK) return st;
   if ((uintptr_t)X % 4 || (uintptr_t)Y % 4) return GQ_ERR_ALIGN;
   if (overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, X, xbytes)) return GQ_ERR_OVERLAP;
+  if (q4k_matrix_cores(fmt, cols) && !gq::gemm_q4k_fits(rows, cols, rb)) return GQ_ERR_SHAPE;
 
   const int cus = current_cus();
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
+  if (q4k_matrix_cores(fmt, cols)) {
+    // one grouped launch per 64 experts: group e multiplies expert e by its
+    // m_per_expert[e] rows of X (starting after the earlier experts' rows)
+    gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0, 0};
+    constexpr int64_t kChunk = 64;
+    int64_t off[kChunk];
+    int64_t m0 = 0;
+    for (int64_t e0 = 0; e0 < n_expert; e0 += kChunk) {
+      const int ne = (int)(n_expert - e0 < kChunk ? n_expert - e0 : kChunk);
+      for (int g = 0; g < ne; ++g) {
+        off[g] = m0;
+        m0 += m_per_expert[e0 + g];
+      }
+      a.W = (const uint8_t*)W + e0 * ebytes;
+      st = finish(gq::launch_gemm_q4k(a, m_per_expert + e0, off, ne, ebytes, cus, (hipStream_t)stream));
+      if (st != GQ_OK) return st;
+    }
+    return GQ_OK;
+  }
   // one gq_matmul per expert with rows, in expert order on the caller's stream
   int64_t m0 = 0;
   for (int64_t e = 0; e < n_expert; ++e) {

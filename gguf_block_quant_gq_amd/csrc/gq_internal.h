@@ -78,15 +78,17 @@ hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi = kE
 bool gemv_q4k_supports(const GemvArgs& a, int cus, const ExpertArgs* ex);
 hipError_t launch_gemv_q4k(GemvArgs a, int cus, hipStream_t s, int epi, const ExpertArgs* ex);
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
-hipError_t launch_gemm_mfma(int fmt, GemmArgs a, int cus, hipStream_t s);
+// The Q4_K product on the fp16 matrix cores (gemm_q4k.hip), one launch for
+// n_groups products that share a shape: group g multiplies the weight tensor
+// at W + g * group_w_bytes by the group_m[g] activation rows starting at row
+// group_off[g] of X, into the same rows of Y (a single product: one group).
+// It takes cols % 4 == 0 (activations are read four at a time);
+// gemm_q4k_fits: whether its 31-bit buffer offsets cover the shape.
+bool gemm_q4k_fits(int64_t rows, int64_t cols, int64_t row_bytes);
+hipError_t launch_gemm_q4k(const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
+                           int n_groups, int64_t group_w_bytes, int cus, hipStream_t s);
+// The fp32 matrix-core product (gemm_f32.hip): Q8_0, Q8_0 split, Q5_0, Q5_K,
+// Q6_K, and Q4_K rows whose length is not a multiple of 4.
 hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s);
-
-// y[i] = sum over z < ks of part[z * n + i], in split order (deterministic).
-hipError_t launch_split_sum(const float* part, float* y, int64_t n, int ks, hipStream_t s);
-
-// Stream-ordered scratch from a per-device pool (workspace.hip): the block is
-// usable by work enqueued on `s` after ws_alloc and before ws_free.
-hipError_t ws_alloc(size_t bytes, hipStream_t s, void** p);
-hipError_t ws_free(void* p, hipStream_t s);
 
 }  // namespace gq

@@ -75,6 +75,33 @@ struct Q5_0Quad {
   __device__ static void load(Raw& r, const uint8_t* row, int i0, int) { load(r, row, i0); }
 };
 
+// Q4_K: super-block i0 / 256, i = i0 % 256 in sub-block j = i / 32 (g = j / 2,
+// h = j % 2) at position l0 = i % 32: one code dword (low nibbles for h = 0,
+// high ones for h = 1) and the header.
+struct Q4KQuad {
+  struct Raw {
+    u32x4 hd;
+    uint32_t w;
+  };
+  __device__ static void load(Raw& r, const uint8_t* row, int i0) {
+    const uint8_t* blk = row + (int64_t)(i0 >> 8) * kQ4KBytes;
+    const int i = i0 & 255, g = i >> 6, l0 = i & 31;
+    r.hd = load_u32x4(blk);
+    r.w = load_u32(blk + 16 + 32 * g + l0);
+  }
+  __device__ static void decode(const Raw& r, int i0, float v[4]) {
+    const int i = i0 & 255, j = i >> 5, g = j >> 1, h = j & 1;
+    uint32_t sc[2], m[2];
+    q4k_scales(q4k_scale_sel(g), r.hd.y, r.hd.z, r.hd.w, sc, m);
+    const float A = half_bits_to_float(r.hd.x & 0xFFFFu) * (float)sc[h];  // exact
+    const float B = half_bits_to_float(r.hd.x >> 16) * (float)m[h];       // exact
+    const uint32_t code = (h ? r.w >> 4 : r.w) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = A * (float)((code >> (8 * e)) & 0xFFu) - B;
+  }
+  __device__ static void load(Raw& r, const uint8_t* row, int i0, int) { load(r, row, i0); }
+};
+
 // Q5_K: super-block i0 / 256, i = i0 % 256 in sub-block j = i / 32 (g = j / 2,
 // h = j % 2) at position l0 = i % 32: one code dword, one qh dword, the header.
 struct Q5KQuad {

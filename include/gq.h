@@ -48,18 +48,11 @@
  *
  * Ownership and threading
  *   All pointers are device pointers owned by the caller; the library never
- *   frees or keeps them. gq_dequant and the gq_matvec family use no memory
- *   beyond their arguments. gq_matmul on the matrix cores takes a
- *   stream-ordered workspace from a library-owned HIP memory pool (one per
- *   device, created on first use, memory kept until the process ends):
- *   Q4_K 17472 * ceil(M/16) * ceil(cols/256) bytes of prepared activations,
- *   and for every format 4 * M * rows bytes per split when the K range is
- *   split over workgroups, each request rounded up to a power of two (at
- *   least 1 MiB) so that calls of different sizes reuse the pool's blocks. It is allocated and released on the caller's stream, so the
- *   call stays asynchronous and calls on different streams never share it;
- *   an allocation failure returns GQ_ERR_DEVICE. Global state: that pool and
- *   a per-device cache of device properties, each filled once. Calls on
- *   different streams may run concurrently.
+ *   frees or keeps them. No entry point uses device memory beyond its
+ *   arguments: there is no workspace (work split along k stays inside one
+ *   workgroup and is added in a fixed order). Global state: a per-device
+ *   cache of device properties, filled once. Calls on different streams may
+ *   run concurrently.
  *
  * Alignment
  *   Q8_0, Q5_0 and Q6_K W: 2-byte aligned (a row range of such a tensor
@@ -221,15 +214,26 @@ int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out, v
  * section: the matmuls run over up to 64 positions at once, each weight read
  * once per chunk). M == 1 runs the gq_matvec kernel. With M < 16 and
  * M * rows * cols <= 2^28 the call is gq_matvec_batch, so every row of Y
- * equals gq_matvec of its activation row bit for bit. Otherwise Q4_K runs on
- * the fp16 matrix cores with exact operands (workspace described above);
- * Q5_K, Q6_K and split Q8_0 with M >= 2, and Q8_0 and Q5_0 with M >= 8, run
- * on the fp32 matrix cores: each k-chunk of W is dequantised exactly to fp32
- * and multiplied with the fp32 activations (a workspace of 4 * M * rows bytes
- * per extra split when the k range is split over workgroups); Q8_0 and Q5_0
- * with 2 <= M < 8 stream W once per 15 activation rows on the fp32 vector
- * units. Same accuracy bound as gq_matvec; repeated calls give bit-identical
- * results. Asynchronous on `stream`.
+ * equals gq_matvec of its activation row bit for bit. Otherwise, in one
+ * launch:
+ *   - Q4_K with cols % 4 == 0 runs on the fp16 matrix cores with exact
+ *     operands (sc * code is exact in fp16; each activation row's 256 values
+ *     of a super-block are scaled by a power of two and split into fp16 hi
+ *     and lo parts). It needs 64 * 4 * cols < 2^31 and
+ *     256 * gq_row_bytes(GQ_FMT_Q4_K, cols) < 2^31 (cols < 2^23), else
+ *     GQ_ERR_SHAPE before any launch. Accuracy: the gq_matvec bound, except
+ *     that activations below about 2^-14 of the largest magnitude max_b in
+ *     their row's super-block b (256 columns) are carried only to an
+ *     absolute 2^-34 max_b: an extra error of at most
+ *     2^-33 * max_b * sum_{c in b} (|d sc_j q_c| + |dmin m_j|) per
+ *     super-block, none when every activation is 0 or within that range.
+ *   - Q4_K with other cols, Q5_K, Q6_K and split Q8_0 with M >= 2, and Q8_0
+ *     and Q5_0 with M >= 8, run on the fp32 matrix cores: each k-chunk of W
+ *     is dequantised exactly to fp32 and multiplied with the fp32
+ *     activations; same accuracy bound as gq_matvec.
+ *   - Q8_0 and Q5_0 with 2 <= M < 8 stream W once per 15 activation rows on
+ *     the fp32 vector units; same accuracy bound as gq_matvec.
+ * Repeated calls give bit-identical results. Asynchronous on `stream`.
  */
 int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
               const float* X, int64_t M, float* Y, void* stream);
@@ -246,15 +250,19 @@ int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
  * order, overwritten:
  *   Y[(o_e + i)*rows + r] = sum_c w_e(r, c) * X[(o_e + i)*cols + c],
  *   o_e = m_0 + ... + m_{e-1}, i < m_e.
- * Each expert's block is exactly gq_matmul of that expert's matrix and rows
- * (same kernels, same bits): the batched matvec for small groups, the
- * matrix cores for large ones, with gq_matmul's workspace per group.
+ * Q4_K with cols % 4 == 0: one launch per 64 experts on the fp16 matrix
+ * cores (every group, whatever its row count, as in gq_matmul's matrix-core
+ * case, with the same accuracy bound and shape limits); each block is
+ * deterministic but may differ in the last bits from gq_matmul of the same
+ * rows, whose tile is chosen for that call alone. Other formats: each
+ * expert's block is exactly gq_matmul of that expert's matrix and rows
+ * (same kernels, same bits), enqueued in expert order.
  * Experts with no rows are skipped. All counts are checked (>= 0, sums
  * without overflow) before the first launch; n_expert == 0, rows == 0 or no
  * rows at all is a no-op. Asynchronous on `stream` (the counts are read
- * during the call and not kept). The groups are enqueued in expert order;
- * if a launch fails (GQ_ERR_DEVICE) the groups before it have been enqueued
- * and Y's later blocks are unspecified.
+ * during the call and not kept). If a launch fails (GQ_ERR_DEVICE) the
+ * launches before it have been enqueued and Y's later blocks are
+ * unspecified.
  */
 int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, int64_t cols,
                       const float* X, const int64_t* m_per_expert, float* Y, void* stream);

@@ -152,6 +152,20 @@ def test_validation_batch(lib):
     assert _mb(lib, Y=W_OK + 4 * 144 - 4) == gq.GQ_ERR_OVERLAP
 
 
+def test_validation_q4k_matrix_core_bounds(lib):
+    """The Q4_K fp16 matrix-core kernel addresses its tiles with 31-bit buffer
+    offsets (64 activation rows, 256 weight rows): wider rows are rejected on
+    the host, before any device call (so this runs without a GPU)."""
+    big = 1 << 23                       # 64 * 4 * cols == 2^31
+    far = 1 << 40                       # X, Y far apart: no overlap with W
+    # M = 16 with these widths is past the batched matvec's work bound
+    assert _mm(lib, rows=16, cols=big, M=16, X=far, Y=2 * far) == gq.GQ_ERR_SHAPE
+    assert _mm(lib, rows=16, cols=big + 256, M=64, X=far, Y=2 * far) == gq.GQ_ERR_SHAPE
+    assert _mge(lib, counts=(16, 0, 20), rows=16, cols=big, X=far, Y=2 * far) == gq.GQ_ERR_SHAPE
+    # (calls that pass validation are not made here: with a GPU present they
+    # would launch on these fake pointers)
+
+
 def _mge(lib, counts=(2, 0, 3), fmt=12, W=W_OK, rows=4, cols=256, X=X_OK, Y=Y_OK, n_expert=None):
     import ctypes
     arr = (ctypes.c_int64 * max(1, len(counts)))(*counts) if counts is not None else None

@@ -88,8 +88,10 @@ GROUPED = [
 
 @pytest.mark.parametrize("fmt,rows,cols,counts", GROUPED)
 def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
-    """Each expert's block of gq_matmul_experts equals gq_matmul of that
-    expert's matrix and rows bit for bit, and the oracle within tolerance."""
+    """Each expert's block of gq_matmul_experts is within tolerance of the
+    oracle. Q4_K with cols % 4 == 0 runs as one grouped launch: a second call
+    gives the same bits. The other formats run gq_matmul per expert: each
+    block equals gq_matmul of that expert's matrix and rows bit for bit."""
     n_expert, total = len(counts), sum(counts)
     rng = synth.rng_for(962, fmt * 1000 + rows)
     W = synth.weights(fmt, n_expert * rows, cols, rng)
@@ -101,6 +103,7 @@ def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
     assert_pad_untouched(Y, total * rows)
     got = to_host(Y)[:total * rows].reshape(total, rows)
     rb = gq.gq_row_bytes(fmt, cols)
+    grouped = fmt == 12 and cols % 4 == 0
     o = 0
     for e, m in enumerate(counts):
         if m == 0:
@@ -108,6 +111,12 @@ def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
         We = W[e * rows * rb:(e + 1) * rows * rb]
         ref, S = oracle.matmul(fmt, We, rows, cols, X[o:o + m], nthreads=oracle_threads())
         assert_within_tolerance(got[o:o + m], ref, S, f"expert {e}")
-        one = to_host(gq.gq_matmul(fmt, Wd[e * rows * rb:(e + 1) * rows * rb], rows, cols, Xd[o:o + m]))
-        assert np.array_equal(one.view(np.uint32), got[o:o + m].view(np.uint32)), e
+        if not grouped:
+            one = to_host(gq.gq_matmul(fmt, Wd[e * rows * rb:(e + 1) * rows * rb], rows, cols, Xd[o:o + m]))
+            assert np.array_equal(one.view(np.uint32), got[o:o + m].view(np.uint32)), e
         o += m
+    if grouped:
+        Y2 = sentinel_buffer(total * rows)
+        gq.gq_matmul_experts(fmt, Wd, n_expert, rows, cols, Xd, counts, Y=Y2[:total * rows])
+        again = to_host(Y2)[:total * rows].reshape(total, rows)
+        assert np.array_equal(again.view(np.uint32), got.view(np.uint32))

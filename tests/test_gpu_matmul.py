@@ -110,3 +110,56 @@ def test_few_rows_large_products(gq, oracle, fmt, rows, cols, M):
     Ws = oracle.select_rows(fmt, W, cols, idx)
     ref, S = oracle.matmul(fmt, Ws, idx.size, cols, X, nthreads=oracle_threads())
     assert_within_tolerance(Y[:, idx], ref, S, f"large few-row fmt={fmt} M={M}")
+
+
+def test_q4k_wide_dynamic_range(gq, oracle):
+    """Q4_K on the fp16 matrix cores: activations whose magnitudes span 2^-113
+    .. 2^100 across rows and super-blocks, each within 2^13 of the largest in
+    its row's super-block, meet the plain bound (every super-block is scaled
+    by its own power of two before the fp16 split)."""
+    rows, cols, M = 80, 1024, 40
+    rng = synth.rng_for(611, 0)
+    W = synth.weights(12, rows, cols, rng)
+    nsb = cols // 256
+    scale = np.exp2(rng.integers(-100, 101, size=(M, nsb))).astype(np.float64)
+    mag = np.exp2(rng.uniform(-13.0, 0.0, size=(M, cols)))
+    sign = np.where(rng.random((M, cols)) < 0.5, -1.0, 1.0)
+    X = (sign * mag * np.repeat(scale, 256, axis=1)).astype(np.float32)
+    X[rng.random((M, cols)) < 0.05] = 0.0
+    _check(gq, oracle, 12, W, rows, cols, X, "wide dynamic range")
+
+
+def test_q4k_outlier_on_zero_weight(gq, oracle):
+    """The documented limit of the fp16 split: in super-block 0 every weight
+    of sub-block 0 is zero (sc_0 = m_0 = 0 in every row) and one activation
+    row holds 2^40 there, so that row's other activations of the super-block
+    fall below 2^-14 of its largest and are carried only to an absolute
+    2^-34 * 2^40. That row stays within the stated extra term; every other row,
+    and that row's other super-blocks, meet the plain bound."""
+    rows, cols, M, hot = 64, 512, 20, 7
+    rng = synth.rng_for(612, 0)
+    W = synth.weights(12, rows, cols, rng).copy()
+    rb = 288
+    blk0 = W.reshape(rows, rb)[:, :144]     # super-block 0 of every row
+    blk0[:, 4] &= 0xC0                      # sc_0 = 0 (top bits belong to sc_4)
+    blk0[:, 8] &= 0xC0                      # m_0 = 0 (top bits belong to m_4)
+    X = synth.activations((M, cols), rng)
+    X[hot, 0] = np.float32(2.0 ** 40)
+    print(f"[matmul] outlier rows={rows} cols={cols} M={M}", flush=True)
+    Y = _run(gq, 12, W, rows, cols, X)
+    ref, S = oracle.matmul(12, W, rows, cols, X, nthreads=oracle_threads())
+    others = np.arange(M) != hot
+    assert_within_tolerance(Y[others], ref[others], S[others], "rows without the outlier")
+    # the stated extra term for the hot row: 2^-33 max_b sum_c (|d sc q| + |dmin m|),
+    # bounded with sc <= 63, q <= 15, m <= 63 from each row's d and dmin
+    hdr = blk0[:, :4].copy().view(np.float16).astype(np.float64).reshape(rows, 2)
+    per_col = np.abs(hdr[:, 0]) * 63 * 15 + np.abs(hdr[:, 1]) * 63
+    extra = 2.0 ** -33 * 2.0 ** 40 * 256 * per_col
+    err = np.abs(Y[hot].astype(np.float64) - ref[hot])
+    assert (err <= 2e-4 * S[hot] + extra).all()
+    # the same row without the outlier's super-block: super-block 1 alone
+    X1 = X.copy()
+    X1[:, :256] = 0.0
+    Y1 = _run(gq, 12, W, rows, cols, X1)
+    ref1, S1 = oracle.matmul(12, W, rows, cols, X1, nthreads=oracle_threads())
+    assert_within_tolerance(Y1, ref1, S1, "outlier's other super-block")
