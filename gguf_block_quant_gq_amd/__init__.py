@@ -24,7 +24,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libgq.so")
+# GQ_LIBRARY names another build of the same library (the sanitizer build
+# that tests/sanitize.py loads); by default the in-tree one.
+LIB_PATH = os.environ.get("GQ_LIBRARY") or os.path.join(HERE, "libgq.so")
 
 FMT_Q8_0 = 8
 FMT_Q4_K = 12

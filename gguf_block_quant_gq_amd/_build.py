@@ -29,6 +29,17 @@ CFLAGS = [
 ]
 
 
+# The sanitizer build (host code only: the GPU code is unchanged) goes to
+# _build/gq-san/libgq.so; tests/sanitize.py loads it in a process that has the
+# clang address-sanitizer runtime preloaded.
+SAN_OBJ = os.path.join(ROOT, "_build", "gq-san")
+SAN_LIB = os.path.join(SAN_OBJ, "libgq.so")
+SAN_FLAGS = [
+    "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
 def _stale(src: str, obj: str) -> bool:
     """True when obj is missing or older than src or any header under csrc/."""
     if not os.path.exists(obj):
@@ -38,11 +49,11 @@ def _stale(src: str, obj: str) -> bool:
     return any(os.path.getmtime(d) > t for d in deps if os.path.exists(d))
 
 
-def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+def _compile(src: str, verbose: bool, incremental: bool = False, sanitize: bool = False) -> str:
+    obj = os.path.join(SAN_OBJ if sanitize else OBJ, os.path.basename(src) + ".o")
     if incremental and not _stale(src, obj):
         return obj
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *(SAN_FLAGS if sanitize else []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,22 +66,25 @@ def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
     return obj
 
 
-def build(verbose: bool = False, incremental: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False, sanitize: bool = False) -> str:
     """Compile every HIP source and link libgq.so. With incremental=True,
-    objects newer than their source and every header are reused."""
-    os.makedirs(OBJ, exist_ok=True)
+    objects newer than their source and every header are reused. With
+    sanitize=True the host code is built with address and undefined-behaviour
+    sanitizers into SAN_LIB (the in-tree library is left alone)."""
+    out_dir, lib = (SAN_OBJ, SAN_LIB) if sanitize else (OBJ, LIB)
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, incremental), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, incremental, sanitize), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
     import sys
-    print(build(verbose=True, incremental="--incremental" in sys.argv))
+    print(build(verbose=True, incremental="--incremental" in sys.argv, sanitize="--sanitize" in sys.argv))

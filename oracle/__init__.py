@@ -22,7 +22,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gq_oracle.c")
-_LIB = os.path.join(_HERE, "libgq_oracle.so")
+# GQ_SANITIZE=1 (set by tests/sanitize.py) selects a build with the clang
+# address and undefined-behaviour sanitizers, loaded into a process that has
+# their runtime preloaded.
+_SANITIZE = os.environ.get("GQ_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "libgq_oracle_san.so" if _SANITIZE else "libgq_oracle.so")
 
 TYPE_Q8_0 = 8
 TYPE_Q4_K = 12
@@ -39,6 +43,12 @@ def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
            "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC,
            "-lm", "-lpthread"]
+    if _SANITIZE:
+        cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-ffp-contract=off",
+               "-fno-fast-math", "-fsanitize=address", "-fsanitize=undefined",
+               "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-shared-libsan",
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC,
+               "-lm", "-lpthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
