@@ -34,6 +34,7 @@ TYPE_Q5_0 = 6
 TYPE_Q5_K = 13
 TYPE_Q6_K = 14
 TYPE_Q8_0_SPLIT = 1008
+TYPE_Q8_1 = 9  # activation blocks only
 
 _lib = None
 
@@ -84,6 +85,10 @@ def _load():
     lib.gqo_quantize_q8_0.restype = i32
     lib.gqo_quantize_q4_k.argtypes = [vp, i64, i64, vp]
     lib.gqo_quantize_q4_k.restype = i32
+    lib.gqo_quantize_q8_1.argtypes = [vp, i64, i64, vp]
+    lib.gqo_quantize_q8_1.restype = i32
+    lib.gqo_dequant_q8_1.argtypes = [vp, i64, i64, vp]
+    lib.gqo_dequant_q8_1.restype = i32
     _lib = lib
     return lib
 
@@ -234,3 +239,34 @@ def q8_0_split_repack(W, rows: int, cols: int) -> np.ndarray:
     _check(_load().gqo_q8_0_split_repack(_ptr(Wb), rows, cols, _ptr(out)), "q8_0_split_repack")
     return out
 
+
+
+def quantize_q8_1(X, cols: int | None = None) -> np.ndarray:
+    """Activations [n, cols] (or one row) -> Q8_1 blocks, n rows of
+    row_bytes(TYPE_Q8_1, cols) bytes: the int8-activation path's input
+    (the Loom porting skill, "What the starter generates": llama.cpp's Q8_1
+    numerics; the reading is spelled out in gq_oracle.c)."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if X.ndim == 1:
+        X = X.reshape(1, -1)
+    n, c = X.shape
+    out = np.empty(n * row_bytes(TYPE_Q8_1, c), np.uint8)
+    _check(_load().gqo_quantize_q8_1(_ptr(X), n, c, _ptr(out)), "quantize_q8_1")
+    return out
+
+
+def dequant_q8_1(xq, n: int, cols: int) -> np.ndarray:
+    """The values x^ = fp16 d * q that the int8 path multiplies, [n, cols]."""
+    xb = _as_bytes(xq)
+    if xb.size < n * row_bytes(TYPE_Q8_1, cols):
+        raise ValueError("xq holds fewer bytes than n * row_bytes")
+    out = np.empty((n, cols), np.float32)
+    _check(_load().gqo_dequant_q8_1(_ptr(xb), n, cols, _ptr(out)), "dequant_q8_1")
+    return out
+
+
+def matvec_q8_1(fmt: int, W, rows: int, cols: int, xq, nthreads: int = 1):
+    """y = W x^ with x^ the dequantised Q8_1 activation row (f64, with
+    S = sum |w x^|): the definition the int8-activation matvec is held to."""
+    xh = dequant_q8_1(xq, 1, cols)[0]
+    return matvec(fmt, W, rows, cols, xh, nthreads=nthreads)

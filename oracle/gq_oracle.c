@@ -69,6 +69,8 @@ enum {
     O_Q5_K_BYTES = 176,
     O_Q6_K_WEIGHTS = 256,
     O_Q6_K_BYTES = 210,
+    O_Q8_1_VALUES = 32,
+    O_Q8_1_BYTES = 36,
 };
 
 /* Weights and bytes of one block of `type`; 0 for an unknown type. */
@@ -86,6 +88,7 @@ static int block_shape(int type, int* bytes)
     case GQO_TYPE_Q5_0: *bytes = O_Q5_0_BYTES; return O_Q5_0_WEIGHTS;
     case GQO_TYPE_Q5_K: *bytes = O_Q5_K_BYTES; return O_Q5_K_WEIGHTS;
     case GQO_TYPE_Q6_K: *bytes = O_Q6_K_BYTES; return O_Q6_K_WEIGHTS;
+    case GQO_TYPE_Q8_1: *bytes = O_Q8_1_BYTES; return O_Q8_1_VALUES;
     default: *bytes = 0; return 0;
     }
 }
@@ -353,7 +356,7 @@ static int dequant_row(int type, const uint8_t* row, int64_t cols, float* out)
 int gqo_dequant(int type, const void* W, int64_t rows, int64_t cols, float* out)
 {
     int64_t rb = gqo_row_bytes(type, cols);
-    if (rb < 0 || rows < 0 || cols <= 0 || !W || !out)
+    if (rb < 0 || type == GQO_TYPE_Q8_1 || rows < 0 || cols <= 0 || !W || !out)
         return -1;
     const uint8_t* base = (const uint8_t*)W;
     for (int64_t r = 0; r < rows; r++)
@@ -409,7 +412,7 @@ int gqo_matmul(int type, const void* W, int64_t rows, int64_t cols,
                const float* X, int64_t M, double* Y, double* S, int nthreads)
 {
     int64_t rb = gqo_row_bytes(type, cols);
-    if (rb < 0 || rows < 0 || cols <= 0 || M < 0 || !W || !X || !Y)
+    if (rb < 0 || type == GQO_TYPE_Q8_1 || rows < 0 || cols <= 0 || M < 0 || !W || !X || !Y)
         return -1;
     if (nthreads < 1)
         nthreads = 1;
@@ -608,6 +611,77 @@ int gqo_quantize_q4_k(const float* w, int64_t rows, int64_t cols, uint8_t* out)
             for (int g = 0; g < 4; g++)
                 for (int l = 0; l < 32; l++)
                     qs[32 * g + l] = (uint8_t)(codes[64 * g + l] | (codes[64 * g + 32 + l] << 4));
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------- Q8_1 activation blocks */
+
+/* The int8-activation decode path of the Loom porting skill ("What the
+ * starter generates", the gen_llm.py row: activations quantised in
+ * llama.cpp's Q8_1 numerics, multiplied with integer dot products). The page
+ * names the numerics without printing them; the public Q8_1 block is the
+ * reading taken, restated here as this file implements it. Per 32 values
+ * (columns >= cols count as 0):
+ *   amax = max |x|            (binary32)
+ *   d    = amax / 127         (binary32 division, to nearest)
+ *   id   = d != 0 ? 1 / d : 0 (binary32 division, to nearest)
+ *   q_i  = roundf(x_i * id)   (binary32 product, then to nearest with ties
+ *                              away from zero; |q_i| <= 127)
+ *   bytes 0-1: fp16(d), 2-3: fp16(d * sum q_i) (binary32 product, then
+ *   binary16, both to nearest even), 4..35: q_0..q_31 (int8).
+ * The values the product then uses are x^_i = f32(fp16(d)) * q_i (exact). */
+int gqo_quantize_q8_1(const float* x, int64_t n, int64_t cols, uint8_t* out)
+{
+    int64_t rb = gqo_row_bytes(GQO_TYPE_Q8_1, cols);
+    if (n < 0 || cols <= 0 || !x || !out)
+        return -1;
+    int64_t nb = rb / O_Q8_1_BYTES;
+    for (int64_t r = 0; r < n; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            uint8_t* blk = out + r * rb + b * O_Q8_1_BYTES;
+            float v[O_Q8_1_VALUES];
+            float amax = 0.0f;
+            for (int i = 0; i < O_Q8_1_VALUES; i++) {
+                int64_t c = b * O_Q8_1_VALUES + i;
+                v[i] = c < cols ? x[r * cols + c] : 0.0f;
+                if (fabsf(v[i]) > amax)
+                    amax = fabsf(v[i]);
+            }
+            float d = amax / 127.0f;
+            float id = d != 0.0f ? 1.0f / d : 0.0f;
+            int sum = 0;
+            for (int i = 0; i < O_Q8_1_VALUES; i++) {
+                float p = v[i] * id;
+                int q = (int)roundf(p);
+                blk[4 + i] = (uint8_t)(int8_t)q;
+                sum += q;
+            }
+            float ds = (float)sum * d;
+            uint16_t d16 = gqo_f32_to_f16_rne(d);
+            uint16_t s16 = gqo_f32_to_f16_rne(ds);
+            blk[0] = (uint8_t)(d16 & 0xFF);
+            blk[1] = (uint8_t)(d16 >> 8);
+            blk[2] = (uint8_t)(s16 & 0xFF);
+            blk[3] = (uint8_t)(s16 >> 8);
+        }
+    }
+    return 0;
+}
+
+/* out[r*cols + c] = x^ of column c: f32(fp16(d)) * q (exact in binary32:
+ * 11 significant bits times 8). */
+int gqo_dequant_q8_1(const uint8_t* xq, int64_t n, int64_t cols, float* out)
+{
+    int64_t rb = gqo_row_bytes(GQO_TYPE_Q8_1, cols);
+    if (n < 0 || cols <= 0 || !xq || !out)
+        return -1;
+    for (int64_t r = 0; r < n; r++) {
+        for (int64_t c = 0; c < cols; c++) {
+            const uint8_t* blk = xq + r * rb + (c / O_Q8_1_VALUES) * O_Q8_1_BYTES;
+            float d = gqo_f16_to_f32(read_u16le(blk));
+            out[r * cols + c] = d * (float)(int8_t)blk[4 + c % O_Q8_1_VALUES];
         }
     }
     return 0;

@@ -40,6 +40,9 @@ extern "C" {
 #define GQO_TYPE_Q5_0 6
 #define GQO_TYPE_Q5_K 13
 #define GQO_TYPE_Q6_K 14
+/* Q8_1 activation blocks (36 bytes per 32 values: fp16 d, fp16 d * sum q,
+ * 32 int8 q): only as an activation format, never as weights. */
+#define GQO_TYPE_Q8_1 9
 /* Q8_0 repacked into the split per-row layout (not a ggml id): per row the
  * nb fp16 scales, zero padding to a multiple of 16 bytes, then the nb * 32
  * int8 codes in block order. */
@@ -76,6 +79,12 @@ int gqo_matmul(int type, const void* W, int64_t rows, int64_t cols,
 /* Repack rows of Q8_0 blocks into the split per-row layout (row stride
  * gqo_row_bytes(GQO_TYPE_Q8_0_SPLIT, cols)); padding bytes are zero. */
 int gqo_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out);
+
+/* Activations (n rows of cols) -> Q8_1 blocks, row stride
+ * gqo_row_bytes(GQO_TYPE_Q8_1, cols); the numerics are spelled out in the .c
+ * file. And back: the values x^ = fp16 d * q that the int8 path multiplies. */
+int gqo_quantize_q8_1(const float* x, int64_t n, int64_t cols, uint8_t* out);
+int gqo_dequant_q8_1(const uint8_t* xq, int64_t n, int64_t cols, float* out);
 
 /* Test-only reference quantisers (the pages print none for Q4_K). */
 int gqo_quantize_q8_0(const float* w, int64_t rows, int64_t cols, uint8_t* out);
