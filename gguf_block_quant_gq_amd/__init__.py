@@ -13,6 +13,8 @@ is no CPU fallback: if the library is not built, loading raises.
     gq_matvec_experts(fmt, W, n_expert, rows, cols, X, xk, expid, Y=None)
                                                        -> Y[a] = W[expid[a]] X[a // xk]
     gq_matmul(fmt, W, rows, cols, X, Y=None)           -> Y [M, rows] fp32
+    gq_quantize_q8_1(X, n, cols, out=None)             -> Q8_1 activation blocks
+    gq_matvec_q8_1(fmt, W, rows, cols, xq, y=None)     -> y = W x^ (int8 activations)
 
 W is a uint8 CUDA tensor holding rows * gq_row_bytes(fmt, cols) bytes of
 GGUF blocks; fmt is FMT_Q8_0 (8), FMT_Q4_K (12), FMT_Q5_0 (6), FMT_Q5_K (13)
@@ -34,6 +36,7 @@ FMT_Q5_0 = 6
 FMT_Q5_K = 13
 FMT_Q6_K = 14
 FMT_Q8_0_SPLIT = 1008  # Q8_0 repacked by gq_q8_0_split_repack (scales apart from codes)
+GQ_FMT_Q8_1 = 9        # activation blocks of the int8 path (gq_quantize_q8_1), never weights
 
 GQ_OK = 0
 GQ_ERR_NULL = 1
@@ -45,7 +48,7 @@ GQ_ERR_OVERLAP = 6
 
 EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matvec_acc",
            "gq_matvec_swiglu", "gq_matvec_experts", "gq_matvec_batch", "gq_q8_0_split_repack",
-           "gq_matmul", "gq_matmul_experts")
+           "gq_matmul", "gq_matmul_experts", "gq_quantize_q8_1", "gq_matvec_q8_1")
 
 _lib = None
 
@@ -84,6 +87,10 @@ def load_library():
     for name in ("gq_matmul", "gq_matvec_batch"):
         getattr(lib, name).argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
         getattr(lib, name).restype = i32
+    lib.gq_quantize_q8_1.argtypes = [vp, i64, i64, vp, vp]
+    lib.gq_quantize_q8_1.restype = i32
+    lib.gq_matvec_q8_1.argtypes = [i32, vp, i64, i64, vp, vp, vp]
+    lib.gq_matvec_q8_1.restype = i32
     _lib = lib
     return lib
 
@@ -167,6 +174,45 @@ def _matvec(name: str, fmt: int, W, rows: int, cols: int, x, y, stream, wrows: i
 def gq_matvec(fmt: int, W, rows: int, cols: int, x, y=None, stream=None):
     """y = W x on `stream` (default: torch's current stream), asynchronous."""
     return _matvec("gq_matvec", fmt, W, rows, cols, x, y, stream, rows)
+
+
+def gq_quantize_q8_1(X, n: int, cols: int, out=None, stream=None):
+    """n rows of cols fp32 activations -> Q8_1 blocks (uint8, n *
+    gq_row_bytes(GQ_FMT_Q8_1, cols) bytes), asynchronous."""
+    torch = _torch()
+    _check_dev(X, "X", torch.float32)
+    if X.numel() < n * cols:
+        raise ValueError("X is too small")
+    need = n * gq_row_bytes(GQ_FMT_Q8_1, cols)
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _check_dev(out, "out", torch.uint8)
+    if out.numel() < need:
+        raise ValueError("out is too small")
+    st = load_library().gq_quantize_q8_1(_ptr(X), int(n), int(cols), _ptr(out), _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_quantize_q8_1")
+    return out
+
+
+def gq_matvec_q8_1(fmt: int, W, rows: int, cols: int, xq, y=None, stream=None):
+    """y = W x^ with xq one quantised activation row (gq_quantize_q8_1),
+    integer dot products, asynchronous."""
+    torch = _torch()
+    _check_w(fmt, W, rows, cols)
+    _check_dev(xq, "xq", torch.uint8)
+    if xq.numel() < gq_row_bytes(GQ_FMT_Q8_1, cols):
+        raise ValueError("xq is too small")
+    if y is None:
+        y = torch.empty(rows, dtype=torch.float32, device=W.device)
+    _check_dev(y, "y", torch.float32)
+    if y.numel() < rows:
+        raise ValueError("y is too small")
+    st = load_library().gq_matvec_q8_1(int(fmt), _ptr(W), int(rows), int(cols), _ptr(xq), _ptr(y),
+                                       _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_matvec_q8_1")
+    return y
 
 
 def gq_matvec_acc(fmt: int, W, rows: int, cols: int, x, y, stream=None):

@@ -42,7 +42,7 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 // Shape and format checks shared by every entry point. On success *rb is
 // the row stride in bytes and *wbytes the size of W.
 int check_shape(int fmt, int64_t rows, int64_t cols, int64_t M, int64_t* rb, int64_t* wbytes) {
-  if (gq_row_bytes(fmt, 1) < 0) return GQ_ERR_FMT;
+  if (gq_row_bytes(fmt, 1) < 0 || fmt == GQ_FMT_Q8_1) return GQ_ERR_FMT;  // Q8_1: activations only
   if (rows < 0 || cols <= 0 || M < 0) return GQ_ERR_SHAPE;
   if (rows > INT_MAX || cols > INT_MAX || M > INT_MAX) return GQ_ERR_SHAPE;
   *rb = gq_row_bytes(fmt, cols);
@@ -101,6 +101,7 @@ extern "C" int64_t gq_row_bytes(int fmt, int64_t cols) {
       const int64_t nb = (cols + 31) / 32;
       return ((2 * nb + 15) / 16) * 16 + 32 * nb;
     }
+    case GQ_FMT_Q8_1: return ((cols + 31) / 32) * 36;
     default: return -1;
   }
 }
@@ -381,4 +382,37 @@ extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64
     m0 += m;
   }
   return GQ_OK;
+}
+
+extern "C" int gq_quantize_q8_1(const float* x, int64_t n, int64_t cols, void* xq, void* stream) {
+  if (n < 0 || cols <= 0 || n > INT_MAX || cols > INT_MAX) return GQ_ERR_SHAPE;
+  const int64_t rb = gq_row_bytes(GQ_FMT_Q8_1, cols);
+  if (n > 0 && (rb > INT64_MAX / n || cols > INT64_MAX / 4 / n || n * ((cols + 31) / 32) > INT64_MAX / 8))
+    return GQ_ERR_SHAPE;
+  if (n == 0) return GQ_OK;
+  if (!x || !xq) return GQ_ERR_NULL;
+  if ((uintptr_t)x % 4 || (uintptr_t)xq % 4) return GQ_ERR_ALIGN;
+  if (overlaps(xq, n * rb, x, n * cols * 4)) return GQ_ERR_OVERLAP;
+  (void)hipGetLastError();
+  return finish(gq::launch_quantize_q8_1(x, n, (int)cols, (uint8_t*)xq, (hipStream_t)stream));
+}
+
+extern "C" int gq_matvec_q8_1(int fmt, const void* W, int64_t rows, int64_t cols, const void* xq, float* y,
+                              void* stream) {
+  int64_t rb = 0, wbytes = 0;
+  int st = check_shape(fmt, rows, cols, 1, &rb, &wbytes);
+  if (st != GQ_OK) return st;
+  if (fmt != GQ_FMT_Q8_0 && fmt != GQ_FMT_Q4_K) return GQ_ERR_FMT;
+  if (cols > 131072) return GQ_ERR_SHAPE;  // the quantised row is staged in LDS
+  if (rows == 0) return GQ_OK;
+  if (!W || !xq || !y) return GQ_ERR_NULL;
+  if ((st = check_align(fmt, W)) != GQ_OK) return st;
+  if ((uintptr_t)xq % 4 || (uintptr_t)y % 4) return GQ_ERR_ALIGN;
+  if (overlaps(y, rows * 4, W, wbytes) || overlaps(y, rows * 4, xq, gq_row_bytes(GQ_FMT_Q8_1, cols)))
+    return GQ_ERR_OVERLAP;
+  const int cus = current_cus();
+  if (cus <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  return finish(gq::launch_gemv_q8a(fmt, (const uint8_t*)W, rb, (int)rows, (int)cols, (const uint8_t*)xq, y, cus,
+                                    (hipStream_t)stream));
 }

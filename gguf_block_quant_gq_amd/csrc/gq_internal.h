@@ -87,6 +87,12 @@ hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
 bool gemm_q4k_fits(int64_t rows, int64_t cols, int64_t row_bytes);
 hipError_t launch_gemm_q4k(const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
                            int n_groups, int64_t group_w_bytes, int cus, hipStream_t s);
+// The int8-activation path (gemv_q8a.hip): Q8_1 quantisation of n rows of
+// activations, and y = W x^ for Q8_0 / Q4_K weights with integer dots.
+hipError_t launch_quantize_q8_1(const float* x, int64_t n, int cols, uint8_t* out, hipStream_t s);
+hipError_t launch_gemv_q8a(int fmt, const uint8_t* W, int64_t row_bytes, int rows, int cols,
+                           const uint8_t* xq, float* y, int cus, hipStream_t s);
+
 // The fp32 matrix-core product (gemm_f32.hip): Q8_0, Q8_0 split, Q5_0, Q5_K,
 // Q6_K, and Q4_K rows whose length is not a multiple of 4.
 hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s);

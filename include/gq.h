@@ -88,6 +88,8 @@ enum gq_fmt {
     GQ_FMT_Q5_K = 13,
     GQ_FMT_Q6_K = 14,
     GQ_FMT_Q8_0_SPLIT = 1008, /* Q8_0 in the split per-row layout (not a ggml id) */
+    GQ_FMT_Q8_1 = 9,          /* activation blocks of the int8 path only (see
+                                 gq_quantize_q8_1); never a weight format */
 };
 
 enum gq_status {
@@ -266,6 +268,39 @@ int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
  */
 int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, int64_t cols,
                       const float* X, const int64_t* m_per_expert, float* Y, void* stream);
+
+/*
+ * The int8-activation decode path (the Loom porting skill, "What the starter
+ * generates": decode-shaped linears with activations in llama.cpp's Q8_1
+ * numerics and 4-way integer dot products, an fp32-activation switch kept
+ * beside them). The page names the numerics without printing them; the
+ * reading taken is the public Q8_1 block.
+ *
+ * gq_quantize_q8_1: n rows of cols fp32 activations (x, [n, cols] row-major,
+ * 4-byte aligned) -> n rows of gq_row_bytes(GQ_FMT_Q8_1, cols) =
+ * 36 * ceil(cols / 32) bytes at xq (4-byte aligned, must not overlap x). Per
+ * 32 values (columns >= cols count as 0): d = amax / 127 (fp32, to nearest),
+ * id = d != 0 ? 1 / d : 0, q_i = round-half-away-from-zero(x_i * id) (fp32
+ * product, |q_i| <= 127); bytes 0-1 fp16(d), 2-3 fp16(d * sum q_i), 4..35 the
+ * int8 q_i. Byte-identical to the CPU oracle's quantiser. n == 0 is a no-op.
+ * Asynchronous on `stream`.
+ */
+int gq_quantize_q8_1(const float* x, int64_t n, int64_t cols, void* xq, void* stream);
+
+/*
+ * y[r] = sum_c w(r, c) * x^_c for r < rows, with x^_c = fp16(d) * q_c the
+ * values of one quantised activation row xq (gq_quantize_q8_1 of a cols-wide
+ * row, 4-byte aligned); y is overwritten. fmt: GQ_FMT_Q8_0 or GQ_FMT_Q4_K
+ * (others: GQ_ERR_FMT), W as for gq_matvec. Integer dot products per 32
+ * weights (exact int32), scales applied in fp32: the result is within
+ * 2e-4 * sum_c |w(r,c) * x^_c| of the exact W x^ (the gq_matvec rule with x^
+ * in place of x); against the fp32 activations themselves it differs by the
+ * quantisation of x, |x_c - x^_c| <= d/2 + 127 |d - fp16(d)| per value
+ * (d of the value's 32-block). cols may be at most 131072 (the quantised row
+ * is staged in LDS): GQ_ERR_SHAPE beyond. Asynchronous on `stream`.
+ */
+int gq_matvec_q8_1(int fmt, const void* W, int64_t rows, int64_t cols, const void* xq, float* y,
+                   void* stream);
 
 #ifdef __cplusplus
 }

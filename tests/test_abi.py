@@ -230,3 +230,42 @@ def test_split_layout_row_bytes_and_repack_validation(lib, oracle):
     assert rp(W_OK, 4, 896, W_OK + 8, None) == gq.GQ_ERR_OVERLAP
     # the split layout needs 4-byte aligned W in every entry point
     assert _mv(lib, fmt=1008, W=W_OK + 2) == gq.GQ_ERR_ALIGN
+
+
+def _q81(lib, x=X_OK, n=2, cols=256, xq=Y_OK):
+    return lib.gq_quantize_q8_1(x, n, cols, xq, None)
+
+
+def _mvq(lib, fmt=12, W=W_OK, rows=4, cols=256, xq=X_OK, y=Y_OK):
+    return lib.gq_matvec_q8_1(fmt, W, rows, cols, xq, y, None)
+
+
+def test_validation_int8_activation_path(lib):
+    assert lib.gq_row_bytes(gq.GQ_FMT_Q8_1, 33) == 72
+    # Q8_1 is an activation format: no weight entry point takes it
+    assert _mv(lib, fmt=gq.GQ_FMT_Q8_1) == gq.GQ_ERR_FMT
+    assert _mm(lib, fmt=gq.GQ_FMT_Q8_1) == gq.GQ_ERR_FMT
+    assert _dq(lib, fmt=gq.GQ_FMT_Q8_1) == gq.GQ_ERR_FMT
+    assert _mvq(lib, fmt=gq.GQ_FMT_Q8_1) == gq.GQ_ERR_FMT
+    for fmt in (6, 13, 14, 1008, 0):   # formats without an integer-dot kernel
+        assert _mvq(lib, fmt=fmt) == gq.GQ_ERR_FMT
+    assert _mvq(lib, cols=0) == gq.GQ_ERR_SHAPE
+    assert _mvq(lib, rows=-1) == gq.GQ_ERR_SHAPE
+    assert _mvq(lib, cols=131072 + 256) == gq.GQ_ERR_SHAPE    # the row is staged in LDS
+    assert _mvq(lib, rows=0, W=None, xq=None, y=None) == gq.GQ_OK
+    assert _mvq(lib, W=None) == gq.GQ_ERR_NULL
+    assert _mvq(lib, xq=None) == gq.GQ_ERR_NULL
+    assert _mvq(lib, y=None) == gq.GQ_ERR_NULL
+    assert _mvq(lib, W=W_OK + 2) == gq.GQ_ERR_ALIGN
+    assert _mvq(lib, xq=X_OK + 2) == gq.GQ_ERR_ALIGN
+    assert _mvq(lib, y=Y_OK + 2) == gq.GQ_ERR_ALIGN
+    assert _mvq(lib, y=X_OK + 4) == gq.GQ_ERR_OVERLAP        # y over the quantised row
+    assert _mvq(lib, y=W_OK + 100) == gq.GQ_ERR_OVERLAP      # y over W
+    assert _q81(lib, n=-1) == gq.GQ_ERR_SHAPE
+    assert _q81(lib, cols=0) == gq.GQ_ERR_SHAPE
+    assert _q81(lib, n=0, x=None, xq=None) == gq.GQ_OK
+    assert _q81(lib, x=None) == gq.GQ_ERR_NULL
+    assert _q81(lib, xq=None) == gq.GQ_ERR_NULL
+    assert _q81(lib, x=X_OK + 2) == gq.GQ_ERR_ALIGN
+    assert _q81(lib, xq=Y_OK + 1) == gq.GQ_ERR_ALIGN
+    assert _q81(lib, xq=X_OK + 1024) == gq.GQ_ERR_OVERLAP    # output over the second row of x
