@@ -12,10 +12,20 @@ value = algorithmic bytes per step (packed W + x + y of every call) / time,
 in GB/s. The JSON line also carries:
   roofline      the dominant kernel (the Q4_K GEMV instance of the K = 4096
                 projections) timed alone with HIP events on its stream;
-  cpu_baseline  the C oracle on the host cores over a bounded sample;
+  per_projection, int8_activation_step_variant, fused_step_variant
+                the step's parts and variants (us per call as the median of
+                5 timed loops, with mean and minimum);
+  prefill_q4_k_llama3_8b
+                the Llama-3-8B prefill products (M = 2..512): us, TFLOP/s,
+                % of the fp16 matrix peak and % of the HBM peak;
+  cpu_baseline  the C oracle on the host cores over a bounded sample, on N
+                threads and on one, with the CPU model, the oracle's time per
+                call of every config, and the GPU's largest relative error
+                against the oracle on every config;
   workloads     the other shapes: Q8_0 lm_head (cold), the Qwen2.5-0.5B and
-                SmolLM-135M decode shapes, the prefill GEMM TFLOP/s at
-                M = 16/64/512 and gq_dequant.
+                SmolLM-135M decode shapes (cold over > 512 MB of rotating
+                copies, and warm), the mixed formats, MoE, the prefill GEMMs
+                and gq_dequant.
 """
 from __future__ import annotations
 
@@ -60,6 +70,21 @@ class Timer:
         e.record()
         torch.cuda.synchronize()
         return s.elapsed_time(e) / iters  # ms per fn()
+
+    def stats(self, fn, iters: int, reps: int = 5, warmup: int = 1):
+        """(mean, median, min) ms per fn() over `reps` event-timed loops of
+        `iters` calls each."""
+        per = [self.time(fn, iters, warmup=warmup if r == 0 else 0) for r in range(reps)]
+        return float(np.mean(per)), float(np.median(per)), float(np.min(per))
+
+
+def rate_row(nbytes: int, calls: int, st) -> dict:
+    """us per call (mean / median / min over the timed loops), GB/s and % of
+    the HBM peak at the median."""
+    mean, med, mn = (v * 1e3 / calls for v in st)
+    gbps = nbytes / (med * 1e-6) / 1e9
+    return dict(us_per_call=round(med, 3), us_mean=round(mean, 3), us_min=round(mn, 3),
+                GBps=round(gbps, 1), pct_hbm=round(100 * gbps / HBM_PEAK_GBS, 2))
 
 
 def capture(torch, fn):
@@ -161,7 +186,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--prefill-probe", action="store_true",
                     help="run each prefill product twice (M from --prefill-probe-m; for counter runs) and exit")
     ap.add_argument("--prefill-probe-m", default="512",
@@ -224,6 +249,8 @@ def main() -> int:
 
     graph = capture(torch, step)
     ms_graph = timer.time(graph.replay, args.steps, warmup=args.warmup)
+    # spread of single steps (each replay timed alone), beside the K-step mean
+    one = [timer.time(graph.replay, 1, warmup=0) for _ in range(max(5, args.steps // 2))]
     ms_eager = timer.time(step, max(5, args.steps // 5), warmup=2)
     value = total_bytes / (ms_graph * 1e-3) / 1e9
     log(f"decode step: {ms_graph * 1e3:.1f} us (graph), {ms_eager * 1e3:.1f} us (eager); "
@@ -234,11 +261,8 @@ def main() -> int:
     for proj in range(7):
         sub = [m for m in mats if m["name"] == synth.LLAMA3_8B_LAYER[proj][0]]
         g = capture(torch, lambda sub=sub: step(sub))
-        ms = timer.time(g.replay, max(5, args.steps // 5), warmup=2)
-        b = sum(m["bytes"] for m in sub)
-        per_proj[sub[0]["name"]] = dict(us_per_call=round(ms * 1e3 / len(sub), 3),
-                                        GBps=round(b / (ms * 1e-3) / 1e9, 1),
-                                        pct_hbm=round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1))
+        st = timer.stats(g.replay, max(2, args.steps // 10), reps=5, warmup=2)
+        per_proj[sub[0]["name"]] = rate_row(sum(m["bytes"] for m in sub) // len(sub), len(sub), st)
     log(f"per projection: {per_proj}")
 
     # --------------------------------- roofline: the dominant GEMV kernel
@@ -259,6 +283,7 @@ def main() -> int:
     log(f"roofline: {roofline}")
 
     fused = fused_step_variant(torch, gq, lib, synth, mats, timer, stream_ptr, args)
+    int8 = int8_step_variant(torch, gq, lib, synth, mats, timer, stream_ptr, args)
 
     extras = {}
     if not args.no_extras:
@@ -268,8 +293,13 @@ def main() -> int:
     # ------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(synth, args.cpu_seconds)
+        gpu = gpu_config_outputs(torch, gq, synth)
+        cpu = cpu_baseline(synth, args.cpu_seconds, gpu)
         log(f"cpu baseline: {cpu}")
+
+    # config 4 (the Llama-3-8B prefill products) at the top level
+    config4 = {k[len("matmul_"):]: v for k, v in extras.items()
+               if k.startswith("matmul_gate_M") or k.startswith("matmul_down_M")}
 
     line = {
         "metric": "Q4_K/Q8_0 GEMV weight GB/s & % of 8 TB/s HBM peak; prefill GEMM TFLOP/s",
@@ -295,11 +325,16 @@ def main() -> int:
             "launch": "hipGraph replay of 224 gq_matvec launches on one stream",
             "eager_ms_per_step": round(ms_eager, 4),
             "eager_GBps": round(total_bytes / (ms_eager * 1e-3) / 1e9, 1),
+            "step_us_median": round(float(np.median(one)) * 1e3, 1),
+            "step_us_min": round(float(np.min(one)) * 1e3, 1),
+            "seed": 3,
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "per_projection": per_proj,
         "fused_step_variant": fused,
+        "int8_activation_step_variant": int8,
         "roofline": roofline,
+        "prefill_q4_k_llama3_8b": config4,
         "cpu_baseline": cpu,
         "workloads": extras,
     }
@@ -363,6 +398,58 @@ def fused_step_variant(torch, gq, lib, synth, mats, timer, stream_ptr, args):
     return out
 
 
+def int8_step_variant(torch, gq, lib, synth, mats, timer, stream_ptr, args):
+    """The same 224 matrices with int8 activations (gq_matvec_q8_1 on each
+    matrix's Q8_1-quantised x, quantised beforehand): the step, each
+    projection, and the quantiser's cost per call (one activation row)."""
+    xq = []
+    for m in mats:
+        q = gq.gq_quantize_q8_1(m["x"], 1, m["cols"])
+        xq.append(q)
+    torch.cuda.synchronize()
+
+    def step(idx):
+        sp = stream_ptr()
+        for i in idx:
+            m = mats[i]
+            st = lib.gq_matvec_q8_1(gq.FMT_Q4_K, m["W"].data_ptr(), m["rows"], m["cols"],
+                                    xq[i].data_ptr(), m["y"].data_ptr(), sp)
+            if st != 0:
+                raise gq.GQError(st, "gq_matvec_q8_1")
+
+    every = list(range(len(mats)))
+    g = capture(torch, lambda: step(every))
+    st = timer.stats(g.replay, max(2, args.steps // 10), reps=5, warmup=2)
+    wbytes = sum(m["rows"] * gq.gq_row_bytes(12, m["cols"]) + 36 * (m["cols"] // 32) + 4 * m["rows"]
+                 for m in mats)
+    out = dict(launch="hipGraph replay of 224 gq_matvec_q8_1 launches (activations quantised beforehand)",
+               bytes_per_step=int(wbytes), step=rate_row(wbytes, 1, st))
+    per = {}
+    for proj in range(7):
+        idx = [i for i, m in enumerate(mats) if m["name"] == synth.LLAMA3_8B_LAYER[proj][0]]
+        gp = capture(torch, lambda idx=idx: step(idx))
+        stp = timer.stats(gp.replay, max(2, args.steps // 10), reps=5, warmup=2)
+        m = mats[idx[0]]
+        per[m["name"]] = rate_row(m["rows"] * gq.gq_row_bytes(12, m["cols"]) + 36 * (m["cols"] // 32)
+                                  + 4 * m["rows"], len(idx), stp)
+        del gp
+    out["per_projection"] = per
+    x0 = mats[0]["x"]
+    q0 = torch.empty(36 * (x0.numel() // 32), dtype=torch.uint8, device="cuda")
+
+    def quant():
+        sp = stream_ptr()
+        for _ in range(32):
+            lib.gq_quantize_q8_1(x0.data_ptr(), 1, x0.numel(), q0.data_ptr(), sp)
+
+    gq_ = capture(torch, quant)
+    mean, med, mn = timer.stats(gq_.replay, 5, reps=5, warmup=2)
+    out["quantize_4096_us_per_call"] = round(med * 1e3 / 32, 3)
+    log(f"int8 activation step: {out}")
+    del g, gq_
+    return out
+
+
 def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
     out = {}
     iters = max(10, args.steps)
@@ -381,14 +468,26 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
         for c in cs:
             lib.gq_matvec(fmt, c.data_ptr(), rows, cols, xd.data_ptr(), yd.data_ptr(), sp)
 
-    ms_cold = timer.time(lambda: lm(copies), iters, warmup=2) / len(copies)
+    st = timer.stats(lambda: lm(copies), max(2, iters // 5), reps=5, warmup=2)
     ms_warm = timer.time(lambda: lm(copies[:1] * 4), iters, warmup=2) / 4
-    out["qwen05b_lm_head_q8_0"] = dict(
-        shape=[rows, cols], us_per_call=round(ms_cold * 1e3, 2),
-        GBps=round(nbytes / (ms_cold * 1e-3) / 1e9, 1),
-        pct_hbm=round(100 * nbytes / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
-        warm_us_per_call=round(ms_warm * 1e3, 2))
+    out["qwen05b_lm_head_q8_0"] = dict(shape=[rows, cols], seed=2, cold_rotating_copies=len(copies),
+                                       **rate_row(nbytes, len(copies), st),
+                                       warm_us_per_call=round(ms_warm * 1e3, 2))
     log(f"lm_head: {out['qwen05b_lm_head_q8_0']}")
+
+    # the same lm_head with int8 activations (cold, same copies)
+    xq = gq.gq_quantize_q8_1(xd, 1, cols)
+
+    def lm8(cs):
+        sp = stream_ptr()
+        for c in cs:
+            lib.gq_matvec_q8_1(fmt, c.data_ptr(), rows, cols, xq.data_ptr(), yd.data_ptr(), sp)
+
+    st = timer.stats(lambda: lm8(copies), max(2, iters // 5), reps=5, warmup=2)
+    out["qwen05b_lm_head_q8_0_int8_act"] = dict(shape=[rows, cols],
+                                                **rate_row(rows * rb + 36 * (cols // 32) + 4 * rows,
+                                                           len(copies), st))
+    log(f"lm_head int8 activations: {out['qwen05b_lm_head_q8_0_int8_act']}")
 
     # the same lm_head repacked into the split per-row layout (scales apart
     # from the codes), cold over 4 copies like the packed one
@@ -434,7 +533,10 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
                                        pct_hbm=round(100 * dbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1))
     del dq, copies
 
-    # small decode shapes (latency-bound), graph-replayed, warm
+    # configs 0 and 1 (SmolLM-135M ffn_up Q8_0, the Qwen2.5-0.5B decode
+    # shapes Q4_K): cold -- one launch per copy over more than 512 MB of
+    # rotating copies in one graph, so W comes from HBM -- and warm (one copy
+    # replayed 20 times, labelled warm_*)
     small = [("smollm135m_ffn_up_q8_0", synth.SMOLLM_FFN_UP, 0, 0)]
     small += [(f"qwen05b_{r}x{c}_q4_k", (f, r, c), 1, i)
               for i, (f, r, c) in enumerate(synth.QWEN05_DECODE)]
@@ -443,17 +545,31 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
         Wd, xd2 = torch.from_numpy(W).cuda(), torch.from_numpy(x).cuda()
         y2 = torch.empty(r, dtype=torch.float32, device="cuda")
         b = gemv_bytes(gq.gq_row_bytes(f, c), r, c)
+        ncopy = min(8192, -(-(520 << 20) // W.size))
+        big = torch.empty((ncopy, W.size), dtype=torch.uint8, device="cuda")
+        big.copy_(Wd.unsqueeze(0).expand(ncopy, -1))
+        base = big.data_ptr()
+
+        def cold(f=f, r=r, c=c, base=base, n=ncopy, size=W.size, xd2=xd2, y2=y2):
+            sp = stream_ptr()
+            for i in range(n):
+                lib.gq_matvec(f, base + i * size, r, c, xd2.data_ptr(), y2.data_ptr(), sp)
 
         def call(f=f, r=r, c=c, Wd=Wd, xd2=xd2, y2=y2):
             sp = stream_ptr()
             for _ in range(20):
                 lib.gq_matvec(f, Wd.data_ptr(), r, c, xd2.data_ptr(), y2.data_ptr(), sp)
 
+        gc = capture(torch, cold)
+        st = timer.stats(gc.replay, 2, reps=5, warmup=1)
         g = capture(torch, call)
-        ms = timer.time(g.replay, 10, warmup=2) / 20
-        out[name] = dict(us_per_call=round(ms * 1e3, 2),
-                         GBps=round(b / (ms * 1e-3) / 1e9, 1))
-    log(f"small shapes: { {k: v for k, v in out.items() if 'q4_k' in k or 'smollm' in k} }")
+        stw = timer.stats(g.replay, 10, reps=5, warmup=2)
+        warm = rate_row(b, 20, stw)
+        out[name] = dict(shape=[r, c], seed=seed, cold_rotating_copies=ncopy,
+                         cold_bytes=int(ncopy * W.size), **rate_row(b, ncopy, st),
+                         **{f"warm_{k}": v for k, v in warm.items()})
+        del gc, g, big
+    log(f"configs 0 and 1: { {k: v for k, v in out.items() if 'q4_k' in k or 'smollm' in k} }")
 
     # the formats that Q4_K_M / Q5_K_M files mix in (Q6_K lm_head and
     # ffn_down, Q5_K projections, Q5_0 896-wide tensors), cold: enough
@@ -573,13 +689,13 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
 
             # median of three timed loops (a single loop of these short
             # calls is at the mercy of one slow launch)
-            ms = float(np.median([timer.time(mm, 10 if M < 512 else 5, warmup=1) for _ in range(3)]))
+            _, ms, ms_min = timer.stats(mm, 10 if M < 512 else 5, reps=5, warmup=1)
             flops = 2.0 * M * rows * cols
             wb = rows * gq.gq_row_bytes(12, cols) + 4 * M * (rows + cols)
             tf = flops / (ms * 1e-3) / 1e12
             key = f"matmul_{which}_M{M}"
             out[key] = dict(
-                us_per_call=round(ms * 1e3, 1), TFLOPs=round(tf, 2),
+                us_per_call=round(ms * 1e3, 1), us_min=round(ms_min * 1e3, 1), TFLOPs=round(tf, 2),
                 pct_mfma_f16_peak=round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2),
                 GBps=round(wb / (ms * 1e-3) / 1e9, 1),
                 pct_hbm=round(100 * wb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2))
@@ -587,38 +703,137 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
     return out
 
 
-def cpu_baseline(synth, seconds: float):
-    """The C oracle (dequant + f64 dot) on the host cores over the q, k, v,
-    o, gate, up, down matrices of layer 0 of the same decode step, repeated
-    until about `seconds` of wall time; reported as weight GB/s."""
+def gpu_config_outputs(torch, gq, synth):
+    """One gq_matvec / gq_matmul of every config on fresh buffers, copied to
+    the host: the GPU side of the per-config error the CPU leg reports."""
+    out = {}
+
+    def mv(fmt, W, rows, cols, x):
+        return gq.gq_matvec(fmt, torch.from_numpy(W).cuda(), rows, cols, torch.from_numpy(x).cuda())
+
+    f, r, c = synth.SMOLLM_FFN_UP
+    W, x = synth.matrix_and_x(f, r, c, 0, 0)
+    out["config0"] = [(f, W, r, c, x[None, :], mv(f, W, r, c, x))]
+    out["config1"] = []
+    for i, (f, r, c) in enumerate(synth.QWEN05_DECODE):
+        W, x = synth.matrix_and_x(f, r, c, 1, i)
+        out["config1"].append((f, W, r, c, x[None, :], mv(f, W, r, c, x)))
+    f, r, c = synth.QWEN05_LM_HEAD
+    W, x = synth.matrix_and_x(f, r, c, 2, 0)
+    out["config2"] = [(f, W, r, c, x[None, :], mv(f, W, r, c, x))]
+    out["config3"] = []
+    for proj in range(7):
+        name, r, c, _, _ = synth.llama3_8b_matrix(0, proj)
+        W, x = synth.llama3_8b_weight_and_x(0, proj)
+        out["config3"].append((12, W, r, c, x[None, :], mv(12, W, r, c, x)))
+    out["config4"] = []
+    for M in (16, 64):
+        for which in ("gate", "down"):
+            W, X, r, c = synth.prefill_inputs(which, M)
+            Y = gq.gq_matmul(12, torch.from_numpy(W).cuda(), r, c, torch.from_numpy(X).cuda())
+            out["config4"].append((12, W, r, c, X, Y))
+    torch.cuda.synchronize()
+    for k, v in out.items():
+        out[k] = [(f, W, r, c, X, Y.cpu().numpy().reshape(X.shape[0], r)) for f, W, r, c, X, Y in v]
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(synth, seconds: float, gpu=None):
+    """The C oracle (dequant + f64 dot) on the host cores. value: weight GB/s
+    over the q, k, v, o, gate, up, down matrices of layer 0 of the decode step
+    on N threads, repeated for about `seconds`; beside it one pass on one
+    thread, and the oracle's time per call of every config (N threads and one
+    thread; config 3 as 32 x layer 0, config 4 at M = 512 as 8 x M = 64,
+    both marked as scaled), and, with `gpu` (gpu_config_outputs), the largest
+    |y - y_ref| / sum |w x| of the GPU output of each config."""
     import oracle
 
     try:
         threads = len(os.sched_getaffinity(0))
     except AttributeError:
         threads = os.cpu_count() or 1
+    threads = max(1, min(16, threads))  # one GPU's share of the host
     mats = []
     for proj in range(7):
         name, rows, cols, _, _ = synth.llama3_8b_matrix(0, proj)
         W, x = synth.llama3_8b_weight_and_x(0, proj)
         mats.append((rows, cols, W, x))
     per_pass = sum(r * oracle.row_bytes(12, c) + 4 * (r + c) for r, c, _, _ in mats)
+
+    def one_pass(n):
+        for rows, cols, W, x in mats:
+            oracle.matvec(12, W, rows, cols, x, nthreads=n)
+
     done = 0
     passes = 0
     t0 = time.perf_counter()
     while True:
-        for rows, cols, W, x in mats:
-            oracle.matvec(12, W, rows, cols, x, nthreads=threads)
+        one_pass(threads)
         passes += 1
         done += per_pass
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    one_pass(1)
+    dt1 = time.perf_counter() - t1
+
+    def timed(fn, n):
+        t = time.perf_counter()
+        r = fn(n)
+        return (time.perf_counter() - t) * 1e6, r
+
+    per_config = {}
+    errors = {}
+    for key, cases in (gpu or {}).items():
+        rows_out = []
+        worst = 0.0
+        for f, W, r, c, X, Y in cases:
+            M = X.shape[0]
+            t_n, (ref, S) = timed(lambda n: oracle.matmul(f, W, r, c, X, nthreads=n), threads)
+            row = dict(shape=[r, c], M=M, oracle_us_nthreads=round(t_n, 1))
+            if key != "config4":  # the prefill products take seconds on one thread
+                row["oracle_us_1thread"] = round(timed(lambda n: oracle.matmul(f, W, r, c, X, nthreads=n), 1)[0], 1)
+            rows_out.append(row)
+            err = np.abs(Y.astype(np.float64) - ref)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                rel = np.where(S > 0, err / S, np.where(err > 0, np.inf, 0.0))
+            worst = max(worst, float(rel.max()))
+        errors[key] = worst
+        if key == "config3":
+            n_us = sum(x["oracle_us_nthreads"] for x in rows_out)
+            one_us = sum(x["oracle_us_1thread"] for x in rows_out)
+            per_config[key] = dict(layer0=rows_out, step_oracle_us_nthreads_scaled=round(32 * n_us, 1),
+                                   step_oracle_us_1thread_scaled=round(32 * one_us, 1),
+                                   note="step = 32 x layer 0 (scaled, not timed)")
+        elif key == "config4":
+            m64 = [x for x in rows_out if x["M"] == 64]
+            per_config[key] = dict(measured=rows_out,
+                                   M512_oracle_us_nthreads_scaled=[dict(shape=x["shape"],
+                                                                        us=round(8 * x["oracle_us_nthreads"], 1))
+                                                                   for x in m64],
+                                   note="M = 512 as 8 x M = 64 (scaled, not timed)")
+        else:
+            per_config[key] = rows_out
     return {"value": round(done / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "value_1thread": round(per_pass / dt1 / 1e9, 3),
             "sample": f"{passes} pass(es) over layer 0's 7 Q4_K projections "
-                      f"({per_pass / 1e6:.1f} MB per pass) of the decode step, "
-                      f"f64 accumulation, {dt:.1f}s"}
+                      f"({per_pass / 1e6:.1f} MB per pass) of the decode step on {threads} threads, "
+                      f"f64 accumulation, {dt:.1f}s; one pass on 1 thread, {dt1:.1f}s",
+            "per_config": per_config,
+            "max_rel_err": errors}
 
 
 if __name__ == "__main__":
