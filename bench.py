@@ -149,6 +149,39 @@ def traffic_probe(torch, gq, lib, synth, mats, stream_ptr):
                                                             rows, cols)}}), flush=True)
 
 
+def decode_probe(torch, gq, lib, synth, mats, stream_ptr):
+    """Eager launches for counter runs: the 224 matvecs of the decode step
+    twice (q/o/gate/up run the row-group kernel instance of the roofline, k/v
+    its 1024-row sibling, down the wide-row Q4_K kernel), then for layers
+    0-3 the fused launches (q|k|v matvec, gate|up SwiGLU matvec, o and down
+    accumulating)."""
+    sp = stream_ptr()
+    for _ in range(2):
+        for m in mats:
+            assert lib.gq_matvec(*m["args"], sp) == 0
+    torch.cuda.synchronize()
+    f = gq.FMT_Q4_K
+    for layer in range(4):
+        q, k, v, o, gate, up, down = mats[7 * layer:7 * layer + 7]
+        wqkv = torch.cat([q["W"], k["W"], v["W"]])
+        wgu = torch.cat([gate["W"], up["W"]])
+        yqkv = torch.empty(q["rows"] + k["rows"] + v["rows"], dtype=torch.float32, device="cuda")
+        h = torch.empty(gate["rows"], dtype=torch.float32, device="cuda")
+        resid = torch.zeros(o["rows"], dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        assert lib.gq_matvec(f, wqkv.data_ptr(), yqkv.numel(), q["cols"], q["x"].data_ptr(),
+                             yqkv.data_ptr(), sp) == 0
+        assert lib.gq_matvec_acc(f, o["W"].data_ptr(), o["rows"], o["cols"], o["x"].data_ptr(),
+                                 resid.data_ptr(), sp) == 0
+        assert lib.gq_matvec_swiglu(f, wgu.data_ptr(), gate["rows"], gate["cols"], gate["x"].data_ptr(),
+                                    h.data_ptr(), sp) == 0
+        assert lib.gq_matvec_acc(f, down["W"].data_ptr(), down["rows"], down["cols"], down["x"].data_ptr(),
+                                 resid.data_ptr(), sp) == 0
+        torch.cuda.synchronize()
+        del wqkv, wgu
+    print(json.dumps({"decode_probe": "done", "step_launches": len(mats), "fused_layers": 4}), flush=True)
+
+
 def prefill_probe(torch, gq, lib, synth, stream_ptr, ms=(512,)):
     """One call of each prefill product per M (after one warm-up call):
     Q4_K gate and down on the fp16 matrix cores and, at M = 512, Q6_K down
@@ -193,6 +226,9 @@ def main() -> int:
                     help="activation rows for --prefill-probe, comma separated")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 256 MiB copy and one pass of the dominant kernel, then exit")
+    ap.add_argument("--decode-probe", action="store_true",
+                    help="run the 224-launch decode step twice and the fused launches of 4 layers "
+                         "once, eagerly (for rocprofv3 counter runs), then exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -238,6 +274,9 @@ def main() -> int:
 
     if args.traffic_probe:
         traffic_probe(torch, gq, lib, synth, mats, stream_ptr)
+        return 0
+    if args.decode_probe:
+        decode_probe(torch, gq, lib, synth, mats, stream_ptr)
         return 0
 
     def step(subset=None):
