@@ -13,6 +13,8 @@ is no CPU fallback: if the library is not built, loading raises.
     gq_matvec_experts(fmt, W, n_expert, rows, cols, X, xk, expid, Y=None)
                                                        -> Y[a] = W[expid[a]] X[a // xk]
     gq_matmul(fmt, W, rows, cols, X, Y=None)           -> Y [M, rows] fp32
+    gq_matmul_acc(fmt, W, rows, cols, X, Y)            -> Y += W X
+    gq_matmul_swiglu(fmt, W, rows, cols, X, Y=None)    -> Y = silu(W_gate X) * (W_up X)
     gq_quantize_q8_1(X, n, cols, out=None)             -> Q8_1 activation blocks
     gq_matvec_q8_1(fmt, W, rows, cols, xq, y=None)     -> y = W x^ (int8 activations)
 
@@ -48,7 +50,8 @@ GQ_ERR_OVERLAP = 6
 
 EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matvec_acc",
            "gq_matvec_swiglu", "gq_matvec_experts", "gq_matvec_batch", "gq_q8_0_split_repack",
-           "gq_matmul", "gq_matmul_experts", "gq_quantize_q8_1", "gq_matvec_q8_1")
+           "gq_matmul", "gq_matmul_experts", "gq_quantize_q8_1", "gq_matvec_q8_1",
+           "gq_matmul_acc", "gq_matmul_swiglu")
 
 _lib = None
 
@@ -84,7 +87,7 @@ def load_library():
     lib.gq_matvec_experts.restype = i32
     lib.gq_matmul_experts.argtypes = [i32, vp, i64, i64, i64, vp, ctypes.POINTER(i64), vp, vp]
     lib.gq_matmul_experts.restype = i32
-    for name in ("gq_matmul", "gq_matvec_batch"):
+    for name in ("gq_matmul", "gq_matvec_batch", "gq_matmul_acc", "gq_matmul_swiglu"):
         getattr(lib, name).argtypes = [i32, vp, i64, i64, vp, i64, vp, vp]
         getattr(lib, name).restype = i32
     lib.gq_quantize_q8_1.argtypes = [vp, i64, i64, vp, vp]
@@ -270,9 +273,9 @@ def gq_q8_0_split_repack(W, rows: int, cols: int, out=None, stream=None):
     return out
 
 
-def _rows_product(name: str, fmt: int, W, rows: int, cols: int, X, Y, stream):
+def _rows_product(name: str, fmt: int, W, rows: int, cols: int, X, Y, stream, wrows=None):
     torch = _torch()
-    _check_w(fmt, W, rows, cols)
+    _check_w(fmt, W, rows if wrows is None else wrows, cols)
     _check_dev(X, "X", torch.float32)
     if X.numel() % cols != 0:
         raise ValueError("X must hold M * cols floats")
@@ -292,6 +295,19 @@ def _rows_product(name: str, fmt: int, W, rows: int, cols: int, X, Y, stream):
 def gq_matmul(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):
     """Y[M, rows] = X[M, cols] W^T on `stream`, asynchronous."""
     return _rows_product("gq_matmul", fmt, W, rows, cols, X, Y, stream)
+
+
+def gq_matmul_acc(fmt: int, W, rows: int, cols: int, X, Y, stream=None):
+    """Y[M, rows] += X[M, cols] W^T (Y holds the addend), asynchronous."""
+    if Y is None:
+        raise ValueError("gq_matmul_acc needs Y")
+    return _rows_product("gq_matmul_acc", fmt, W, rows, cols, X, Y, stream)
+
+
+def gq_matmul_swiglu(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):
+    """Y[m, r] = silu(g) * u for the gate|up tensor W (2 * rows weight rows:
+    gate rows first, then up rows), asynchronous."""
+    return _rows_product("gq_matmul_swiglu", fmt, W, rows, cols, X, Y, stream, wrows=2 * rows)
 
 
 def gq_matvec_batch(fmt: int, W, rows: int, cols: int, X, Y=None, stream=None):

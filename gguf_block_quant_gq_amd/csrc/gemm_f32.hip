@@ -23,6 +23,7 @@
 //
 // Q4_K runs here only for rows whose length is not a multiple of 4 (the
 // fp16 matrix-core kernel reads activations four at a time).
+#include "gemv_common.h"
 #include "gq_device.h"
 #include "gq_internal.h"
 #include "gq_quads.h"
@@ -42,7 +43,7 @@ struct F32Args {
   int xvec;    // X rows are 16-byte aligned and cols % 4 == 0
 };
 
-template <class Q, int WM, int RW, int KS, int PF, int KC>
+template <class Q, int WM, int RW, int KS, int PF, int KC, int EPI>
 __global__ __launch_bounds__(64 * RW * KS) void gemm_f32_kernel(F32Args a) {
   static_assert(PF == 1 || PF == 2, "prefetch depth");
   static_assert(KC == 64 || KC == 128, "chunk");
@@ -193,16 +194,21 @@ __global__ __launch_bounds__(64 * RW * KS) void gemm_f32_kernel(F32Args a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = m0 + 16 * t + 4 * q + e;
-      if (m < a.M) a.Y[(int64_t)m * a.rows + r] = acc[t][e];
+      if (m < a.M) {
+        float* p = a.Y + (int64_t)m * a.rows + r;
+        if constexpr (EPI == kMmAcc) *p += acc[t][e];
+        else if constexpr (EPI == kMmSiluMul) *p = silu_mul(acc[t][e], *p);
+        else *p = acc[t][e];
+      }
     }
   }
 }
 
-template <class Q, int WM, int RW, int KS, int PF, int KC>
+template <class Q, int WM, int RW, int KS, int PF, int KC, int EPI>
 hipError_t launch(F32Args a, int gy, hipStream_t s) {
   const int gx = (a.rows + 16 * RW - 1) / (16 * RW);
   a.nchunk = (a.cols + KC - 1) / KC;
-  hipLaunchKernelGGL((gemm_f32_kernel<Q, WM, RW, KS, PF, KC>), dim3(gx, gy), dim3(64 * RW * KS), 0, s, a);
+  hipLaunchKernelGGL((gemm_f32_kernel<Q, WM, RW, KS, PF, KC, EPI>), dim3(gx, gy), dim3(64 * RW * KS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -214,34 +220,48 @@ hipError_t launch(F32Args a, int gy, hipStream_t s) {
 // m-tile (Q6_K M = 16: 58 us against 127 with four), six or eight with 64-k
 // chunks (so that their tiles fit the LDS) for four or two (Q6_K M = 64:
 // 158 us against 232 with four).
-template <class Q>
+template <class Q, int EPI>
 hipError_t launch_wm(const F32Args& a, int cus, hipStream_t s) {
   const int mtiles = (a.M + 15) / 16;
   const int WM = mtiles >= 4 ? 4 : mtiles >= 2 ? 2 : 1;
   const int gy = (mtiles + WM - 1) / WM;
   const int64_t grid = (int64_t)((a.rows + 63) / 64) * gy;
   if (grid >= 2LL * cus || (WM > 1 && grid >= (int64_t)cus * 7 / 8)) {
-    if (WM == 4) return launch<Q, 4, 4, 1, 1, 128>(a, gy, s);
-    if (WM == 2) return launch<Q, 2, 4, 1, 1, 128>(a, gy, s);
-    return launch<Q, 1, 4, 1, 1, 128>(a, gy, s);
+    if (WM == 4) return launch<Q, 4, 4, 1, 1, 128, EPI>(a, gy, s);
+    if (WM == 2) return launch<Q, 2, 4, 1, 1, 128, EPI>(a, gy, s);
+    return launch<Q, 1, 4, 1, 1, 128, EPI>(a, gy, s);
   }
-  if (WM == 4) return launch<Q, 4, 1, 6, 1, 64>(a, gy, s);
-  if (WM == 2) return launch<Q, 2, 1, 8, 1, 64>(a, gy, s);
-  return launch<Q, 1, 1, 8, 1, 128>(a, mtiles, s);
+  if (WM == 4) return launch<Q, 4, 1, 6, 1, 64, EPI>(a, gy, s);
+  if (WM == 2) return launch<Q, 2, 1, 8, 1, 64, EPI>(a, gy, s);
+  return launch<Q, 1, 1, 8, 1, 128, EPI>(a, mtiles, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s) {
+namespace {
+
+template <int EPI>
+hipError_t launch_gemm_f32_epi(int fmt, const F32Args& fa, int cus, hipStream_t s) {
+  switch (fmt) {
+    case kFmtQ8_0: return launch_wm<Q8Quad, EPI>(fa, cus, s);
+    case kFmtQ5_0: return launch_wm<Q5_0Quad, EPI>(fa, cus, s);
+    case kFmtQ4_K: return launch_wm<Q4KQuad, EPI>(fa, cus, s);
+    case kFmtQ5_K: return launch_wm<Q5KQuad, EPI>(fa, cus, s);
+    case kFmtQ6_K: return launch_wm<Q6KQuad, EPI>(fa, cus, s);
+    case kFmtQ8_0Split: return launch_wm<Q8SplitQuad, EPI>(fa, cus, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s, int epi) {
   const int xvec = (a.cols % 4 == 0) && (((uintptr_t)a.X & 15) == 0);
   const F32Args fa{a.W, a.X, a.Y, a.row_bytes, a.rows, a.cols, a.M, 0, xvec};
-  switch (fmt) {
-    case kFmtQ8_0: return launch_wm<Q8Quad>(fa, cus, s);
-    case kFmtQ5_0: return launch_wm<Q5_0Quad>(fa, cus, s);
-    case kFmtQ4_K: return launch_wm<Q4KQuad>(fa, cus, s);
-    case kFmtQ5_K: return launch_wm<Q5KQuad>(fa, cus, s);
-    case kFmtQ6_K: return launch_wm<Q6KQuad>(fa, cus, s);
-    case kFmtQ8_0Split: return launch_wm<Q8SplitQuad>(fa, cus, s);
+  switch (epi) {
+    case kMmStore: return launch_gemm_f32_epi<kMmStore>(fmt, fa, cus, s);
+    case kMmAcc: return launch_gemm_f32_epi<kMmAcc>(fmt, fa, cus, s);
+    case kMmSiluMul: return launch_gemm_f32_epi<kMmSiluMul>(fmt, fa, cus, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -37,6 +37,7 @@
 //     i, takes the row's largest magnitude with two lane exchanges, and
 //     splits its values into the hi and lo operands.
 // The four waves' products are added in LDS in wave order (deterministic).
+#include "gemv_common.h"
 #include "gq_device.h"
 #include "gq_internal.h"
 
@@ -155,6 +156,14 @@ struct MmTile {
 
 constexpr int kMaxGroups = 64;
 
+// The epilogue of one output element (see GemmEpilogue).
+template <int EPI>
+__device__ __forceinline__ void mm_out(float* p, float v) {
+  if constexpr (EPI == kMmAcc) *p += v;
+  else if constexpr (EPI == kMmSiluMul) *p = silu_mul(v, *p);
+  else *p = v;
+}
+
 struct MmArgs {
   const uint8_t* W;
   const float* X;
@@ -186,7 +195,7 @@ constexpr int kXTile = 16 * kXRow;
 // straight from memory would make every instruction touch 16 rows whose
 // stride (cols * 4 bytes, a multiple of 4 KB for 4096 or 14336 columns)
 // maps them all to one L2 channel.
-template <int WR, int KW>
+template <int WR, int KW, int EPI>
 __global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
   __shared__ f32x4 red[KW][WR][64];
   __shared__ __attribute__((aligned(16))) uint8_t xbuf[KW][2][kXTile];
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int m = m0 + 4 * q + c;
-        if (m < m_end) a.Y[(int64_t)m * a.rows + r] = v[c];
+        if (m < m_end) mm_out<EPI>(a.Y + (int64_t)m * a.rows + r, v[c]);
       }
     }
   }
@@ -411,7 +420,7 @@ __device__ __forceinline__ f32x4 buf_f32x4(__amdgpu_buffer_rsrc_t rs, int voff) 
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
 }
 
-template <int R, int C, int D, int KS, int RS>
+template <int R, int C, int D, int KS, int RS, int EPI>
 __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
   static_assert(RS == 4 || (RS == 8 && C % 2 == 0), "row groups");
   constexpr int CW = C * 4 / RS;          // m-tiles each wave converts
@@ -663,7 +672,7 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
           const int m = m0 + 16 * c + 4 * q + cc;
-          if (m < m_end) a.Y[(int64_t)m * a.rows + r] = acc[t][c][cc];
+          if (m < m_end) mm_out<EPI>(a.Y + (int64_t)m * a.rows + r, acc[t][c][cc]);
         }
     }
   }
@@ -673,16 +682,16 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
 #define GQ_MM_KW 4  // waves per workgroup (splitting the super-blocks)
 #endif
 
-template <int WR>
+template <int WR, int EPI>
 hipError_t launch(const MmArgs& a, int gx, int gy, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_q4k_kernel<WR, GQ_MM_KW>), dim3(gx, gy), dim3(GQ_MM_KW * 64), 0, s, a);
+  hipLaunchKernelGGL((gemm_q4k_kernel<WR, GQ_MM_KW, EPI>), dim3(gx, gy), dim3(GQ_MM_KW * 64), 0, s, a);
   return hipGetLastError();
 }
 
-template <int R, int C, int D, int KS, int RS>
+template <int R, int C, int D, int KS, int RS, int EPI>
 hipError_t launch_xs(const MmArgs& a, int gy, hipStream_t s) {
   const int gx = (a.rows + 16 * RS * R - 1) / (16 * RS * R);
-  hipLaunchKernelGGL((gemm_q4k_xs_kernel<R, C, D, KS, RS>), dim3(gx, gy), dim3(64 * RS * KS), 0, s, a);
+  hipLaunchKernelGGL((gemm_q4k_xs_kernel<R, C, D, KS, RS, EPI>), dim3(gx, gy), dim3(64 * RS * KS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -723,16 +732,11 @@ bool gemm_q4k_fits(int64_t rows, int64_t cols, int64_t row_bytes) {
 // in four (gate M = 16: 19 us, down M = 64: 56 us) -- else the per-wave
 // kernel with as many weight-row tiles per workgroup as still fill the GPU
 // (down M = 16: 30 us).
-hipError_t launch_gemm_q4k(const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
-                           int n_groups, int64_t group_w_bytes, int cus, hipStream_t s) {
-  MmArgs m{};
-  m.W = a.W;
-  m.X = a.X;
-  m.Y = a.Y;
-  m.row_bytes = a.row_bytes;
-  m.rows = a.rows;
-  m.cols = a.cols;
-  m.nsb = (a.cols + 255) / 256;
+namespace {
+
+template <int EPI>
+hipError_t launch_gemm_q4k_epi(MmArgs& m, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
+                               int n_groups, int64_t group_w_bytes, int cus, hipStream_t s) {
   const int64_t fill = (int64_t)cus * 7 / 8;
   auto grid = [&](int tr, int tm) { return ((a.rows + tr - 1) / tr) * count_mtiles(group_m, n_groups, tm); };
   auto run_xs = [&](auto launch, int tm) {
@@ -741,15 +745,36 @@ hipError_t launch_gemm_q4k(const GemmArgs& a, const int64_t* group_m, const int6
     if (gy == 0) return hipSuccess;
     return launch(m, gy, s);
   };
-  if (grid(256, 64) >= fill) return run_xs(launch_xs<2, 4, 1, 1, 8>, 64);
-  if (grid(256, 32) >= fill) return run_xs(launch_xs<2, 2, 2, 1, 8>, 32);
-  if (grid(128, 32) >= fill) return run_xs(launch_xs<1, 2, 1, 2, 8>, 32);
-  if (grid(64, 16) >= fill) return run_xs(launch_xs<1, 1, 1, 4, 4>, 16);
+  if (grid(256, 64) >= fill) return run_xs(launch_xs<2, 4, 1, 1, 8, EPI>, 64);
+  if (grid(256, 32) >= fill) return run_xs(launch_xs<2, 2, 2, 1, 8, EPI>, 32);
+  if (grid(128, 32) >= fill) return run_xs(launch_xs<1, 2, 1, 2, 8, EPI>, 32);
+  if (grid(64, 16) >= fill) return run_xs(launch_xs<1, 1, 1, 4, 4, EPI>, 16);
   const int gy = build_groups(m, group_m, group_off, n_groups, group_w_bytes, 16);
   if (gy < 0) return hipErrorInvalidValue;
   if (gy == 0) return hipSuccess;
-  if (grid(32, 16) >= fill) return launch<2>(m, (a.rows + 31) / 32, gy, s);
-  return launch<1>(m, (a.rows + 15) / 16, gy, s);
+  if (grid(32, 16) >= fill) return launch<2, EPI>(m, (a.rows + 31) / 32, gy, s);
+  return launch<1, EPI>(m, (a.rows + 15) / 16, gy, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_q4k(const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
+                           int n_groups, int64_t group_w_bytes, int cus, hipStream_t s, int epi) {
+  MmArgs m{};
+  m.W = a.W;
+  m.X = a.X;
+  m.Y = a.Y;
+  m.row_bytes = a.row_bytes;
+  m.rows = a.rows;
+  m.cols = a.cols;
+  m.nsb = (a.cols + 255) / 256;
+  switch (epi) {
+    case kMmStore: return launch_gemm_q4k_epi<kMmStore>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
+    case kMmAcc: return launch_gemm_q4k_epi<kMmAcc>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
+    case kMmSiluMul:
+      return launch_gemm_q4k_epi<kMmSiluMul>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace gq

@@ -276,37 +276,69 @@ bool matmul_addressable(int fmt, int64_t rows, int64_t cols, int64_t M, int64_t 
   return true;
 }
 
-// gq_matmul after its checks: the kernel route for M activation rows.
-int matmul_route(int fmt, const void* W, int64_t rb, int64_t rows, int64_t cols, const float* X,
-                 int64_t M, float* Y, void* stream, int cus) {
-  // One activation row is the matvec (same rounding, its kernel). A few rows
-  // over a small enough product run as the batched matvec, so each row again
-  // rounds exactly as the matvec does (its cost grows with M * rows * cols:
-  // every row repeats the decode; measured faster than the matrix cores up
-  // to about 2^28 weight-rows for every format). Larger Q4_K products run on
-  // the fp16 matrix cores (exact operands), the other formats on the fp32
-  // matrix cores from a per-format M, else on the fp32 few-row kernel.
-  if (M == 1) {
-    gq::GemvArgs v{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
-    return finish(gq::launch_gemv(fmt, v, cus, (hipStream_t)stream));
-  }
-  if (batched_matvec(M, rows, cols)) return batch_launch(fmt, W, rb, rows, cols, X, M, Y, stream, cus);
-  gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
+// The three output modes of the prefill product.
+enum MatmulMode { kModeStore = 0, kModeAcc = 1, kModeSwiglu = 2 };
+
+// One matrix-core product of the route for (fmt, cols, M) with a GEMM epilogue.
+int matrix_product(int fmt, const uint8_t* W, int64_t rb, int64_t rows, int64_t cols, const float* X,
+                   int64_t M, float* Y, hipStream_t s, int cus, int epi) {
+  gq::GemmArgs a{W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
   if (q4k_matrix_cores(fmt, cols)) {
     const int64_t off = 0;
-    return finish(gq::launch_gemm_q4k(a, &M, &off, 1, 0, cus, (hipStream_t)stream));
+    return finish(gq::launch_gemm_q4k(a, &M, &off, 1, 0, cus, s, epi));
   }
-  if (fmt == GQ_FMT_Q4_K || M >= f32_matrix_core_min_m(fmt))
-    return finish(gq::launch_gemm_f32(fmt, a, cus, (hipStream_t)stream));
-  return finish(gq::launch_gemm_small(fmt, a, cus, (hipStream_t)stream));
+  // the few-row fp32 kernel stores only: the other modes take the fp32 matrix cores
+  if (fmt == GQ_FMT_Q4_K || M >= f32_matrix_core_min_m(fmt) || epi != gq::kMmStore)
+    return finish(gq::launch_gemm_f32(fmt, a, cus, s, epi));
+  return finish(gq::launch_gemm_small(fmt, a, cus, s));
 }
 
-}  // namespace
+// gq_matmul (and its accumulate / SwiGLU forms) after the checks: the kernel
+// route for M activation rows. One activation row is the matvec (same
+// rounding, its kernel and epilogue). A few rows over a small enough product
+// run as matvecs, so each row again rounds exactly as the matvec does (its
+// cost grows with M * rows * cols: every row repeats the decode; measured
+// faster than the matrix cores up to about 2^28 weight-rows for every
+// format): one batched launch for the stored form, one launch per row for
+// the others. Larger Q4_K products run on the fp16 matrix cores (exact
+// operands), the other formats on the fp32 matrix cores from a per-format M,
+// else on the fp32 few-row kernel. The SwiGLU form on the matrix cores is
+// two launches: Y = W_up X, then Y = silu(W_gate X) * Y.
+int matmul_route(int fmt, const void* W, int64_t rb, int64_t rows, int64_t cols, const float* X,
+                 int64_t M, float* Y, void* stream, int cus, int mode = kModeStore) {
+  const hipStream_t s = (hipStream_t)stream;
+  const int gemv_epi = mode == kModeAcc ? gq::kEpiAcc : mode == kModeSwiglu ? gq::kEpiSwiglu : gq::kEpiStore;
+  if (M == 1) {
+    gq::GemvArgs v{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0};
+    return finish(gq::launch_gemv(fmt, v, cus, s, gemv_epi));
+  }
+  if (batched_matvec(M, rows, cols)) {
+    if (mode == kModeStore) return batch_launch(fmt, W, rb, rows, cols, X, M, Y, stream, cus);
+    for (int64_t m = 0; m < M; ++m) {
+      gq::GemvArgs v{(const uint8_t*)W, X + m * cols, Y + m * rows, rb, (int)rows, (int)cols, 0};
+      const int st = finish(gq::launch_gemv(fmt, v, cus, s, gemv_epi));
+      if (st != GQ_OK) return st;
+    }
+    return GQ_OK;
+  }
+  const uint8_t* w = (const uint8_t*)W;
+  if (mode == kModeSwiglu) {
+    const int st = matrix_product(fmt, w + rows * rb, rb, rows, cols, X, M, Y, s, cus, gq::kMmStore);
+    if (st != GQ_OK) return st;
+    return matrix_product(fmt, w, rb, rows, cols, X, M, Y, s, cus, gq::kMmSiluMul);
+  }
+  return matrix_product(fmt, w, rb, rows, cols, X, M, Y, s, cus,
+                        mode == kModeAcc ? gq::kMmAcc : gq::kMmStore);
+}
 
-extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,
-                         int64_t M, float* Y, void* stream) {
+// The checks and launch shared by gq_matmul, gq_matmul_acc and
+// gq_matmul_swiglu (W holds 2 * rows weight rows for the SwiGLU form).
+int matmul_entry(int fmt, const void* W, int64_t rows, int64_t cols, const float* X, int64_t M, float* Y,
+                 void* stream, int mode) {
   int64_t rb = 0, wbytes = 0;
-  int st = check_shape(fmt, rows, cols, M, &rb, &wbytes);
+  const int64_t wrows = mode == kModeSwiglu ? 2 * rows : rows;
+  if (rows > INT_MAX) return GQ_ERR_SHAPE;
+  int st = check_shape(fmt, wrows, cols, M, &rb, &wbytes);
   if (st != GQ_OK) return st;
   if (M > 0 && (rows > INT64_MAX / 4 / M || cols > INT64_MAX / 4 / M)) return GQ_ERR_SHAPE;
   if (rows == 0 || M == 0) return GQ_OK;
@@ -320,7 +352,24 @@ extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, con
   const int cus = current_cus();
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
-  return matmul_route(fmt, W, rb, rows, cols, X, M, Y, stream, cus);
+  return matmul_route(fmt, W, rb, rows, cols, X, M, Y, stream, cus, mode);
+}
+
+}  // namespace
+
+extern "C" int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,
+                         int64_t M, float* Y, void* stream) {
+  return matmul_entry(fmt, W, rows, cols, X, M, Y, stream, kModeStore);
+}
+
+extern "C" int gq_matmul_acc(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,
+                             int64_t M, float* Y, void* stream) {
+  return matmul_entry(fmt, W, rows, cols, X, M, Y, stream, kModeAcc);
+}
+
+extern "C" int gq_matmul_swiglu(int fmt, const void* W, int64_t rows, int64_t cols, const float* X,
+                                int64_t M, float* Y, void* stream) {
+  return matmul_entry(fmt, W, rows, cols, X, M, Y, stream, kModeSwiglu);
 }
 
 extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64_t rows,

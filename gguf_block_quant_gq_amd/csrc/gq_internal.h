@@ -44,6 +44,14 @@ enum GemvEpilogue : int {
   kEpiSwiglu = 2,  // y[r] = silu(sum of row r) * (sum of row rows + r)
 };
 
+// What the prefill products do with each finished output (one write per
+// output element, so the read-modify-write forms are exact and race-free).
+enum GemmEpilogue : int {
+  kMmStore = 0,    // Y = sum
+  kMmAcc = 1,      // Y += sum
+  kMmSiluMul = 2,  // Y = silu(sum) * Y (Y holds the up projection: the SwiGLU's second half)
+};
+
 struct DequantArgs {
   const uint8_t* W;
   float* out;
@@ -86,7 +94,7 @@ hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
 // gemm_q4k_fits: whether its 31-bit buffer offsets cover the shape.
 bool gemm_q4k_fits(int64_t rows, int64_t cols, int64_t row_bytes);
 hipError_t launch_gemm_q4k(const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
-                           int n_groups, int64_t group_w_bytes, int cus, hipStream_t s);
+                           int n_groups, int64_t group_w_bytes, int cus, hipStream_t s, int epi = kMmStore);
 // The int8-activation path (gemv_q8a.hip): Q8_1 quantisation of n rows of
 // activations, and y = W x^ for Q8_0 / Q4_K weights with integer dots.
 hipError_t launch_quantize_q8_1(const float* x, int64_t n, int cols, uint8_t* out, hipStream_t s);
@@ -95,6 +103,6 @@ hipError_t launch_gemv_q8a(int fmt, const uint8_t* W, int64_t row_bytes, int row
 
 // The fp32 matrix-core product (gemm_f32.hip): Q8_0, Q8_0 split, Q5_0, Q5_K,
 // Q6_K, and Q4_K rows whose length is not a multiple of 4.
-hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s);
+hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s, int epi = kMmStore);
 
 }  // namespace gq

@@ -241,6 +241,28 @@ int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
               const float* X, int64_t M, float* Y, void* stream);
 
 /*
+ * The prefill product's other output modes (the Loom porting skill, "What
+ * the starter generates": its GEMM generator has store, acc and swiglu
+ * modes, as the matvec does here), same arguments, routes, limits and
+ * accuracy as gq_matmul:
+ *   gq_matmul_acc:    Y[m*rows + r] += sum_c w(r, c) * X[m*cols + c]
+ *                     (Y holds the addend; one fp32 addition per output).
+ *   gq_matmul_swiglu: W is a gate|up tensor of 2 * rows weight rows (gate
+ *                     rows first), Y[m*rows + r] = silu(g) * u with g, u the
+ *                     products of gate row r and up row rows + r, evaluated
+ *                     in fp32 as g / (1 + e^-g) * u, as gq_matvec_swiglu does.
+ * M == 1 runs gq_matvec_acc / gq_matvec_swiglu, and the few-row range (M <
+ * 16, M * rows * cols <= 2^28) runs them once per activation row, so those
+ * rows equal the matvec forms bit for bit. On the matrix cores the SwiGLU
+ * form is two launches on `stream` (Y = up products, then Y = silu(gate
+ * products) * Y), with no memory beyond the arguments. Asynchronous.
+ */
+int gq_matmul_acc(int fmt, const void* W, int64_t rows, int64_t cols,
+                  const float* X, int64_t M, float* Y, void* stream);
+int gq_matmul_swiglu(int fmt, const void* W, int64_t rows, int64_t cols,
+                     const float* X, int64_t M, float* Y, void* stream);
+
+/*
  * Grouped product for the prefill of a mixture-of-experts layer: activation
  * rows already bucketed by expert (the Loom porting skill, "Beyond the
  * starter": tokens bucketed by expert, then one grouped GEMM per expert for

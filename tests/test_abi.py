@@ -269,3 +269,24 @@ def test_validation_int8_activation_path(lib):
     assert _q81(lib, x=X_OK + 2) == gq.GQ_ERR_ALIGN
     assert _q81(lib, xq=Y_OK + 1) == gq.GQ_ERR_ALIGN
     assert _q81(lib, xq=X_OK + 1024) == gq.GQ_ERR_OVERLAP    # output over the second row of x
+
+
+def test_validation_matmul_modes(lib):
+    for name in ("gq_matmul_acc", "gq_matmul_swiglu"):
+        fn = getattr(lib, name)
+        call = lambda fmt=12, W=W_OK, rows=4, cols=256, X=X_OK, M=2, Y=Y_OK: fn(fmt, W, rows, cols, X, M, Y, None)
+        assert call(fmt=7) == gq.GQ_ERR_FMT
+        assert call(fmt=gq.GQ_FMT_Q8_1) == gq.GQ_ERR_FMT
+        assert call(rows=-1) == gq.GQ_ERR_SHAPE
+        assert call(cols=0) == gq.GQ_ERR_SHAPE
+        assert call(M=-1) == gq.GQ_ERR_SHAPE
+        assert call(rows=0, W=None, X=None, Y=None) == gq.GQ_OK
+        assert call(M=0, W=None, X=None, Y=None) == gq.GQ_OK
+        assert call(W=None) == gq.GQ_ERR_NULL
+        assert call(W=W_OK + 2) == gq.GQ_ERR_ALIGN
+        assert call(Y=X_OK + 256 * 4) == gq.GQ_ERR_OVERLAP
+    # the SwiGLU form reads 2 * rows weight rows: Y over the up half overlaps
+    assert lib.gq_matmul_swiglu(12, W_OK, 4, 256, X_OK, 2, W_OK + 6 * 144, None) == gq.GQ_ERR_OVERLAP
+    # the Q4_K matrix-core bound holds per half
+    far = 1 << 40
+    assert lib.gq_matmul_swiglu(12, W_OK, 16, 1 << 23, far, 16, 2 * far, None) == gq.GQ_ERR_SHAPE
