@@ -52,16 +52,33 @@ def log(msg: str) -> None:
 
 
 class Timer:
-    """HIP events on torch's current stream, which is where libgq launches."""
+    """HIP events on torch's current stream, which is where libgq launches.
 
-    def __init__(self, torch):
+    Before a timed loop the same work runs for at least `warm_ms` of wall
+    time: the GPU's clock falls while it idles and ramps back up under load
+    (an M = 512 prefill product measured 219-222 us right after an idle gap
+    against 186-195 us after a few milliseconds of work), so a few calls
+    timed from cold measure the ramp, not the kernel."""
+
+    def __init__(self, torch, warm_ms: float = 20.0):
         self.torch = torch
+        self.warm_ms = warm_ms
 
-    def time(self, fn, iters: int, warmup: int = 1) -> float:
+    def warm(self, fn, batch: int) -> None:
+        torch = self.torch
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < self.warm_ms:
+            for _ in range(max(1, batch)):
+                fn()
+            torch.cuda.synchronize()
+
+    def time(self, fn, iters: int, warmup: int = 1, warm: bool = True) -> float:
         torch = self.torch
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        if warm and warmup > 0:
+            self.warm(fn, iters)
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record()
@@ -287,7 +304,9 @@ def main() -> int:
                 raise gq.GQError(st, "gq_matvec")
 
     graph = capture(torch, step)
-    ms_graph = timer.time(graph.replay, args.steps, warmup=args.warmup)
+    # exactly W untimed steps, then K timed ones (the K-step loop is long
+    # enough that the clock ramp is a small part of it)
+    ms_graph = timer.time(graph.replay, args.steps, warmup=args.warmup, warm=False)
     # spread of single steps (each replay timed alone), beside the K-step mean
     one = [timer.time(graph.replay, 1, warmup=0) for _ in range(max(5, args.steps // 2))]
     ms_eager = timer.time(step, max(5, args.steps // 5), warmup=2)

@@ -112,6 +112,36 @@ def test_few_rows_large_products(gq, oracle, fmt, rows, cols, M):
     assert_within_tolerance(Y[:, idx], ref, S, f"large few-row fmt={fmt} M={M}")
 
 
+@pytest.mark.parametrize("rows,M", [
+    (14336, 512),   # 256 x 64 tiles
+    (14336, 160),   # 256 x 32 tiles
+    (14336, 64),    # 128 x 32 tiles, k split in two
+    (14336, 16),    # 64 x 16 tiles, k split in four
+    (300, 20),      # one wave per tile
+])
+def test_q4k_ragged_row_on_each_tile(gq, oracle, rows, M):
+    """Q4_K rows of 4000 columns (the last super-block a partial one) on each
+    fp16 matrix-core tile: the product equals, bit for bit, the one over 4096
+    columns whose last 96 activations are zero (the storage and the scaling
+    of every super-block are the same), and the oracle on a sample of rows."""
+    cols, full = 4000, 4096
+    rng = synth.rng_for(613, rows + M)
+    W = synth.weights(12, rows, full, rng)
+    X = synth.activations((M, cols), rng)
+    Xp = np.zeros((M, full), np.float32)
+    Xp[:, :cols] = X
+    print(f"[matmul] q4k ragged rows={rows} cols={cols} M={M}", flush=True)
+    Wd = to_dev(W)
+    Y = _run(gq, 12, Wd, rows, cols, X)
+    Yp = _run(gq, 12, Wd, rows, full, Xp)
+    assert np.array_equal(Y.view(np.uint32), Yp.view(np.uint32))
+    idx = np.unique(np.concatenate([np.arange(0, rows, 97), [1, 15, 16, 255, 256, rows - 1]]))
+    idx = idx[idx < rows]
+    Ws = oracle.select_rows(12, W, cols, idx)
+    ref, S = oracle.matmul(12, Ws, idx.size, cols, X, nthreads=oracle_threads())
+    assert_within_tolerance(Y[:, idx], ref, S, f"q4k ragged M={M}")
+
+
 def test_q4k_wide_dynamic_range(gq, oracle):
     """Q4_K on the fp16 matrix cores: activations whose magnitudes span 2^-113
     .. 2^100 across rows and super-blocks, each within 2^13 of the largest in
