@@ -142,6 +142,24 @@ def test_q4k_ragged_row_on_each_tile(gq, oracle, rows, M):
     assert_within_tolerance(Y[:, idx], ref, S, f"q4k ragged M={M}")
 
 
+@pytest.mark.parametrize("fmt,rows", [(12, 16), (12, 300), (14, 16)])
+def test_many_activation_rows(gq, oracle, fmt, rows):
+    """4.3 million activation rows of 8 columns: the matrix-core grids have
+    more than 65535 m-tiles in their second dimension (64-row tiles: 67188).
+    Every output is finite, nothing is written past Y, and sampled rows on
+    both sides of the 65536th m-tile meet the oracle's bound."""
+    cols, M = 8, 4_300_000
+    rng = synth.rng_for(614, fmt * 1000 + rows)
+    W = synth.weights(fmt, rows, cols, rng)
+    X = synth.activations((M, cols), rng)
+    print(f"[matmul] many activation rows fmt={fmt} rows={rows} cols={cols} M={M}", flush=True)
+    Y = _run(gq, fmt, W, rows, cols, X)
+    assert np.isfinite(Y).all()
+    idx = np.array([0, 1, 65535 * 64 - 1, 65535 * 64, 65536 * 64 + 5, M - 1])
+    ref, S = oracle.matmul(fmt, W, rows, cols, X[idx])
+    assert_within_tolerance(Y[idx], ref, S, f"many activation rows fmt={fmt}")
+
+
 def test_q4k_wide_dynamic_range(gq, oracle):
     """Q4_K on the fp16 matrix cores: activations whose magnitudes span 2^-113
     .. 2^100 across rows and super-blocks, each within 2^13 of the largest in
