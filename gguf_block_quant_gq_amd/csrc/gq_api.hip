@@ -184,15 +184,15 @@ extern "C" int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64
   int64_t rb = 0, ebytes = 0;
   int st = check_shape(fmt, rows, cols, 1, &rb, &ebytes);
   if (st != GQ_OK) return st;
-  // the assignments are the grid's second dimension (at most 65535)
+  // the assignments are the grid's second dimension (an int index)
   if (n_expert < 1 || n_expert > INT_MAX || xk < 1 || xk > INT_MAX || n_assign < 0 ||
-      n_assign > 65535)
+      n_assign > INT_MAX)
     return GQ_ERR_SHAPE;
   if (rows == 0 || n_assign == 0) return GQ_OK;
   if (ebytes > INT64_MAX / n_expert) return GQ_ERR_SHAPE;
   const int64_t wbytes = ebytes * n_expert;
   const int64_t xrows = (n_assign + xk - 1) / xk;
-  if (rows > INT64_MAX / 4 / n_assign) return GQ_ERR_SHAPE;
+  if (rows > INT64_MAX / 4 / n_assign || cols > INT64_MAX / 4 / xrows) return GQ_ERR_SHAPE;
   const int64_t xbytes = xrows * cols * 4, ybytes = n_assign * rows * 4;
   if (!W || !X || !expid || !Y) return GQ_ERR_NULL;
   if ((st = check_align(fmt, W)) != GQ_OK) return st;
@@ -228,7 +228,6 @@ extern "C" int gq_matvec_batch(int fmt, const void* W, int64_t rows, int64_t col
   int64_t rb = 0, wbytes = 0;
   int st = check_shape(fmt, rows, cols, batch, &rb, &wbytes);
   if (st != GQ_OK) return st;
-  if (batch > 65535) return GQ_ERR_SHAPE;  // the grid's second dimension
   if (rows == 0 || batch == 0) return GQ_OK;
   if (rows > INT64_MAX / 4 / batch || cols > INT64_MAX / 4 / batch) return GQ_ERR_SHAPE;
   if (!W || !X || !Y) return GQ_ERR_NULL;

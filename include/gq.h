@@ -174,7 +174,7 @@ int gq_matvec_swiglu(int fmt, const void* W, int64_t rows, int64_t cols,
  * expert and activation row, bit for bit. An id outside [0, n_expert) reads
  * no weights and fills that assignment's output row with NaN (the ids live
  * on the device, so they cannot be checked before the launch). n_assign is
- * at most 65535 (GQ_ERR_SHAPE beyond). Asynchronous on `stream`.
+ * at most INT_MAX (GQ_ERR_SHAPE beyond). Asynchronous on `stream`.
  */
 int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, int64_t cols,
                       const float* X, int64_t xk, const int32_t* expid, int64_t n_assign,
@@ -192,7 +192,7 @@ int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, in
  * of results (same README, "What it runs"). One launch: every batch row is a slice of the matvec grid, and
  * the slices walk the same rows together, so W is streamed from HBM about
  * once. X: [batch, cols] row-major fp32 (4-byte aligned); Y: [batch, rows],
- * overwritten, must not overlap W or X. batch is at most 65535 (GQ_ERR_SHAPE
+ * overwritten, must not overlap W or X. batch is at most INT_MAX (GQ_ERR_SHAPE
  * beyond); batch == 0 or rows == 0 is a no-op. No workspace. Asynchronous
  * on `stream`.
  */

@@ -140,8 +140,8 @@ def test_validation_vectors(lib):
 
 def test_validation_batch(lib):
     assert _mb(lib, M=-1) == gq.GQ_ERR_SHAPE
-    assert _mb(lib, M=65536) == gq.GQ_ERR_SHAPE     # the grid's second dimension
-    assert _mb(lib, M=65535, Y=None) == gq.GQ_ERR_NULL
+    assert _mb(lib, M=2 ** 31) == gq.GQ_ERR_SHAPE    # past an int grid index
+    assert _mb(lib, M=65536, Y=None) == gq.GQ_ERR_NULL
     assert _mb(lib, M=0, X=None, Y=None) == gq.GQ_OK
     assert _mb(lib, X=None) == gq.GQ_ERR_NULL
     assert _mb(lib, Y=None) == gq.GQ_ERR_NULL
@@ -204,7 +204,10 @@ def test_validation_experts(lib):
     assert _mx(lib, n_expert=0) == gq.GQ_ERR_SHAPE
     assert _mx(lib, xk=0) == gq.GQ_ERR_SHAPE
     assert _mx(lib, n_assign=-1) == gq.GQ_ERR_SHAPE
-    assert _mx(lib, n_assign=65536) == gq.GQ_ERR_SHAPE
+    assert _mx(lib, n_assign=2 ** 31) == gq.GQ_ERR_SHAPE
+    assert _mx(lib, n_assign=65536, Y=None) == gq.GQ_ERR_NULL
+    # X rows times cols overflowing 64 bits
+    assert _mx(lib, n_assign=2 ** 31 - 1, xk=1, cols=2 ** 31 - 1, rows=1) == gq.GQ_ERR_SHAPE
     assert _mx(lib, cols=0) == gq.GQ_ERR_SHAPE
     assert _mx(lib, n_assign=0, W=None, expid=None) == gq.GQ_OK
     assert _mx(lib, rows=0, W=None) == gq.GQ_OK

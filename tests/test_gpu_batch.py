@@ -70,3 +70,27 @@ def test_batch_repeatable_and_empty(gq):
     Y0 = torch.full((1, rows), 7.0, device="cuda")
     gq.gq_matvec_batch(fmt, Wd, rows, cols, torch.empty(0, device="cuda"), Y=Y0)
     assert (to_host(Y0) == 7.0).all()
+
+
+@pytest.mark.parametrize("fmt,rows,cols", [(12, 8, 256), (8, 300, 64)])
+def test_batch_past_65535_rows(gq, oracle, fmt, rows, cols):
+    """70000 activation rows: the batch is the grid's second dimension, past
+    65535. Sampled rows on both sides of that boundary equal gq_matvec bit
+    for bit and meet the oracle's bound; nothing is written past Y."""
+    batch = 70000
+    rng = synth.rng_for(972, fmt * 1000 + rows)
+    W = synth.weights(fmt, rows, cols, rng)
+    X = synth.activations((batch, cols), rng)
+    print(f"[batch] past 65535 fmt={fmt} rows={rows} cols={cols} batch={batch}", flush=True)
+    Wd, Xd = to_dev(W), to_dev(X)
+    Yb = sentinel_buffer(batch * rows)
+    gq.gq_matvec_batch(fmt, Wd, rows, cols, Xd, Y=Yb[:batch * rows])
+    assert_pad_untouched(Yb, batch * rows)
+    got = to_host(Yb)[:batch * rows].reshape(batch, rows)
+    assert np.isfinite(got).all()
+    idx = [0, 1, 65534, 65535, 65536, batch - 1]
+    ref, S = oracle.matmul(fmt, W, rows, cols, X[idx])
+    assert_within_tolerance(got[idx], ref, S, "batch past 65535")
+    for b in idx:
+        y = gq.gq_matvec(fmt, Wd, rows, cols, Xd[b])
+        assert np.array_equal(to_host(y).view(np.uint32), got[b].view(np.uint32)), b

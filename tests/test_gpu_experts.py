@@ -54,6 +54,34 @@ def test_experts(gq, oracle, fmt, n_expert, rows, cols, positions, xk):
         assert np.array_equal(to_host(y).view(np.uint32), got[a].view(np.uint32)), a
 
 
+def test_experts_past_65535_assignments(gq, oracle):
+    """70000 assignments (35000 positions, top 2 of 4 experts): the
+    assignments are the grid's second dimension, past 65535. Every output
+    meets the oracle's bound and assignments on both sides of the boundary
+    equal gq_matvec of their expert bit for bit."""
+    import torch
+    fmt, n_expert, rows, cols, xk, n_assign = 12, 4, 8, 256, 2, 70000
+    rng = synth.rng_for(963, 0)
+    W = synth.weights(fmt, n_expert * rows, cols, rng)
+    X = synth.activations((n_assign // xk, cols), rng)
+    expid = rng.integers(0, n_expert, n_assign).astype(np.int32)
+    print(f"[experts] past 65535: n_assign={n_assign} rows={rows} cols={cols}", flush=True)
+    Wd, Xd = to_dev(W), to_dev(X)
+    Y = torch.full((n_assign + 1, rows), float("nan"), dtype=torch.float32, device="cuda")
+    gq.gq_matvec_experts(fmt, Wd, n_expert, rows, cols, Xd, xk, to_dev(expid), Y=Y)
+    got = to_host(Y)
+    assert np.isnan(got[n_assign]).all(), "wrote past the last assignment"
+    got = got[:n_assign]
+    ref, S = oracle.experts_matvec(fmt, W, n_expert, rows, cols, X, xk, expid,
+                                   nthreads=oracle_threads())
+    assert_within_tolerance(got, ref, S, "experts past 65535")
+    rb = gq.gq_row_bytes(fmt, cols)
+    for a in (0, 65534, 65535, 65536, n_assign - 1):
+        e = int(expid[a])
+        y = gq.gq_matvec(fmt, Wd[e * rows * rb:(e + 1) * rows * rb], rows, cols, Xd[a // xk])
+        assert np.array_equal(to_host(y).view(np.uint32), got[a].view(np.uint32)), a
+
+
 def test_invalid_ids_and_empty(gq, oracle):
     import torch
     fmt, n_expert, rows, cols = 12, 4, 300, 1024
