@@ -94,7 +94,11 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float* x, uint
   int q[4], s = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    q[e] = (int)roundf(v[e] * id);
+    // clamped to +-127, NaN to 0: only a block whose 1 / d overflows (max
+    // |x| under about 3.7e-37) reaches these cases (its products are +-inf,
+    // or NaN for x = 0); every other product rounds to at most 127
+    const float p = v[e] * id;
+    q[e] = p != p ? 0 : (int)roundf(fminf(fmaxf(p, -127.f), 127.f));
     s += q[e];
   }
   s = group8_sum(s);
@@ -363,12 +367,19 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t n, int cols, uint8_t* ou
 #define GQ_Q8A_WG_PER_CU 2  // each workgroup stages the whole activation row
 #endif
 
+// The largest staged row: 131072 columns = 4096 blocks of 32 codes + 8 bytes
+// (the host rejects wider rows), which is all 160 KB of a CU's LDS.
+constexpr int kQ8aMaxLds = 4096 * (kQ81Values + 8);
+
 template <class F>
 hipError_t launch_q8a(const Q8aArgs& a, int grid, int lds, hipStream_t s) {
-  // LDS past the default 64 KB per workgroup must be requested
+  if (lds > kQ8aMaxLds) return hipErrorInvalidValue;
+  // LDS past the default 64 KB per workgroup must be requested; every call
+  // requests the same maximum, so calls from several host threads cannot
+  // lower the limit under one another's launch
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute((const void*)gemv_q8a_kernel<F>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kQ8aMaxLds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(gemv_q8a_kernel<F>, dim3(grid), dim3(256), lds, s, a);

@@ -304,7 +304,10 @@ int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, in
  * 32 values (columns >= cols count as 0): d = amax / 127 (fp32, to nearest),
  * id = d != 0 ? 1 / d : 0, q_i = round-half-away-from-zero(x_i * id) (fp32
  * product, |q_i| <= 127); bytes 0-1 fp16(d), 2-3 fp16(d * sum q_i), 4..35 the
- * int8 q_i. Byte-identical to the CPU oracle's quantiser. n == 0 is a no-op.
+ * int8 q_i. A block whose 1 / d overflows (largest |x| under about 3.7e-37)
+ * has products +-inf, or NaN where x_i = 0: its codes are clamped to +-127
+ * and NaN gives 0 (its fp16 scale is 0, so its values are 0 either way).
+ * Byte-identical to the CPU oracle's quantiser. n == 0 is a no-op.
  * Asynchronous on `stream`.
  */
 int gq_quantize_q8_1(const float* x, int64_t n, int64_t cols, void* xq, void* stream);

@@ -629,6 +629,14 @@ int gqo_quantize_q4_k(const float* w, int64_t rows, int64_t cols, uint8_t* out)
  *   id   = d != 0 ? 1 / d : 0 (binary32 division, to nearest)
  *   q_i  = roundf(x_i * id)   (binary32 product, then to nearest with ties
  *                              away from zero; |q_i| <= 127)
+ *   Where 1 / d overflows (d below 2^-128, a block whose largest magnitude
+ *   is under about 3.7e-37) the product is +-inf or, for x_i = 0, NaN; the
+ *   public block leaves the conversion of those to an integer undefined.
+ *   Reading taken: the rounded product is clamped to [-127, 127] and a NaN
+ *   product gives 0, so such a block's codes are +-127 (by sign) and 0.
+ *   Every other block's products lie within 127 * (1 + 2^-22) and round
+ *   to at most 127, so the clamp never changes them. fp16(d) is 0 for
+ *   these blocks, so their values x^ are 0 either way.
  *   bytes 0-1: fp16(d), 2-3: fp16(d * sum q_i) (binary32 product, then
  *   binary16, both to nearest even), 4..35: q_0..q_31 (int8).
  * The values the product then uses are x^_i = f32(fp16(d)) * q_i (exact). */
@@ -654,7 +662,15 @@ int gqo_quantize_q8_1(const float* x, int64_t n, int64_t cols, uint8_t* out)
             int sum = 0;
             for (int i = 0; i < O_Q8_1_VALUES; i++) {
                 float p = v[i] * id;
-                int q = (int)roundf(p);
+                int q;
+                if (p != p)
+                    q = 0;
+                else if (p >= 127.0f)
+                    q = 127;
+                else if (p <= -127.0f)
+                    q = -127;
+                else
+                    q = (int)roundf(p);
                 blk[4 + i] = (uint8_t)(int8_t)q;
                 sum += q;
             }

@@ -38,12 +38,14 @@ def test_quantize_bit_exact(gq, oracle, n, cols, seed):
 def test_quantize_ties_tiny_and_zero_blocks(gq, oracle):
     # block 0: a scale of exactly 1 with half-integer values (ties go away
     # from zero); block 1: values near the fp32 normal limit (subnormal fp16
-    # scale); block 2: all zero; block 3: one value only
-    x = np.zeros(128, np.float32)
+    # scale); block 2: all zero; block 3: one value only; block 4: largest
+    # magnitude 1e-38, so 1 / d overflows (codes clamped to +-127, zeros 0)
+    x = np.zeros(160, np.float32)
     x[0:31] = (np.arange(-15, 16) + 0.5).astype(np.float32)
     x[31] = 127.0
     x[32:64] = np.float32(3e-37) * np.arange(1, 33, dtype=np.float32)
     x[100] = -5.0
+    x[128], x[129], x[140] = 1e-38, -1e-38, 2e-39
     X = x.reshape(1, -1)
     assert np.array_equal(_quantize_gpu(gq, X), oracle.quantize_q8_1(X))
 

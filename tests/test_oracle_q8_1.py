@@ -147,6 +147,34 @@ def test_product_is_integer_with_unit_scales():
     assert np.array_equal(S, (np.abs(codes.astype(np.int64)) @ np.abs(xi.astype(np.int64))).astype(np.float64))
 
 
+def test_scale_whose_reciprocal_overflows():
+    # largest magnitude 1e-38: d = amax / 127 is below 2^-128, so 1 / d is
+    # +inf and x * (1 / d) is +-inf (x != 0) or NaN (x = 0). The reading
+    # clamps: codes +-127 by sign, 0 for zeros; fp16(d) and fp16(d sum q)
+    # are 0, so every x^ is 0.
+    x = np.zeros(32, np.float32)
+    x[0], x[1], x[5] = 1e-38, -1e-38, 3e-39
+    d32 = np.float32(1e-38) / np.float32(127.0)
+    assert d32 < np.float32(2.0 ** -128)
+    with np.errstate(divide="ignore", over="ignore"):
+        assert np.isinf(np.float32(1.0) / d32)
+    q = oracle.quantize_q8_1(x)
+    d16, s16, c = blocks(q, 1, 32)
+    want = np.zeros(32, np.int64)
+    want[0], want[1], want[5] = 127, -127, 127
+    assert np.array_equal(c[0, 0].astype(np.int64), want)
+    assert d16[0, 0] == 0 and s16[0, 0] == 0
+    assert (oracle.dequant_q8_1(q, 1, 32) == 0).all()
+    # the largest block whose reciprocal still is finite keeps its codes
+    y = np.zeros(32, np.float32)
+    y[0] = np.float32(2.0 ** -128) * np.float32(127.0) * np.float32(1.0 + 2.0 ** -20)
+    y[1] = -y[0] / np.float32(2.0)
+    with np.errstate(divide="ignore", over="ignore"):
+        assert np.isfinite(np.float32(1.0) / (y[0] / np.float32(127.0)))
+    cq = blocks(oracle.quantize_q8_1(y), 1, 32)[2][0, 0].astype(np.int64)
+    assert cq[0] == 127 and cq[1] == -64 and (cq[2:] == 0).all()
+
+
 def test_weights_of_type_q8_1_are_rejected():
     with pytest.raises(Exception):
         oracle.dequant(oracle.TYPE_Q8_1, np.zeros(36, np.uint8), 1, 32)
