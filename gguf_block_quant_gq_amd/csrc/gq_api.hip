@@ -388,6 +388,8 @@ extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64
     total += m;
   }
   if (total == 0) return GQ_OK;
+  // activation rows are int indices in the kernels (as gq_matmul's M)
+  if (total > INT_MAX) return GQ_ERR_SHAPE;
   if (ebytes > INT64_MAX / n_expert) return GQ_ERR_SHAPE;
   if (rows > INT64_MAX / 4 / total || cols > INT64_MAX / 4 / total) return GQ_ERR_SHAPE;
   const int64_t wbytes = ebytes * n_expert, xbytes = total * cols * 4, ybytes = total * rows * 4;

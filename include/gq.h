@@ -281,8 +281,8 @@ int gq_matmul_swiglu(int fmt, const void* W, int64_t rows, int64_t cols,
  * rows, whose tile is chosen for that call alone. Other formats: each
  * expert's block is exactly gq_matmul of that expert's matrix and rows
  * (same kernels, same bits), enqueued in expert order.
- * Experts with no rows are skipped. All counts are checked (>= 0, sums
- * without overflow) before the first launch; n_expert == 0, rows == 0 or no
+ * Experts with no rows are skipped. All counts are checked (>= 0, at most
+ * INT_MAX rows in all, as gq_matmul's M) before the first launch; n_expert == 0, rows == 0 or no
  * rows at all is a no-op. Asynchronous on `stream` (the counts are read
  * during the call and not kept). If a launch fails (GQ_ERR_DEVICE) the
  * launches before it have been enqueued and Y's later blocks are

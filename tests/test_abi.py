@@ -180,6 +180,8 @@ def test_validation_grouped_experts(lib):
     assert _mge(lib, cols=0) == gq.GQ_ERR_SHAPE
     assert _mge(lib, counts=(2, -1, 3)) == gq.GQ_ERR_SHAPE        # every count checked first
     assert _mge(lib, counts=(1 << 62, 1 << 62)) == gq.GQ_ERR_SHAPE
+    # every count an int, but more than INT_MAX activation rows in all
+    assert _mge(lib, counts=(1 << 30, 1 << 30)) == gq.GQ_ERR_SHAPE
     assert _mge(lib, counts=None, n_expert=3) == gq.GQ_ERR_NULL
     assert _mge(lib, counts=(), W=None, X=None, Y=None) == gq.GQ_OK   # no experts
     assert _mge(lib, counts=(0, 0), W=None, X=None, Y=None) == gq.GQ_OK  # no rows
