@@ -34,6 +34,12 @@ int current_cus() {
   return n;
 }
 
+// Rows, columns, activation rows, batch rows and assignments are at most
+// 2^30: the kernels index them with 32-bit ints, and every index they form
+// (an index plus a grid stride, a row plus a tile, a unit count times 32)
+// then stays below 2^31.
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
   return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
@@ -44,7 +50,7 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 int check_shape(int fmt, int64_t rows, int64_t cols, int64_t M, int64_t* rb, int64_t* wbytes) {
   if (gq_row_bytes(fmt, 1) < 0 || fmt == GQ_FMT_Q8_1) return GQ_ERR_FMT;  // Q8_1: activations only
   if (rows < 0 || cols <= 0 || M < 0) return GQ_ERR_SHAPE;
-  if (rows > INT_MAX || cols > INT_MAX || M > INT_MAX) return GQ_ERR_SHAPE;
+  if (rows > kMaxDim || cols > kMaxDim || M > kMaxDim) return GQ_ERR_SHAPE;
   *rb = gq_row_bytes(fmt, cols);
   if (*rb <= 0) return GQ_ERR_SHAPE;
   if (rows > 0 && *rb > INT64_MAX / rows) return GQ_ERR_SHAPE;
@@ -144,7 +150,7 @@ namespace {
 int matvec_common(int fmt, const void* W, int64_t rows, int64_t cols, const float* x, float* y,
                   void* stream, int epi) {
   const int64_t wmul = epi == gq::kEpiSwiglu ? 2 : 1;
-  if (rows > INT_MAX / wmul) return GQ_ERR_SHAPE;
+  if (rows > kMaxDim / wmul) return GQ_ERR_SHAPE;
   int64_t rb = 0, wbytes = 0;
   int st = check_shape(fmt, rows * wmul, cols, 1, &rb, &wbytes);
   if (st != GQ_OK) return st;
@@ -186,7 +192,7 @@ extern "C" int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64
   if (st != GQ_OK) return st;
   // the assignments are the grid's second dimension (an int index)
   if (n_expert < 1 || n_expert > INT_MAX || xk < 1 || xk > INT_MAX || n_assign < 0 ||
-      n_assign > INT_MAX)
+      n_assign > kMaxDim)
     return GQ_ERR_SHAPE;
   if (rows == 0 || n_assign == 0) return GQ_OK;
   if (ebytes > INT64_MAX / n_expert) return GQ_ERR_SHAPE;
@@ -336,7 +342,7 @@ int matmul_entry(int fmt, const void* W, int64_t rows, int64_t cols, const float
                  void* stream, int mode) {
   int64_t rb = 0, wbytes = 0;
   const int64_t wrows = mode == kModeSwiglu ? 2 * rows : rows;
-  if (rows > INT_MAX) return GQ_ERR_SHAPE;
+  if (rows > kMaxDim) return GQ_ERR_SHAPE;
   int st = check_shape(fmt, wrows, cols, M, &rb, &wbytes);
   if (st != GQ_OK) return st;
   if (M > 0 && (rows > INT64_MAX / 4 / M || cols > INT64_MAX / 4 / M)) return GQ_ERR_SHAPE;
@@ -388,8 +394,8 @@ extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64
     total += m;
   }
   if (total == 0) return GQ_OK;
-  // activation rows are int indices in the kernels (as gq_matmul's M)
-  if (total > INT_MAX) return GQ_ERR_SHAPE;
+  // activation rows are int indices in the kernels (bounded as gq_matmul's M)
+  if (total > kMaxDim) return GQ_ERR_SHAPE;
   if (ebytes > INT64_MAX / n_expert) return GQ_ERR_SHAPE;
   if (rows > INT64_MAX / 4 / total || cols > INT64_MAX / 4 / total) return GQ_ERR_SHAPE;
   const int64_t wbytes = ebytes * n_expert, xbytes = total * cols * 4, ybytes = total * rows * 4;
@@ -435,7 +441,7 @@ extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64
 }
 
 extern "C" int gq_quantize_q8_1(const float* x, int64_t n, int64_t cols, void* xq, void* stream) {
-  if (n < 0 || cols <= 0 || n > INT_MAX || cols > INT_MAX) return GQ_ERR_SHAPE;
+  if (n < 0 || cols <= 0 || n > kMaxDim || cols > kMaxDim) return GQ_ERR_SHAPE;
   const int64_t rb = gq_row_bytes(GQ_FMT_Q8_1, cols);
   if (n > 0 && (rb > INT64_MAX / n || cols > INT64_MAX / 4 / n || n * ((cols + 31) / 32) > INT64_MAX / 8))
     return GQ_ERR_SHAPE;

@@ -54,6 +54,13 @@
  *   cache of device properties, filled once. Calls on different streams may
  *   run concurrently.
  *
+ * Sizes
+ *   rows, cols, M, batch rows, expert assignments and the activation rows of
+ *   a grouped product are each at most 2^30 (GQ_ERR_SHAPE beyond; for the
+ *   gate|up forms 2 * rows counts): the kernels index them with 32-bit
+ *   integers, and this bound keeps every index they form below 2^31.
+ *   Byte counts are computed in 64 bits and checked for overflow.
+ *
  * Alignment
  *   Q8_0, Q5_0 and Q6_K W: 2-byte aligned (a row range of such a tensor
  *   starts on any block boundary, and their blocks are 34, 22 and 210 bytes).
@@ -174,7 +181,7 @@ int gq_matvec_swiglu(int fmt, const void* W, int64_t rows, int64_t cols,
  * expert and activation row, bit for bit. An id outside [0, n_expert) reads
  * no weights and fills that assignment's output row with NaN (the ids live
  * on the device, so they cannot be checked before the launch). n_assign is
- * at most INT_MAX (GQ_ERR_SHAPE beyond). Asynchronous on `stream`.
+ * at most 2^30 (GQ_ERR_SHAPE beyond). Asynchronous on `stream`.
  */
 int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, int64_t cols,
                       const float* X, int64_t xk, const int32_t* expid, int64_t n_assign,
@@ -192,7 +199,7 @@ int gq_matvec_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, in
  * of results (same README, "What it runs"). One launch: every batch row is a slice of the matvec grid, and
  * the slices walk the same rows together, so W is streamed from HBM about
  * once. X: [batch, cols] row-major fp32 (4-byte aligned); Y: [batch, rows],
- * overwritten, must not overlap W or X. batch is at most INT_MAX (GQ_ERR_SHAPE
+ * overwritten, must not overlap W or X. batch is at most 2^30 (GQ_ERR_SHAPE
  * beyond); batch == 0 or rows == 0 is a no-op. No workspace. Asynchronous
  * on `stream`.
  */
@@ -282,7 +289,7 @@ int gq_matmul_swiglu(int fmt, const void* W, int64_t rows, int64_t cols,
  * expert's block is exactly gq_matmul of that expert's matrix and rows
  * (same kernels, same bits), enqueued in expert order.
  * Experts with no rows are skipped. All counts are checked (>= 0, at most
- * INT_MAX rows in all, as gq_matmul's M) before the first launch; n_expert == 0, rows == 0 or no
+ * 2^30 rows in all, as gq_matmul's M) before the first launch; n_expert == 0, rows == 0 or no
  * rows at all is a no-op. Asynchronous on `stream` (the counts are read
  * during the call and not kept). If a launch fails (GQ_ERR_DEVICE) the
  * launches before it have been enqueued and Y's later blocks are

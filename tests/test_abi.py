@@ -22,9 +22,32 @@ def _declared_functions():
     return sorted(set(names))
 
 
+class _NoLaunch:
+    """The library with every status-returning entry point wrapped: a call
+    that returns GQ_ERR_DEVICE has passed every host check, so on a machine
+    with a GPU it would have launched a kernel on the fake pointers these
+    tests use. Every call here must be rejected before that point."""
+
+    _PLAIN = {"gq_row_bytes", "gq_status_str"}
+
+    def __init__(self, real):
+        self._real = real
+
+    def __getattr__(self, name):
+        f = getattr(self._real, name)
+        if name in self._PLAIN or not name.startswith("gq_"):
+            return f
+
+        def call(*args):
+            st = f(*args)
+            assert st != gq.GQ_ERR_DEVICE, f"{name}{args} passed every host check"
+            return st
+        return call
+
+
 @pytest.fixture(scope="module")
 def lib():
-    return gq.load_library()
+    return _NoLaunch(gq.load_library())
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -108,6 +131,20 @@ def test_validation_before_any_device_call(lib, call):
     assert call(lib, rows=0, W=None) == gq.GQ_OK
 
 
+def test_validation_size_bound(lib):
+    # rows, cols and M are at most 2^30: one more is rejected before any
+    # pointer is looked at; at the bound the NULL check comes next
+    big = 1 << 30
+    assert _mv(lib, rows=big + 1) == gq.GQ_ERR_SHAPE
+    assert _mv(lib, rows=big, W=None) == gq.GQ_ERR_NULL
+    assert _mv(lib, fmt=8, cols=big + 1) == gq.GQ_ERR_SHAPE
+    assert _mv(lib, fmt=8, cols=big, W=None) == gq.GQ_ERR_NULL
+    assert _mm(lib, M=big + 1) == gq.GQ_ERR_SHAPE
+    assert _mm(lib, M=big, X=None) == gq.GQ_ERR_NULL
+    assert _mvs(lib, rows=big // 2 + 1) == gq.GQ_ERR_SHAPE      # 2 * rows weight rows
+    assert _dq(lib, rows=big + 1) == gq.GQ_ERR_SHAPE
+
+
 def test_validation_vectors(lib):
     assert _mv(lib, x=None) == gq.GQ_ERR_NULL
     assert _mv(lib, y=None) == gq.GQ_ERR_NULL
@@ -129,7 +166,7 @@ def test_validation_vectors(lib):
     # the gate|up epilogue reads 2 * rows weight rows: an output placed just
     # past rows * row_bytes still overlaps W; 2^30 rows overflow the row index
     assert _mvs(lib, rows=4, y=W_OK + 4 * 144) == gq.GQ_ERR_OVERLAP
-    assert _mv(lib, rows=4, y=W_OK + 4 * 144) != gq.GQ_ERR_OVERLAP
+    assert _mv(lib, rows=4, y=W_OK + 4 * 144 - 4) == gq.GQ_ERR_OVERLAP
     assert _mvs(lib, rows=1 << 30) == gq.GQ_ERR_SHAPE
     assert _mva(lib, y=None) == gq.GQ_ERR_NULL
     assert _mva(lib, y=W_OK + 8) == gq.GQ_ERR_OVERLAP
@@ -140,7 +177,8 @@ def test_validation_vectors(lib):
 
 def test_validation_batch(lib):
     assert _mb(lib, M=-1) == gq.GQ_ERR_SHAPE
-    assert _mb(lib, M=2 ** 31) == gq.GQ_ERR_SHAPE    # past an int grid index
+    assert _mb(lib, M=2 ** 30 + 1) == gq.GQ_ERR_SHAPE    # past the 2^30 size bound
+    assert _mb(lib, M=2 ** 30, Y=None) == gq.GQ_ERR_NULL
     assert _mb(lib, M=65536, Y=None) == gq.GQ_ERR_NULL
     assert _mb(lib, M=0, X=None, Y=None) == gq.GQ_OK
     assert _mb(lib, X=None) == gq.GQ_ERR_NULL
@@ -180,8 +218,8 @@ def test_validation_grouped_experts(lib):
     assert _mge(lib, cols=0) == gq.GQ_ERR_SHAPE
     assert _mge(lib, counts=(2, -1, 3)) == gq.GQ_ERR_SHAPE        # every count checked first
     assert _mge(lib, counts=(1 << 62, 1 << 62)) == gq.GQ_ERR_SHAPE
-    # every count an int, but more than INT_MAX activation rows in all
-    assert _mge(lib, counts=(1 << 30, 1 << 30)) == gq.GQ_ERR_SHAPE
+    # every count an int, but more than 2^30 activation rows in all
+    assert _mge(lib, counts=(1 << 29, (1 << 29) + 1)) == gq.GQ_ERR_SHAPE
     assert _mge(lib, counts=None, n_expert=3) == gq.GQ_ERR_NULL
     assert _mge(lib, counts=(), W=None, X=None, Y=None) == gq.GQ_OK   # no experts
     assert _mge(lib, counts=(0, 0), W=None, X=None, Y=None) == gq.GQ_OK  # no rows
@@ -206,10 +244,10 @@ def test_validation_experts(lib):
     assert _mx(lib, n_expert=0) == gq.GQ_ERR_SHAPE
     assert _mx(lib, xk=0) == gq.GQ_ERR_SHAPE
     assert _mx(lib, n_assign=-1) == gq.GQ_ERR_SHAPE
-    assert _mx(lib, n_assign=2 ** 31) == gq.GQ_ERR_SHAPE
+    assert _mx(lib, n_assign=2 ** 30 + 1) == gq.GQ_ERR_SHAPE
     assert _mx(lib, n_assign=65536, Y=None) == gq.GQ_ERR_NULL
     # X rows times cols overflowing 64 bits
-    assert _mx(lib, n_assign=2 ** 31 - 1, xk=1, cols=2 ** 31 - 1, rows=1) == gq.GQ_ERR_SHAPE
+    assert _mx(lib, n_assign=2 ** 30, xk=1, cols=2 ** 30 + 1, rows=1) == gq.GQ_ERR_SHAPE
     assert _mx(lib, cols=0) == gq.GQ_ERR_SHAPE
     assert _mx(lib, n_assign=0, W=None, expid=None) == gq.GQ_OK
     assert _mx(lib, rows=0, W=None) == gq.GQ_OK
@@ -226,7 +264,9 @@ def test_split_layout_row_bytes_and_repack_validation(lib, oracle):
     for cols in (1, 31, 32, 33, 896, 4096, 14336):
         assert gq.gq_row_bytes(1008, cols) == oracle.row_bytes(1008, cols)
     rp = lib.gq_q8_0_split_repack
-    assert rp(W_OK, 4, 896, Y_OK, None) != gq.GQ_ERR_ALIGN           # passes the host checks
+    # a 2-byte aligned W passes the alignment check (the overlap check after
+    # it fires; no call here passes every check, so none would launch)
+    assert rp(W_OK + 2, 4, 896, W_OK + 12, None) == gq.GQ_ERR_OVERLAP
     assert rp(W_OK + 1, 4, 896, Y_OK, None) == gq.GQ_ERR_ALIGN       # W: 2-byte aligned
     assert rp(W_OK, 4, 896, Y_OK + 2, None) == gq.GQ_ERR_ALIGN       # out: 4-byte aligned
     assert rp(None, 4, 896, Y_OK, None) == gq.GQ_ERR_NULL
