@@ -541,9 +541,7 @@ hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi,
     return dispatch_split(a, cus, s, epi, ex);
   }
   // K-quants: four units per 256-weight super-block
-#ifndef GQ_Q4K_OFF
   if (fmt == kFmtQ4_K && gemv_q4k_supports(a, cus, ex)) return launch_gemv_q4k(a, cus, s, epi, ex);
-#endif
   a.units = 4 * ((a.cols + 255) / 256);
   if (fmt == kFmtQ5_K) return dispatch<Q5KUnit>(a, cus, s, epi, ex);
   if (fmt == kFmtQ6_K) return dispatch<Q6KUnit>(a, cus, s, epi, ex);

@@ -171,18 +171,9 @@ struct Q4kArgs {
   int nlo, rem;
 };
 
-// Output row of item k of row group g: the group's rows are contiguous
-// (GQ_Q4K_CONTIG) or dealt round-robin over the ng groups.
-#ifndef GQ_Q4K_CONTIG
-#define GQ_Q4K_CONTIG 0
-#endif
-#ifndef GQ_Q4K_GLOBAL
-#define GQ_Q4K_GLOBAL 0
-#endif
-__device__ __forceinline__ int item_row(int g, int k, int ng, int nlo, int rem) {
-  if (GQ_Q4K_CONTIG) return g * nlo + (g < rem ? g : rem) + k;
-  return g + k * ng;
-}
+// Output row of item k of row group g: rows are dealt round-robin over the
+// ng groups of the grid.
+__device__ __forceinline__ int item_row(int g, int k, int ng) { return g + k * ng; }
 
 template <int NW, int H, int D, int EPI, bool EXPERTS>
 __global__ __launch_bounds__(NW * 64) void gemv_q4k_kernel(Q4kArgs<EXPERTS> q4) {
@@ -229,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4k_kernel(Q4kArgs<EXPERTS> q4) 
   const uint32_t voff_h = (uint32_t)(u_ld >> 2) * kQ4KBytes;
   const uint32_t voff_q = voff_h + 16u + 32u * (uint32_t)(u_ld & 3);
   auto row_of = [&](int k) {  // item k's output row, clamped to a real one
-    const int r = item_row(gi, k < n ? k : n - 1, ng, q4.nlo, q4.rem);
+    const int r = item_row(gi, k < n ? k : n - 1, ng);
     return r < a.rows ? (r < 0 ? 0 : r) : a.rows - 1;
   };
   auto row_off = [&](int k) { return row_of(k) * row_bytes; };
@@ -239,17 +230,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4k_kernel(Q4kArgs<EXPERTS> q4) 
     const int so = row_off(k);
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
-#if GQ_Q4K_GLOBAL
-      const uint8_t* rp = a.W + (int64_t)i * a.rows * a.row_bytes + so;
-      ring[slot][i].h = load_u32x4(rp + voff_h);
-      ring[slot][i].q0 = load_u32x4(rp + voff_q);
-      ring[slot][i].q1 = load_u32x4(rp + voff_q + 16u);
-#else
       const __amdgpu_buffer_rsrc_t rs = i == 0 ? rs0 : rs1;
       ring[slot][i].h = buf_load16(rs, voff_h, so);
       ring[slot][i].q0 = buf_load16(rs, voff_q, so);
       ring[slot][i].q1 = buf_load16(rs, voff_q + 16u, so);
-#endif
     }
   };
 
@@ -273,7 +257,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4k_kernel(Q4kArgs<EXPERTS> q4) 
       const int g = t / kRing, sl = t % kRing;
       const int gg = gi0 + g;
       if (sl < cnt && k0 + sl < q4.nlo + (gg < q4.rem ? 1 : 0)) {
-        const int rr = item_row(gg, k0 + sl, ng, q4.nlo, q4.rem);
+        const int rr = item_row(gg, k0 + sl, ng);
         float v[RI];
 #pragma unroll
         for (int i = 0; i < RI; ++i) {
@@ -293,7 +277,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4k_kernel(Q4kArgs<EXPERTS> q4) 
 #pragma unroll
     for (int i = 0; i < RI; ++i) v[i] = group_sum_last<64>(v[i]);
     if constexpr (H == 1) {
-      if (lane == 63) store_row<EPI>(a.y, item_row(gi, k, ng, q4.nlo, q4.rem), v[0], v[RI - 1]);
+      if (lane == 63) store_row<EPI>(a.y, item_row(gi, k, ng), v[0], v[RI - 1]);
     } else {
       const int sl = k % kRing;
       if (lane == 63) {
@@ -315,8 +299,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4k_kernel(Q4kArgs<EXPERTS> q4) 
         w[i] = group_sum_last<64>(w[i]);
       }
       if (lane == 63) {
-        store_row<EPI>(a.y, item_row(gi, k, ng, q4.nlo, q4.rem), v[0], v[RI - 1]);
-        store_row<EPI>(a.y, item_row(gi, k + 1, ng, q4.nlo, q4.rem), w[0], w[RI - 1]);
+        store_row<EPI>(a.y, item_row(gi, k, ng), v[0], v[RI - 1]);
+        store_row<EPI>(a.y, item_row(gi, k + 1, ng), w[0], w[RI - 1]);
       }
     } else {
       finish(k, v);

@@ -417,7 +417,6 @@ hipError_t launch_reg_any(const Q8aArgs& a, int cus, hipStream_t s) {
 hipError_t launch_gemv_q8a(int fmt, const uint8_t* W, int64_t row_bytes, int rows, int cols,
                            const uint8_t* xq, float* y, int cus, hipStream_t s) {
   Q8aArgs a{W, xq, y, row_bytes, rows, cols, (cols + 31) / 32, 0, 0};
-#ifndef GQ_Q8A_LDS_ONLY
   if (fmt == kFmtQ4_K && 4 * ((cols + 255) / 256) <= 256) {
     a.units = 4 * ((cols + 255) / 256);
     return launch_reg_any<Q8aQ4K>(a, cus, s);
@@ -426,7 +425,6 @@ hipError_t launch_gemv_q8a(int fmt, const uint8_t* W, int64_t row_bytes, int row
     a.units = a.nb;
     return launch_reg_any<Q8aQ8>(a, cus, s);
   }
-#endif
   const int pairs = (rows + 1) / 2;
   const int grid = (int)min((int64_t)(pairs + 3) / 4, (int64_t)cus * GQ_Q8A_WG_PER_CU);
   if (fmt == kFmtQ4_K) {
