@@ -142,10 +142,6 @@ __device__ __forceinline__ u32x2 buf_b64(__amdgpu_buffer_rsrc_t rs, int voff, in
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0));
 }
 
-__device__ __forceinline__ float buf_b32f(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
-}
-
 // One product (or one group of a grouped product): W rows, X rows, Y rows.
 struct MmTile {
   int64_t w_off;   // byte offset of the group's weight tensor from W

@@ -279,6 +279,8 @@ __device__ __forceinline__ float group_sum_last(float v) {
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, void* lds, int voff, int soff) {
 #if __HIP_DEVICE_COMPILE__
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#else
+  (void)rs, (void)lds, (void)voff, (void)soff;
 #endif
 }
 

@@ -26,7 +26,7 @@ struct Q8Unit {
 
   __device__ static int units_per_row(int cols) { return (cols + 31) / 32; }
 
-  __device__ static bool valid(int unit, int units, int cols) {
+  __device__ static bool valid(int unit, int units, int /*cols*/) {
     return unit < units;  // every block holds at least one column
   }
 
