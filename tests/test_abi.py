@@ -16,7 +16,8 @@ def _declared_functions():
     names = []
     for h in os.listdir(os.path.join(ROOT, "include")):
         if h.endswith(".h"):
-            text = open(os.path.join(ROOT, "include", h)).read()
+            with open(os.path.join(ROOT, "include", h)) as f:
+                text = f.read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
             names += re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(gq_\w+)\s*\(", text, re.M)
     return sorted(set(names))

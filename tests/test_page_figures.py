@@ -6,11 +6,12 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.txt")
 
 def _figures():
     out = {}
-    for line in open(GOLDEN):
-        line = line.split("#", 1)[0].strip()
-        if line:
-            k, v = (s.strip() for s in line.split("="))
-            out[k] = float(v)
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = (s.strip() for s in line.split("="))
+                out[k] = float(v)
     return out
 
 
