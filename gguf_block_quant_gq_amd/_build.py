@@ -85,6 +85,29 @@ def build(verbose: bool = False, incremental: bool = False, sanitize: bool = Fal
     return lib
 
 
+# The plain C client of the C ABI (tests/c_client.c): gcc, C11, linked
+# against libgq.so (found next to the package through the run path) and the
+# HIP runtime. The binary sits beside its source and is git-ignored.
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "gq_c_client")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror",
+           "-D__HIP_PLATFORM_AMD__", f"-I{os.path.join(ROCM, 'include')}",
+           f"-I{os.path.join(ROOT, 'include')}", C_CLIENT_SRC, "-o", C_CLIENT + ".tmp",
+           f"-L{HERE}", "-lgq", f"-L{os.path.join(ROCM, 'lib')}", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../gguf_block_quant_gq_amd", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed for {C_CLIENT_SRC}:\n{r.stdout}{r.stderr}")
+    os.replace(C_CLIENT + ".tmp", C_CLIENT)
+    return C_CLIENT
+
+
 if __name__ == "__main__":
     import sys
     print(build(verbose=True, incremental="--incremental" in sys.argv, sanitize="--sanitize" in sys.argv))

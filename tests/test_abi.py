@@ -336,3 +336,15 @@ def test_validation_matmul_modes(lib):
     # the Q4_K matrix-core bound holds per half
     far = 1 << 40
     assert lib.gq_matmul_swiglu(12, W_OK, 16, 1 << 23, far, 16, 2 * far, None) == gq.GQ_ERR_SHAPE
+
+
+def test_c_client_compiles_as_c11():
+    """The header and the C client compile as strict C11 with gcc (the client
+    itself runs on the GPU in test_gpu_c_client.py)."""
+    import subprocess
+    src = os.path.join(ROOT, "tests", "c_client.c")
+    r = subprocess.run(["gcc", "-std=c11", "-fsyntax-only", "-Wall", "-Wextra", "-Werror",
+                        "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                        f"-I{os.path.join(ROOT, 'include')}", src],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
