@@ -1,0 +1,98 @@
+"""Randomized sweep of gq_matmul (store and accumulate), gq_matvec and the
+split Q8_0 repack on the GPU, for a time budget: every case draws a format,
+rows (1..2999), columns (up to 70 blocks or super-blocks, ragged or whole)
+and activation rows M (1..200) from a seeded generator, checks a sample of
+output rows against the f64 oracle at 2e-4 * sum |w x| and that nothing is
+written past the outputs. Prints each case before running it and exits 1 on
+any failure. Not collected by pytest (the seeded parity tests are); run it on
+a machine with a GPU:
+
+    python tests/fuzz.py [--seconds 240] [--seed 11]
+"""
+import argparse
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(HERE))
+sys.path.insert(0, HERE)
+
+import numpy as np  # noqa: E402
+
+FORMATS = (8, 12, 6, 13, 14, 1008)
+M_CHOICES = (1, 2, 3, 7, 15, 16, 17, 31, 64, 65, 100, 200)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--seconds", type=float, default=240.0)
+    ap.add_argument("--seed", type=int, default=11)
+    args = ap.parse_args()
+
+    import torch
+
+    import gguf_block_quant_gq_amd as gq
+    import oracle
+    import synth
+    from helpers import oracle_threads, sentinel_buffer, to_dev, to_host
+
+    torch.cuda.set_device(0)
+    failures = 0
+
+    def within(got, ref, S, what, info):
+        nonlocal failures
+        ok = np.abs(got.astype(np.float64) - ref) <= 2e-4 * S + 1e-30
+        if not ok.all():
+            failures += 1
+            i = tuple(np.argwhere(~ok)[0])
+            print(f"  FAIL {what} {info} at {i}: got {got[i]} ref {ref[i]} S {S[i]}", flush=True)
+
+    def pad_ok(buf, n, what, info):
+        nonlocal failures
+        if not np.isnan(to_host(buf)[n:]).all():
+            failures += 1
+            print(f"  FAIL {what} {info}: wrote past the output", flush=True)
+
+    t0, n = time.time(), 0
+    while time.time() - t0 < args.seconds:
+        rng = np.random.default_rng([args.seed, n])
+        fmt = FORMATS[int(rng.integers(0, len(FORMATS)))]
+        base = 8 if fmt == 1008 else fmt
+        qk = 256 if base in (12, 13, 14) else 32
+        cols = int(rng.integers(1, 70 * qk))
+        if fmt == 12 and rng.random() < 0.5:
+            cols = (cols + 3) // 4 * 4   # the fp16 matrix-core route needs cols % 4 == 0
+        rows = int(rng.integers(1, 3000))
+        M = int(rng.choice(M_CHOICES))
+        acc = M > 1 and rng.random() < 0.5
+        info = f"case {n} fmt={fmt} rows={rows} cols={cols} M={M}{' acc' if acc else ''}"
+        print(info, flush=True)
+        W = synth.weights(base, rows, cols, rng)
+        X = synth.activations((M, cols), rng)
+        Wd, Xd = to_dev(W), to_dev(X)
+        if fmt == 1008:
+            Wd = gq.gq_q8_0_split_repack(Wd, rows, cols)
+        idx = np.unique(np.concatenate([rng.integers(0, rows, 12), [0, rows - 1]]))
+        ref, S = oracle.matmul(base, oracle.select_rows(base, W, cols, idx), idx.size, cols, X,
+                               nthreads=oracle_threads())
+        Y = sentinel_buffer(M * rows)
+        if acc:
+            Y[:M * rows].zero_()
+            gq.gq_matmul_acc(fmt, Wd, rows, cols, Xd, Y[:M * rows])
+        else:
+            gq.gq_matmul(fmt, Wd, rows, cols, Xd, Y=Y[:M * rows])
+        pad_ok(Y, M * rows, "matmul", info)
+        within(to_host(Y)[:M * rows].reshape(M, rows)[:, idx], ref, S, "matmul", info)
+        y = sentinel_buffer(rows)
+        gq.gq_matvec(fmt, Wd, rows, cols, Xd[M - 1], y=y[:rows])
+        pad_ok(y, rows, "matvec", info)
+        within(to_host(y)[:rows][idx], ref[M - 1], S[M - 1], "matvec", info)
+        n += 1
+    print(f"fuzz done: {n} cases, {failures} failures, {time.time() - t0:.0f} s, seed {args.seed}",
+          flush=True)
+    return 1 if failures else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
