@@ -477,8 +477,11 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
   f32x4 xr[SX][CW][4];
   WStage<R> ws[SW];
 
-  // the group's k-th super-block (k past the last re-reads the last)
-  auto sb_of = [&](int k) { return wk + KS * (k < nk ? k : nk - 1); };
+  // the group's k-th super-block (k past the last re-reads the last; a group
+  // with no super-block -- fewer super-blocks than groups -- re-reads
+  // super-block 0, so that the scalar part of every weight load's offset,
+  // which the buffer's range check does not cover, is a real position)
+  auto sb_of = [&](int k) { return nk > 0 ? wk + KS * (k < nk ? k : nk - 1) : 0; };
 
   // requests for super-block sb (the column offset is clamped so that a
   // ragged row's tail stays inside the buffer)

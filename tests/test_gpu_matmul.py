@@ -160,6 +160,22 @@ def test_many_activation_rows(gq, oracle, fmt, rows):
     assert_within_tolerance(Y[idx], ref, S, f"many activation rows fmt={fmt}")
 
 
+@pytest.mark.parametrize("rows,cols,M", [
+    (2464, 232, 100),   # 64 x 16 tiles, k split in four: one super-block
+    (2926, 292, 100),   # two super-blocks
+    (2373, 664, 100),   # three super-blocks
+    (14336, 256, 64),   # 128 x 32 tiles, k split in two: one super-block
+])
+def test_q4k_fewer_super_blocks_than_k_groups(gq, oracle, rows, cols, M):
+    """Q4_K products on the tiles that split the super-blocks over wave
+    groups, with fewer super-blocks than groups: the idle groups must not
+    disturb the result (every output against the oracle)."""
+    rng = synth.rng_for(615, rows + cols)
+    W = synth.weights(12, rows, cols, rng)
+    X = synth.activations((M, cols), rng)
+    _check(gq, oracle, 12, W, rows, cols, X, "fewer super-blocks than k groups")
+
+
 def test_q4k_wide_dynamic_range(gq, oracle):
     """Q4_K on the fp16 matrix cores: activations whose magnitudes span 2^-113
     .. 2^100 across rows and super-blocks, each within 2^13 of the largest in
