@@ -78,6 +78,69 @@ __device__ __forceinline__ h8 weight_operand(uint32_t w0, uint32_t w1, h2 sc, h2
   return as_h8(r[0], r[1], r[2], r[3]);
 }
 
+// The super-block layouts these kernels take. Q4_K and Q5_K share the
+// header (fp16 d and dmin, then the twelve 6-bit scale/min bytes) and the
+// nibble layout; Q5_K puts 32 bytes of fifth bits between them (bit 2g + h
+// of byte l is bit 4 of weight 64g + 32h + l). Its codes reach 31 and
+// sc * code 63 * 31 = 1953, still an exact fp16 integer, and the packed fma
+// that forms sc * code from the biased code (up to 63 * 1055) rounds only
+// its result, so the operand stays exact.
+struct MmQ4K {
+  static constexpr int kBytes = 144, kCodes = 16;
+  static constexpr bool kQh = false;
+};
+struct MmQ5K {
+  static constexpr int kBytes = 176, kCodes = 48;
+  static constexpr bool kQh = true;
+};
+
+// Q5_K: the Q4_K operand of sub-block J with the fifth bits merged in: qh0 /
+// qh1 are the fifth-bit bytes of the same 8 code bytes (w0 / w1), and bit J
+// of each is moved to bit 4 of its code byte.
+template <int J>
+__device__ __forceinline__ h8 weight_operand5(uint32_t w0, uint32_t w1, uint32_t qh0, uint32_t qh1,
+                                              h2 sc, h2 nsc) {
+  constexpr uint32_t kMagic = 0x64646464u;
+  constexpr int H = J & 1;
+  const uint32_t b0 = J <= 4 ? qh0 << (4 - J) : qh0 >> (J - 4);
+  const uint32_t b1 = J <= 4 ? qh1 << (4 - J) : qh1 >> (J - 4);
+  const uint32_t n0 = ((H ? w0 >> 4 : w0) & 0x0F0F0F0Fu) | (b0 & 0x10101010u);
+  const uint32_t n1 = ((H ? w1 >> 4 : w1) & 0x0F0F0F0Fu) | (b1 & 0x10101010u);
+  uint32_t p[4];
+  p[0] = __builtin_amdgcn_perm(kMagic, n0, 0x04010400u);  // codes 0, 1
+  p[1] = __builtin_amdgcn_perm(kMagic, n0, 0x04030402u);  // codes 2, 3
+  p[2] = __builtin_amdgcn_perm(kMagic, n1, 0x04010400u);  // codes 4, 5
+  p[3] = __builtin_amdgcn_perm(kMagic, n1, 0x04030402u);  // codes 6, 7
+  uint32_t r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    r[k] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(h2, p[k]), sc, nsc));
+  return as_h8(r[0], r[1], r[2], r[3]);
+}
+
+// The weight operand of sub-block J for either layout.
+template <class Fm, int J>
+__device__ __forceinline__ h8 weight_op(u32x2 cw, u32x2 qh, h2 sc, h2 nsc) {
+  if constexpr (Fm::kQh) return weight_operand5<J>(cw.x, cw.y, qh.x, qh.y, sc, nsc);
+  else return weight_operand<J & 1>(cw.x, cw.y, sc, nsc);
+}
+
+// weight_op for a sub-block index that is a constant once the loop over the
+// eight sub-blocks is unrolled.
+template <class Fm>
+__device__ __forceinline__ h8 weight_op_j(int j, u32x2 cw, u32x2 qh, h2 sc, h2 nsc) {
+  switch (j) {
+    case 0: return weight_op<Fm, 0>(cw, qh, sc, nsc);
+    case 1: return weight_op<Fm, 1>(cw, qh, sc, nsc);
+    case 2: return weight_op<Fm, 2>(cw, qh, sc, nsc);
+    case 3: return weight_op<Fm, 3>(cw, qh, sc, nsc);
+    case 4: return weight_op<Fm, 4>(cw, qh, sc, nsc);
+    case 5: return weight_op<Fm, 5>(cw, qh, sc, nsc);
+    case 6: return weight_op<Fm, 6>(cw, qh, sc, nsc);
+    default: return weight_op<Fm, 7>(cw, qh, sc, nsc);
+  }
+}
+
 // Two six-bit fields (bits 0-5 and 16-21) as an exact fp16 pair.
 __device__ __forceinline__ h2 pair_f16(uint32_t two_fields) {
   const h2 v = __builtin_bit_cast(h2, two_fields | 0x64006400u);
@@ -176,6 +239,7 @@ template <int WR>
 struct Stage {
   u32x4 hd[WR];
   u32x2 cw[WR][4];
+  u32x2 qh[WR];  // Q5_K: the fifth-bit bytes of the lane's 8 code bytes
 };
 
 // An activation tile (16 rows x the 256 columns of one super-block) in LDS:
@@ -191,7 +255,7 @@ constexpr int kXTile = 16 * kXRow;
 // straight from memory would make every instruction touch 16 rows whose
 // stride (cols * 4 bytes, a multiple of 4 KB for 4096 or 14336 columns)
 // maps them all to one L2 channel.
-template <int WR, int KW, int EPI>
+template <class Fm, int WR, int KW, int EPI>
 __global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
   __shared__ f32x4 red[KW][WR][64];
   __shared__ __attribute__((aligned(16))) uint8_t xbuf[KW][2][kXTile];
@@ -235,9 +299,11 @@ __global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
     for (int r = 0; r < 16; ++r) load_lds16(xrs, &xbuf[wave][slot][r * kXRow], r * a.cols * 4 + col, 0);
 #pragma unroll
     for (int t = 0; t < WR; ++t) {
-      st.hd[t] = buf_b128(wrs, wv[t], sb * kQ4KBytes);
+      st.hd[t] = buf_b128(wrs, wv[t], sb * Fm::kBytes);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) st.cw[t][g] = buf_b64(wrs, wv[t] + 16 + 32 * g + 8 * q, sb * kQ4KBytes);
+      for (int g = 0; g < 4; ++g)
+        st.cw[t][g] = buf_b64(wrs, wv[t] + Fm::kCodes + 32 * g + 8 * q, sb * Fm::kBytes);
+      if constexpr (Fm::kQh) st.qh[t] = buf_b64(wrs, wv[t] + 16 + 8 * q, sb * Fm::kBytes);
     }
     issue_fence();
   };
@@ -312,7 +378,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
       for (int t = 0; t < WR; ++t) {
         const u32x2 c = st.cw[t][j >> 1];
         const h2 sc = {h[t].sc[j], h[t].sc[j]}, nsc = {h[t].nsc[j], h[t].nsc[j]};
-        const h8 wop = (j & 1) ? weight_operand<1>(c.x, c.y, sc, nsc) : weight_operand<0>(c.x, c.y, sc, nsc);
+        const h8 wop = weight_op_j<Fm>(j, c, st.qh[t], sc, nsc);
         p1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, wop, p1[t], 0, 0, 0);
         p1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, wop, p1[t], 0, 0, 0);
       }
@@ -410,13 +476,14 @@ template <int R>
 struct WStage {
   u32x4 hd[R];
   u32x2 cw[R][4];
+  u32x2 qh[R];  // Q5_K: the fifth-bit bytes of the lane's 8 code bytes
 };
 
 __device__ __forceinline__ f32x4 buf_f32x4(__amdgpu_buffer_rsrc_t rs, int voff) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
 }
 
-template <int R, int C, int D, int KS, int RS, int EPI>
+template <class Fm, int R, int C, int D, int KS, int RS, int EPI>
 __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
   static_assert(RS == 4 || (RS == 8 && C % 2 == 0), "row groups");
   constexpr int CW = C * 4 / RS;          // m-tiles each wave converts
@@ -496,9 +563,11 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
       for (int v = 0; v < 4; ++v) xr[xslot][c][v] = buf_f32x4(xrs, xv[c] + col[v]);
 #pragma unroll
     for (int t = 0; t < R; ++t) {
-      ws[wslot].hd[t] = buf_b128(wrs, wv[t], sb * kQ4KBytes);
+      ws[wslot].hd[t] = buf_b128(wrs, wv[t], sb * Fm::kBytes);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) ws[wslot].cw[t][g] = buf_b64(wrs, wv[t] + 16 + 32 * g + 8 * q, sb * kQ4KBytes);
+      for (int g = 0; g < 4; ++g)
+        ws[wslot].cw[t][g] = buf_b64(wrs, wv[t] + Fm::kCodes + 32 * g + 8 * q, sb * Fm::kBytes);
+      if constexpr (Fm::kQh) ws[wslot].qh[t] = buf_b64(wrs, wv[t] + 16 + 8 * q, sb * Fm::kBytes);
     }
     issue_fence();
   };
@@ -583,7 +652,7 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
       for (int t = 0; t < R; ++t) {
         const u32x2 cw = ws[wslot].cw[t][j >> 1];
         const h2 sc = {h[t].sc[j], h[t].sc[j]}, nsc = {h[t].nsc[j], h[t].nsc[j]};
-        const h8 wop = (j & 1) ? weight_operand<1>(cw.x, cw.y, sc, nsc) : weight_operand<0>(cw.x, cw.y, sc, nsc);
+        const h8 wop = weight_op_j<Fm>(j, cw, ws[wslot].qh[t], sc, nsc);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
           ph[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[c], wop, ph[t][c], 0, 0, 0);
@@ -681,16 +750,16 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
 #define GQ_MM_KW 4  // waves per workgroup (splitting the super-blocks)
 #endif
 
-template <int WR, int EPI>
+template <class Fm, int WR, int EPI>
 hipError_t launch(const MmArgs& a, int gx, int gy, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_q4k_kernel<WR, GQ_MM_KW, EPI>), dim3(gx, gy), dim3(GQ_MM_KW * 64), 0, s, a);
+  hipLaunchKernelGGL((gemm_q4k_kernel<Fm, WR, GQ_MM_KW, EPI>), dim3(gx, gy), dim3(GQ_MM_KW * 64), 0, s, a);
   return hipGetLastError();
 }
 
-template <int R, int C, int D, int KS, int RS, int EPI>
+template <class Fm, int R, int C, int D, int KS, int RS, int EPI>
 hipError_t launch_xs(const MmArgs& a, int gy, hipStream_t s) {
   const int gx = (a.rows + 16 * RS * R - 1) / (16 * RS * R);
-  hipLaunchKernelGGL((gemm_q4k_xs_kernel<R, C, D, KS, RS, EPI>), dim3(gx, gy), dim3(64 * RS * KS), 0, s, a);
+  hipLaunchKernelGGL((gemm_q4k_xs_kernel<Fm, R, C, D, KS, RS, EPI>), dim3(gx, gy), dim3(64 * RS * KS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -733,7 +802,7 @@ bool gemm_q4k_fits(int64_t rows, int64_t cols, int64_t row_bytes) {
 // (down M = 16: 30 us).
 namespace {
 
-template <int EPI>
+template <class Fm, int EPI>
 hipError_t launch_gemm_q4k_epi(MmArgs& m, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
                                int n_groups, int64_t group_w_bytes, int cus, hipStream_t s) {
   const int64_t fill = (int64_t)cus * 7 / 8;
@@ -744,20 +813,34 @@ hipError_t launch_gemm_q4k_epi(MmArgs& m, const GemmArgs& a, const int64_t* grou
     if (gy == 0) return hipSuccess;
     return launch(m, gy, s);
   };
-  if (grid(256, 64) >= fill) return run_xs(launch_xs<2, 4, 1, 1, 8, EPI>, 64);
-  if (grid(256, 32) >= fill) return run_xs(launch_xs<2, 2, 2, 1, 8, EPI>, 32);
-  if (grid(128, 32) >= fill) return run_xs(launch_xs<1, 2, 1, 2, 8, EPI>, 32);
-  if (grid(64, 16) >= fill) return run_xs(launch_xs<1, 1, 1, 4, 4, EPI>, 16);
+  if (grid(256, 64) >= fill) return run_xs(launch_xs<Fm, 2, 4, 1, 1, 8, EPI>, 64);
+  if (grid(256, 32) >= fill) return run_xs(launch_xs<Fm, 2, 2, 2, 1, 8, EPI>, 32);
+  if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 2, 8, EPI>, 32);
+  if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
   const int gy = build_groups(m, group_m, group_off, n_groups, group_w_bytes, 16);
   if (gy < 0) return hipErrorInvalidValue;
   if (gy == 0) return hipSuccess;
-  if (grid(32, 16) >= fill) return launch<2, EPI>(m, (a.rows + 31) / 32, gy, s);
-  return launch<1, EPI>(m, (a.rows + 15) / 16, gy, s);
+  if (grid(32, 16) >= fill) return launch<Fm, 2, EPI>(m, (a.rows + 31) / 32, gy, s);
+  return launch<Fm, 1, EPI>(m, (a.rows + 15) / 16, gy, s);
+}
+
+template <class Fm>
+hipError_t launch_gemm_fmt(MmArgs& m, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
+                           int n_groups, int64_t group_w_bytes, int cus, hipStream_t s, int epi) {
+  switch (epi) {
+    case kMmStore:
+      return launch_gemm_q4k_epi<Fm, kMmStore>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
+    case kMmAcc:
+      return launch_gemm_q4k_epi<Fm, kMmAcc>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
+    case kMmSiluMul:
+      return launch_gemm_q4k_epi<Fm, kMmSiluMul>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_gemm_q4k(const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
+hipError_t launch_gemm_q4k(int fmt, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
                            int n_groups, int64_t group_w_bytes, int cus, hipStream_t s, int epi) {
   MmArgs m{};
   m.W = a.W;
@@ -767,13 +850,9 @@ hipError_t launch_gemm_q4k(const GemmArgs& a, const int64_t* group_m, const int6
   m.rows = a.rows;
   m.cols = a.cols;
   m.nsb = (a.cols + 255) / 256;
-  switch (epi) {
-    case kMmStore: return launch_gemm_q4k_epi<kMmStore>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
-    case kMmAcc: return launch_gemm_q4k_epi<kMmAcc>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
-    case kMmSiluMul:
-      return launch_gemm_q4k_epi<kMmSiluMul>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
-    default: return hipErrorInvalidValue;
-  }
+  if (fmt == kFmtQ4_K) return launch_gemm_fmt<MmQ4K>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
+  if (fmt == kFmtQ5_K) return launch_gemm_fmt<MmQ5K>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gq

@@ -265,9 +265,11 @@ extern "C" int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, v
 
 namespace {
 
-// Q4_K products run on the fp16 matrix cores when rows are whole groups of
-// four floats, else on the fp32 matrix cores.
-bool q4k_matrix_cores(int fmt, int64_t cols) { return fmt == GQ_FMT_Q4_K && cols % 4 == 0; }
+// Q4_K and Q5_K products run on the fp16 matrix cores when rows are whole
+// groups of four floats, else on the fp32 matrix cores.
+bool q4k_matrix_cores(int fmt, int64_t cols) {
+  return (fmt == GQ_FMT_Q4_K || fmt == GQ_FMT_Q5_K) && cols % 4 == 0;
+}
 
 bool batched_matvec(int64_t M, int64_t rows, int64_t cols) {
   return M > 1 && M < 16 && rows * cols <= kBatchMaxWork / M;
@@ -290,7 +292,7 @@ int matrix_product(int fmt, const uint8_t* W, int64_t rb, int64_t rows, int64_t 
   gq::GemmArgs a{W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
   if (q4k_matrix_cores(fmt, cols)) {
     const int64_t off = 0;
-    return finish(gq::launch_gemm_q4k(a, &M, &off, 1, 0, cus, s, epi));
+    return finish(gq::launch_gemm_q4k(fmt, a, &M, &off, 1, 0, cus, s, epi));
   }
   // the few-row fp32 kernel stores only: the other modes take the fp32 matrix cores
   if (fmt == GQ_FMT_Q4_K || M >= f32_matrix_core_min_m(fmt) || epi != gq::kMmStore)
@@ -422,7 +424,7 @@ extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64
         m0 += m_per_expert[e0 + g];
       }
       a.W = (const uint8_t*)W + e0 * ebytes;
-      st = finish(gq::launch_gemm_q4k(a, m_per_expert + e0, off, ne, ebytes, cus, (hipStream_t)stream));
+      st = finish(gq::launch_gemm_q4k(fmt, a, m_per_expert + e0, off, ne, ebytes, cus, (hipStream_t)stream));
       if (st != GQ_OK) return st;
     }
     return GQ_OK;

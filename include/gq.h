@@ -225,18 +225,18 @@ int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out, v
  * M * rows * cols <= 2^28 the call is gq_matvec_batch, so every row of Y
  * equals gq_matvec of its activation row bit for bit. Otherwise, in one
  * launch:
- *   - Q4_K with cols % 4 == 0 runs on the fp16 matrix cores with exact
- *     operands (sc * code is exact in fp16; each activation row's 256 values
- *     of a super-block are scaled by a power of two and split into fp16 hi
- *     and lo parts). It needs 64 * 4 * cols < 2^31 and
- *     256 * gq_row_bytes(GQ_FMT_Q4_K, cols) < 2^31 (cols < 2^23), else
- *     GQ_ERR_SHAPE before any launch. Accuracy: the gq_matvec bound, except
+ *   - Q4_K and Q5_K with cols % 4 == 0 run on the fp16 matrix cores with
+ *     exact operands (sc * code, at most 63 * 31, is exact in fp16; each
+ *     activation row's 256 values of a super-block are scaled by a power of
+ *     two and split into fp16 hi and lo parts). They need 64 * 4 * cols <
+ *     2^31 and 256 * gq_row_bytes(fmt, cols) < 2^31 (Q4_K: cols < 2^23),
+ *     else GQ_ERR_SHAPE before any launch. Accuracy: the gq_matvec bound, except
  *     that activations below about 2^-14 of the largest magnitude max_b in
  *     their row's super-block b (256 columns) are carried only to an
  *     absolute 2^-34 max_b: an extra error of at most
  *     2^-33 * max_b * sum_{c in b} (|d sc_j q_c| + |dmin m_j|) per
  *     super-block, none when every activation is 0 or within that range.
- *   - Q4_K with other cols, Q5_K, Q6_K and split Q8_0 with M >= 2, and Q8_0
+ *   - Q4_K and Q5_K with other cols, Q6_K and split Q8_0 with M >= 2, and Q8_0
  *     and Q5_0 with M >= 8, run on the fp32 matrix cores: each k-chunk of W
  *     is dequantised exactly to fp32 and multiplied with the fp32
  *     activations; same accuracy bound as gq_matvec.
@@ -281,7 +281,7 @@ int gq_matmul_swiglu(int fmt, const void* W, int64_t rows, int64_t cols,
  * order, overwritten:
  *   Y[(o_e + i)*rows + r] = sum_c w_e(r, c) * X[(o_e + i)*cols + c],
  *   o_e = m_0 + ... + m_{e-1}, i < m_e.
- * Q4_K with cols % 4 == 0: one launch per 64 experts on the fp16 matrix
+ * Q4_K and Q5_K with cols % 4 == 0: one launch per 64 experts on the fp16 matrix
  * cores (every group, whatever its row count, as in gq_matmul's matrix-core
  * case, with the same accuracy bound and shape limits); each block is
  * deterministic but may differ in the last bits from gq_matmul of the same

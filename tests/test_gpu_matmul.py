@@ -97,6 +97,7 @@ def test_few_rows_round_like_matvec(gq, fmt, rows, cols, M):
     (12, 14336, 4096, 5),     # Q4_K past the batched-matvec bound: fp16 matrix cores
     (8, 151936, 896, 2),      # Q8_0 lm_head, two rows: the fp32 few-row kernel
     (14, 4096, 14336, 5),     # Q6_K: fp32 matrix cores
+    (13, 14336, 4096, 3),     # Q5_K past the batched-matvec bound: fp16 matrix cores
 ])
 def test_few_rows_large_products(gq, oracle, fmt, rows, cols, M):
     """A few activation rows over products larger than 2^28 weight-rows run
@@ -112,6 +113,7 @@ def test_few_rows_large_products(gq, oracle, fmt, rows, cols, M):
     assert_within_tolerance(Y[:, idx], ref, S, f"large few-row fmt={fmt} M={M}")
 
 
+@pytest.mark.parametrize("fmt", [12, 13])
 @pytest.mark.parametrize("rows,M", [
     (14336, 512),   # 256 x 64 tiles
     (14336, 160),   # 256 x 32 tiles
@@ -119,27 +121,28 @@ def test_few_rows_large_products(gq, oracle, fmt, rows, cols, M):
     (14336, 16),    # 64 x 16 tiles, k split in four
     (300, 20),      # one wave per tile
 ])
-def test_q4k_ragged_row_on_each_tile(gq, oracle, rows, M):
-    """Q4_K rows of 4000 columns (the last super-block a partial one) on each
-    fp16 matrix-core tile: the product equals, bit for bit, the one over 4096
-    columns whose last 96 activations are zero (the storage and the scaling
-    of every super-block are the same), and the oracle on a sample of rows."""
+def test_fp16_route_ragged_row_on_each_tile(gq, oracle, fmt, rows, M):
+    """Q4_K and Q5_K rows of 4000 columns (the last super-block a partial
+    one) on each fp16 matrix-core tile: the product equals, bit for bit, the
+    one over 4096 columns whose last 96 activations are zero (the storage and
+    the scaling of every super-block are the same), and the oracle on a
+    sample of rows."""
     cols, full = 4000, 4096
-    rng = synth.rng_for(613, rows + M)
-    W = synth.weights(12, rows, full, rng)
+    rng = synth.rng_for(613, fmt * 100000 + rows + M)
+    W = synth.weights(fmt, rows, full, rng)
     X = synth.activations((M, cols), rng)
     Xp = np.zeros((M, full), np.float32)
     Xp[:, :cols] = X
-    print(f"[matmul] q4k ragged rows={rows} cols={cols} M={M}", flush=True)
+    print(f"[matmul] fp16-route ragged fmt={fmt} rows={rows} cols={cols} M={M}", flush=True)
     Wd = to_dev(W)
-    Y = _run(gq, 12, Wd, rows, cols, X)
-    Yp = _run(gq, 12, Wd, rows, full, Xp)
+    Y = _run(gq, fmt, Wd, rows, cols, X)
+    Yp = _run(gq, fmt, Wd, rows, full, Xp)
     assert np.array_equal(Y.view(np.uint32), Yp.view(np.uint32))
     idx = np.unique(np.concatenate([np.arange(0, rows, 97), [1, 15, 16, 255, 256, rows - 1]]))
     idx = idx[idx < rows]
-    Ws = oracle.select_rows(12, W, cols, idx)
-    ref, S = oracle.matmul(12, Ws, idx.size, cols, X, nthreads=oracle_threads())
-    assert_within_tolerance(Y[:, idx], ref, S, f"q4k ragged M={M}")
+    Ws = oracle.select_rows(fmt, W, cols, idx)
+    ref, S = oracle.matmul(fmt, Ws, idx.size, cols, X, nthreads=oracle_threads())
+    assert_within_tolerance(Y[:, idx], ref, S, f"fp16-route ragged fmt={fmt} M={M}")
 
 
 @pytest.mark.parametrize("fmt,rows", [(12, 16), (12, 300), (14, 16)])
@@ -160,70 +163,75 @@ def test_many_activation_rows(gq, oracle, fmt, rows):
     assert_within_tolerance(Y[idx], ref, S, f"many activation rows fmt={fmt}")
 
 
+@pytest.mark.parametrize("fmt", [12, 13])
 @pytest.mark.parametrize("rows,cols,M", [
     (2464, 232, 100),   # 64 x 16 tiles, k split in four: one super-block
     (2926, 292, 100),   # two super-blocks
     (2373, 664, 100),   # three super-blocks
     (14336, 256, 64),   # 128 x 32 tiles, k split in two: one super-block
 ])
-def test_q4k_fewer_super_blocks_than_k_groups(gq, oracle, rows, cols, M):
-    """Q4_K products on the tiles that split the super-blocks over wave
-    groups, with fewer super-blocks than groups: the idle groups must not
-    disturb the result (every output against the oracle)."""
-    rng = synth.rng_for(615, rows + cols)
-    W = synth.weights(12, rows, cols, rng)
+def test_fp16_route_fewer_super_blocks_than_k_groups(gq, oracle, fmt, rows, cols, M):
+    """Q4_K and Q5_K products on the tiles that split the super-blocks over
+    wave groups, with fewer super-blocks than groups: the idle groups must
+    not disturb the result (every output against the oracle)."""
+    rng = synth.rng_for(615, fmt * 100000 + rows + cols)
+    W = synth.weights(fmt, rows, cols, rng)
     X = synth.activations((M, cols), rng)
-    _check(gq, oracle, 12, W, rows, cols, X, "fewer super-blocks than k groups")
+    _check(gq, oracle, fmt, W, rows, cols, X, "fewer super-blocks than k groups")
 
 
-def test_q4k_wide_dynamic_range(gq, oracle):
-    """Q4_K on the fp16 matrix cores: activations whose magnitudes span 2^-113
-    .. 2^100 across rows and super-blocks, each within 2^13 of the largest in
-    its row's super-block, meet the plain bound (every super-block is scaled
-    by its own power of two before the fp16 split)."""
+@pytest.mark.parametrize("fmt", [12, 13])
+def test_fp16_route_wide_dynamic_range(gq, oracle, fmt):
+    """Q4_K and Q5_K on the fp16 matrix cores: activations whose magnitudes
+    span 2^-113 .. 2^100 across rows and super-blocks, each within 2^13 of
+    the largest in its row's super-block, meet the plain bound (every
+    super-block is scaled by its own power of two before the fp16 split)."""
     rows, cols, M = 80, 1024, 40
-    rng = synth.rng_for(611, 0)
-    W = synth.weights(12, rows, cols, rng)
+    rng = synth.rng_for(611, fmt)
+    W = synth.weights(fmt, rows, cols, rng)
     nsb = cols // 256
     scale = np.exp2(rng.integers(-100, 101, size=(M, nsb))).astype(np.float64)
     mag = np.exp2(rng.uniform(-13.0, 0.0, size=(M, cols)))
     sign = np.where(rng.random((M, cols)) < 0.5, -1.0, 1.0)
     X = (sign * mag * np.repeat(scale, 256, axis=1)).astype(np.float32)
     X[rng.random((M, cols)) < 0.05] = 0.0
-    _check(gq, oracle, 12, W, rows, cols, X, "wide dynamic range")
+    _check(gq, oracle, fmt, W, rows, cols, X, "wide dynamic range")
 
 
-def test_q4k_outlier_on_zero_weight(gq, oracle):
+@pytest.mark.parametrize("fmt", [12, 13])
+def test_fp16_route_outlier_on_zero_weight(gq, oracle, fmt):
     """The documented limit of the fp16 split: in super-block 0 every weight
     of sub-block 0 is zero (sc_0 = m_0 = 0 in every row) and one activation
     row holds 2^40 there, so that row's other activations of the super-block
     fall below 2^-14 of its largest and are carried only to an absolute
     2^-34 * 2^40. That row stays within the stated extra term; every other row,
-    and that row's other super-blocks, meet the plain bound."""
+    and that row's other super-blocks, meet the plain bound. Q4_K and Q5_K
+    share the header and scale bytes, so the same bytes are cleared."""
     rows, cols, M, hot = 64, 512, 20, 7
-    rng = synth.rng_for(612, 0)
-    W = synth.weights(12, rows, cols, rng).copy()
-    rb = 288
-    blk0 = W.reshape(rows, rb)[:, :144]     # super-block 0 of every row
+    rng = synth.rng_for(612, fmt)
+    W = synth.weights(fmt, rows, cols, rng).copy()
+    sbb = {12: 144, 13: 176}[fmt]           # bytes of one super-block
+    qmax = {12: 15, 13: 31}[fmt]            # largest code
+    blk0 = W.reshape(rows, 2 * sbb)[:, :sbb]  # super-block 0 of every row
     blk0[:, 4] &= 0xC0                      # sc_0 = 0 (top bits belong to sc_4)
     blk0[:, 8] &= 0xC0                      # m_0 = 0 (top bits belong to m_4)
     X = synth.activations((M, cols), rng)
     X[hot, 0] = np.float32(2.0 ** 40)
     print(f"[matmul] outlier rows={rows} cols={cols} M={M}", flush=True)
-    Y = _run(gq, 12, W, rows, cols, X)
-    ref, S = oracle.matmul(12, W, rows, cols, X, nthreads=oracle_threads())
+    Y = _run(gq, fmt, W, rows, cols, X)
+    ref, S = oracle.matmul(fmt, W, rows, cols, X, nthreads=oracle_threads())
     others = np.arange(M) != hot
     assert_within_tolerance(Y[others], ref[others], S[others], "rows without the outlier")
     # the stated extra term for the hot row: 2^-33 max_b sum_c (|d sc q| + |dmin m|),
-    # bounded with sc <= 63, q <= 15, m <= 63 from each row's d and dmin
+    # bounded with sc <= 63, q <= qmax, m <= 63 from each row's d and dmin
     hdr = blk0[:, :4].copy().view(np.float16).astype(np.float64).reshape(rows, 2)
-    per_col = np.abs(hdr[:, 0]) * 63 * 15 + np.abs(hdr[:, 1]) * 63
+    per_col = np.abs(hdr[:, 0]) * 63 * qmax + np.abs(hdr[:, 1]) * 63
     extra = 2.0 ** -33 * 2.0 ** 40 * 256 * per_col
     err = np.abs(Y[hot].astype(np.float64) - ref[hot])
     assert (err <= 2e-4 * S[hot] + extra).all()
     # the same row without the outlier's super-block: super-block 1 alone
     X1 = X.copy()
     X1[:, :256] = 0.0
-    Y1 = _run(gq, 12, W, rows, cols, X1)
-    ref1, S1 = oracle.matmul(12, W, rows, cols, X1, nthreads=oracle_threads())
+    Y1 = _run(gq, fmt, W, rows, cols, X1)
+    ref1, S1 = oracle.matmul(fmt, W, rows, cols, X1, nthreads=oracle_threads())
     assert_within_tolerance(Y1, ref1, S1, "outlier's other super-block")
