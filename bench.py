@@ -734,6 +734,30 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
         del Wd
     log(f"mixed-format prefill: { {k: v for k, v in out.items() if k.startswith('matmul_llama3')} }")
 
+    # Q8_0 prefill products at the Llama-3-8B gate and down shapes (fp16
+    # matrix cores), packed and in the split per-row layout; weights seed 6,
+    # matrix_id 0 (gate) / 1 (down)
+    for k, (which, r, c) in enumerate((("gate", 14336, 4096), ("down", 4096, 14336))):
+        Wd = torch.from_numpy(synth.weights(gq.FMT_Q8_0, r, c, synth.rng_for(6, k))).cuda()
+        Sd = gq.gq_q8_0_split_repack(Wd, r, c)
+        for f, Wf, tag in ((gq.FMT_Q8_0, Wd, "q8_0"), (gq.FMT_Q8_0_SPLIT, Sd, "q8_0_split")):
+            for M in synth.PREFILL_M:
+                Xd = torch.from_numpy(synth.activations((M, c), synth.rng_for(911, M))).cuda()
+                Yd = torch.empty((M, r), dtype=torch.float32, device="cuda")
+
+                def mq(f=f, Wf=Wf, r=r, c=c, M=M, Xd=Xd, Yd=Yd):
+                    st = lib.gq_matmul(f, Wf.data_ptr(), r, c, Xd.data_ptr(), M, Yd.data_ptr(),
+                                       stream_ptr())
+                    assert st == 0
+
+                _, ms, ms_min = timer.stats(mq, 10 if M < 512 else 5, reps=3, warmup=1)
+                tf = 2.0 * M * r * c / (ms * 1e-3) / 1e12
+                out[f"matmul_{tag}_{which}_M{M}"] = dict(
+                    us_per_call=round(ms * 1e3, 1), us_min=round(ms_min * 1e3, 1), TFLOPs=round(tf, 2),
+                    pct_mfma_f16_peak=round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2))
+        del Wd, Sd
+    log(f"q8_0 prefill: { {k: v for k, v in out.items() if k.startswith('matmul_q8_0')} }")
+
     # Q4_K products with a few (M = 2, 4, 8) and many activation rows at the
     # Llama-3-8B prefill shapes (matrix cores)
     for which in ("gate", "down"):

@@ -1,6 +1,8 @@
-// gemm_q4k.hip -- Y = X W^T for Q4_K weights and two or more activation rows,
-// on the gfx950 matrix cores (v_mfma_f32_16x16x32_f16). One launch; the
-// kernel uses no memory beyond its arguments.
+// gemm_q4k.hip -- Y = X W^T for Q4_K (and Q5_K, Q8_0) weights and two or
+// more activation rows, on the gfx950 matrix cores
+// (v_mfma_f32_16x16x32_f16). One launch; the kernel uses no memory beyond
+// its arguments. The Q5_K and Q8_0 forms are described with their layout
+// traits below; this header describes Q4_K.
 //
 // The prompt-chunk product ("nurllama 0.18.1 API", model.nu section: the
 // matmuls run over a chunk of positions at once, each weight read once per
@@ -9,7 +11,7 @@
 // Exact operands. A Q4_K super-block contributes, per output,
 //   d * sum_j sc_j * sum_{c in j} code_c * x_c  -  dmin * sum_j m_j * X_j
 // with X_j the sum of x over sub-block j:
-//   * the weight operand is sc_j * code_c, an integer <= 945, exact in fp16;
+//   * the weight operand is sc_j * code_c, an integer <= 63 * 15, exact in fp16;
 //   * the 256 x of one activation row and super-block are scaled by 2^e so
 //     that the largest magnitude lies in [2^9, 2^10), and split into fp16
 //     parts hi = fp16(x 2^e) and lo = fp16(x 2^e - hi) (v_fma_mix: one
@@ -48,6 +50,7 @@ namespace {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 
 __device__ __forceinline__ h8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -86,13 +89,47 @@ __device__ __forceinline__ h8 weight_operand(uint32_t w0, uint32_t w1, h2 sc, h2
 // that forms sc * code from the biased code (up to 63 * 1055) rounds only
 // its result, so the operand stays exact.
 struct MmQ4K {
-  static constexpr int kBytes = 144, kCodes = 16;
+  static constexpr int kKind = 0, kBytes = 144, kCodes = 16;
   static constexpr bool kQh = false;
 };
 struct MmQ5K {
-  static constexpr int kBytes = 176, kCodes = 48;
+  static constexpr int kKind = 0, kBytes = 176, kCodes = 48;
   static constexpr bool kQh = true;
 };
+// Q8_0: one fp16 d and 32 int8 codes per block, eight blocks per 256-column
+// step (kBytes: the step's bytes in a row). Each 32-wide k-slice of an
+// operand is one block, so the weight operand is the codes themselves (exact
+// in fp16) and d scales the slice's product in fp32. Packed (kKind 1): the
+// 34-byte blocks as stored; the rows must be a multiple of 4 bytes long and W
+// 4-byte aligned, so that every dword load below is aligned (an even block's
+// codes start 2 bytes into a dword and are shifted out with v_alignbyte).
+// Split (kKind 2): the per-row layout with the scales ahead of the codes.
+struct MmQ8P {
+  static constexpr int kKind = 1, kBytes = 272;
+  static constexpr bool kQh = false;
+};
+struct MmQ8S {
+  static constexpr int kKind = 2, kBytes = 256;
+  static constexpr bool kQh = false;
+};
+
+// Eight int8 codes (the bytes of w0, then w1) as fp16 values: a byte with its
+// sign bit flipped is 128 + code, v_perm_b32 places it under the exponent of
+// 1024, and (1152 + code) - 1152 = code is exact.
+__device__ __forceinline__ h8 q8_operand(uint32_t w0, uint32_t w1) {
+  constexpr uint32_t kMagic = 0x64646464u;
+  const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+  uint32_t p[4];
+  p[0] = __builtin_amdgcn_perm(kMagic, u0, 0x04010400u);  // codes 0, 1
+  p[1] = __builtin_amdgcn_perm(kMagic, u0, 0x04030402u);  // codes 2, 3
+  p[2] = __builtin_amdgcn_perm(kMagic, u1, 0x04010400u);  // codes 4, 5
+  p[3] = __builtin_amdgcn_perm(kMagic, u1, 0x04030402u);  // codes 6, 7
+  const h2 k = {(_Float16)-1152.f, (_Float16)-1152.f};
+  uint32_t r[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r[c] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p[c]) + k);
+  return as_h8(r[0], r[1], r[2], r[3]);
+}
 
 // Q5_K: the Q4_K operand of sub-block J with the fifth bits merged in: qh0 /
 // qh1 are the fifth-bit bytes of the same 8 code bytes (w0 / w1), and bit J
@@ -229,18 +266,119 @@ struct MmArgs {
   float* Y;
   int64_t row_bytes;
   int rows, cols, nsb;
+  int nb;        // Q8_0: blocks of 32 per row
+  int code_off;  // split Q8_0: bytes of a row's scale region
   int n_groups;
   MmTile g[kMaxGroups];
 };
 
-// The weight bytes a wave needs for one super-block (its rows' headers and
-// code bytes); the activation tile goes to LDS.
-template <int WR>
-struct Stage {
-  u32x4 hd[WR];
-  u32x2 cw[WR][4];
-  u32x2 qh[WR];  // Q5_K: the fifth-bit bytes of the lane's 8 code bytes
+// The weight bytes lane (i, q) needs for one 256-column step of R row tiles
+// (row i of each): K-quants -- the super-block header and the lane's 8 code
+// bytes of each 32-byte group (and Q5_K's fifth-bit bytes of the same
+// positions).
+template <class Fm, int R, int K = Fm::kKind>
+struct WStage {
+  u32x4 hd[R];
+  u32x2 cw[R][4];
+  u32x2 qh[R];
 };
+// Packed Q8_0: block 2h's 12 bytes from 2 bytes before the lane's codes,
+// block 2h + 1's 8 code bytes, and the dwords holding the d of blocks 2q and
+// 2q + 1 (low half, high half): lane (i, q) fetches two of its row's eight
+// scales, and q8_scales hands them round the row's four lanes.
+template <class Fm, int R>
+struct WStage<Fm, R, 1> {
+  u32x3 ce[R][4];
+  u32x2 co[R][4];
+  uint32_t dq[R][2];
+};
+// Split Q8_0: the lane's 8 code bytes of each block and the step's 8 scales.
+template <class Fm, int R>
+struct WStage<Fm, R, 2> {
+  u32x2 cs[R][8];
+  u32x4 dd[R];
+};
+
+__device__ __forceinline__ u32x3 buf_b96(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  return __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs, voff, soff, 0));
+}
+
+__device__ __forceinline__ uint32_t buf_b32(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+}
+
+// Requests for the weight bytes of step sb: wv[t] is the byte offset of the
+// lane's row in tile t, code_off where a split row's codes start. The
+// per-lane parts of the offsets are checked by the buffer's range; the
+// scalar part (the step) must be a real position.
+template <class Fm, int R>
+__device__ __forceinline__ void fetch_w(WStage<Fm, R>& st, __amdgpu_buffer_rsrc_t wrs, const int (&wv)[R], int q,
+                                        int sb, int code_off) {
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    if constexpr (Fm::kKind == 0) {
+      st.hd[t] = buf_b128(wrs, wv[t], sb * Fm::kBytes);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) st.cw[t][g] = buf_b64(wrs, wv[t] + Fm::kCodes + 32 * g + 8 * q, sb * Fm::kBytes);
+      if constexpr (Fm::kQh) st.qh[t] = buf_b64(wrs, wv[t] + 16 + 8 * q, sb * Fm::kBytes);
+    } else if constexpr (Fm::kKind == 1) {
+      // block 2h at 68h (codes at 68h + 2 + 8q), block 2h + 1 at 68h + 34
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        st.ce[t][h] = buf_b96(wrs, wv[t] + 68 * h + 8 * q, sb * Fm::kBytes);
+        st.co[t][h] = buf_b64(wrs, wv[t] + 68 * h + 36 + 8 * q, sb * Fm::kBytes);
+      }
+      st.dq[t][0] = buf_b32(wrs, wv[t] + 68 * q, sb * Fm::kBytes);
+      st.dq[t][1] = buf_b32(wrs, wv[t] + 68 * q + 32, sb * Fm::kBytes);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.cs[t][j] = buf_b64(wrs, wv[t] + code_off + 32 * j + 8 * q, sb * Fm::kBytes);
+      st.dd[t] = buf_b128(wrs, wv[t], sb * 16);
+    }
+  }
+}
+
+// Vector-memory requests of one fetch_w per row tile.
+template <class Fm>
+constexpr int fetch_w_ops() {
+  return Fm::kKind == 0 ? (Fm::kQh ? 6 : 5) : Fm::kKind == 1 ? 10 : 9;
+}
+
+// Q8_0: the lane's 8 code bytes of block j of row tile t, and the block's d
+// (zero for a block past the row's last, whose bytes belong to the next row).
+template <class Fm, int R>
+__device__ __forceinline__ u32x2 q8_codes(const WStage<Fm, R>& st, int t, int j) {
+  if constexpr (Fm::kKind == 1) {
+    if (j & 1) return st.co[t][j >> 1];
+    const u32x3 r = st.ce[t][j >> 1];
+    return u32x2{__builtin_amdgcn_alignbyte(r.y, r.x, 2), __builtin_amdgcn_alignbyte(r.z, r.y, 2)};
+  } else {
+    return st.cs[t][j];
+  }
+}
+
+// The eight scales of row tile t as four dwords, d of blocks 2h and 2h + 1
+// in dword h (low, high half). Packed: lane (i, h) holds that pair, so every
+// lane reads it from there (ds_bpermute; i = lane % 16).
+template <class Fm, int R>
+__device__ __forceinline__ u32x4 q8_scales(const WStage<Fm, R>& st, int t, int i) {
+  if constexpr (Fm::kKind == 1) {
+    const int pair = (int)__builtin_amdgcn_perm(st.dq[t][1], st.dq[t][0], 0x07060100u);
+    u32x4 d;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) d[h] = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * h + i) << 2, pair);
+    return d;
+  } else {
+    return st.dd[t];
+  }
+}
+
+// d of block j from q8_scales (zero for a block past the row's last).
+__device__ __forceinline__ float q8_scale(u32x4 d4, int j, bool real) {
+  const uint32_t w = d4[j >> 1];
+  const float d = half_bits_to_float((j & 1) ? w >> 16 : w & 0xFFFFu);
+  return real ? d : 0.f;
+}
 
 // An activation tile (16 rows x the 256 columns of one super-block) in LDS:
 // row r at r * kXRow bytes. The 16-byte pad makes the lane reads of the
@@ -289,7 +427,7 @@ __global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
   // this wave's super-blocks: wave, wave + KW, ... (n of them); requests past
   // the last one re-read it (their results are never used)
   const int n = a.nsb > wave ? (a.nsb - wave + KW - 1) / KW : 0;
-  auto fetch = [&](Stage<WR>& st, int slot, int k) {
+  auto fetch = [&](WStage<Fm, WR>& st, int slot, int k) {
     const int sb = wave + KW * (k < n ? k : n - 1);
     // every offset in the per-lane part (the buffer's range check covers it);
     // a ragged row's tail is clamped to the next row's start (cleared later)
@@ -297,24 +435,17 @@ __global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
     issue_fence();
 #pragma unroll
     for (int r = 0; r < 16; ++r) load_lds16(xrs, &xbuf[wave][slot][r * kXRow], r * a.cols * 4 + col, 0);
-#pragma unroll
-    for (int t = 0; t < WR; ++t) {
-      st.hd[t] = buf_b128(wrs, wv[t], sb * Fm::kBytes);
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        st.cw[t][g] = buf_b64(wrs, wv[t] + Fm::kCodes + 32 * g + 8 * q, sb * Fm::kBytes);
-      if constexpr (Fm::kQh) st.qh[t] = buf_b64(wrs, wv[t] + 16 + 8 * q, sb * Fm::kBytes);
-    }
+    fetch_w<Fm, WR>(st, wrs, wv, q, sb, a.code_off);
     issue_fence();
   };
   // vector-memory operations of one fetch (they retire in order)
-  constexpr int kFetchOps = 16 + 5 * WR;
+  constexpr int kFetchOps = 16 + fetch_w_ops<Fm>() * WR;
 
   f32x4 acc[WR];
 #pragma unroll
   for (int t = 0; t < WR; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Stage<WR>& st, int slot, int k) {
+  auto compute = [&](const WStage<Fm, WR>& st, int slot, int k) {
     const int sb = wave + KW * k;
     // this stage's loads (one fetch was issued after them)
     wait_vmcnt<kFetchOps>();
@@ -356,52 +487,89 @@ __global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) sv[c] = lane_read(sinv, 4 * q + c);
 
-    RowHead h[WR];
-#pragma unroll
-    for (int t = 0; t < WR; ++t) h[t] = decode_head(st.hd[t]);
-    f32x4 p1[WR];
-#pragma unroll
-    for (int t = 0; t < WR; ++t) p1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float ps[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    // the activation operands of sub-block (or block) j
+    auto x_operands = [&](int j, h8& xh, h8& xl) {
       const f32x4 a0 = xr[2 * j], a1 = xr[2 * j + 1];
       uint32_t hi[4], lo[4];
       split2(a0.x, a0.y, s, hi[0], lo[0]);
       split2(a0.z, a0.w, s, hi[1], lo[1]);
       split2(a1.x, a1.y, s, hi[2], lo[2]);
       split2(a1.z, a1.w, s, hi[3], lo[3]);
-      const h8 xh = as_h8(hi[0], hi[1], hi[2], hi[3]);
-      const h8 xl = as_h8(lo[0], lo[1], lo[2], lo[3]);
-      ps[j] = ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w));
+      xh = as_h8(hi[0], hi[1], hi[2], hi[3]);
+      xl = as_h8(lo[0], lo[1], lo[2], lo[3]);
+    };
+    if constexpr (Fm::kKind == 0) {
+      RowHead h[WR];
+#pragma unroll
+      for (int t = 0; t < WR; ++t) h[t] = decode_head(st.hd[t]);
+      f32x4 p1[WR];
+#pragma unroll
+      for (int t = 0; t < WR; ++t) p1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float ps[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h8 xh, xl;
+        x_operands(j, xh, xl);
+        const f32x4 a0 = xr[2 * j], a1 = xr[2 * j + 1];
+        ps[j] = ((a0.x + a0.y) + (a0.z + a0.w)) + ((a1.x + a1.y) + (a1.z + a1.w));
+#pragma unroll
+        for (int t = 0; t < WR; ++t) {
+          const u32x2 c = st.cw[t][j >> 1];
+          const h2 sc = {h[t].sc[j], h[t].sc[j]}, nsc = {h[t].nsc[j], h[t].nsc[j]};
+          const h8 wop = weight_op_j<Fm>(j, c, st.qh[t], sc, nsc);
+          p1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, wop, p1[t], 0, 0, 0);
+          p1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, wop, p1[t], 0, 0, 0);
+        }
+      }
+      uint32_t mh[4], ml[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) split2(ps[2 * c], ps[2 * c + 1], s, mh[c], ml[c]);
+      const h8 mhi = as_h8(mh[0], mh[1], mh[2], mh[3]);
+      const h8 mlo = as_h8(ml[0], ml[1], ml[2], ml[3]);
 #pragma unroll
       for (int t = 0; t < WR; ++t) {
-        const u32x2 c = st.cw[t][j >> 1];
-        const h2 sc = {h[t].sc[j], h[t].sc[j]}, nsc = {h[t].nsc[j], h[t].nsc[j]};
-        const h8 wop = weight_op_j<Fm>(j, c, st.qh[t], sc, nsc);
-        p1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, wop, p1[t], 0, 0, 0);
-        p1[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, wop, p1[t], 0, 0, 0);
+        f32x4 p2 = {0.f, 0.f, 0.f, 0.f};
+        p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(mhi, h[t].mop, p2, 0, 0, 0);
+        p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(mlo, h[t].mop, p2, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float v = __builtin_fmaf(h[t].d, p1[t][c], -(h[t].dmin * p2[c]));
+          acc[t][c] = __builtin_fmaf(v, sv[c], acc[t][c]);
+        }
       }
-    }
-    uint32_t mh[4], ml[4];
+    } else {
+      // Q8_0: block j's product scaled by its d, per block
+      const int real = a.nb - 8 * sb;  // blocks of this step inside the row
+      u32x4 d4[WR];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) split2(ps[2 * c], ps[2 * c + 1], s, mh[c], ml[c]);
-    const h8 mhi = as_h8(mh[0], mh[1], mh[2], mh[3]);
-    const h8 mlo = as_h8(ml[0], ml[1], ml[2], ml[3]);
+      for (int t = 0; t < WR; ++t) d4[t] = q8_scales(st, t, i);
+      f32x4 pd[WR];
 #pragma unroll
-    for (int t = 0; t < WR; ++t) {
-      f32x4 p2 = {0.f, 0.f, 0.f, 0.f};
-      p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(mhi, h[t].mop, p2, 0, 0, 0);
-      p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(mlo, h[t].mop, p2, 0, 0, 0);
+      for (int t = 0; t < WR; ++t) pd[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float v = __builtin_fmaf(h[t].d, p1[t][c], -(h[t].dmin * p2[c]));
-        acc[t][c] = __builtin_fmaf(v, sv[c], acc[t][c]);
+      for (int j = 0; j < 8; ++j) {
+        h8 xh, xl;
+        x_operands(j, xh, xl);
+#pragma unroll
+        for (int t = 0; t < WR; ++t) {
+          const u32x2 c = q8_codes(st, t, j);
+          const h8 wop = q8_operand(c.x, c.y);
+          const float d = q8_scale(d4[t], j, j < real);
+          f32x4 p = {0.f, 0.f, 0.f, 0.f};
+          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, wop, p, 0, 0, 0);
+          p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, wop, p, 0, 0, 0);
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) pd[t][c4] = __builtin_fmaf(d, p[c4], pd[t][c4]);
+        }
       }
+#pragma unroll
+      for (int t = 0; t < WR; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[t][c] = __builtin_fmaf(pd[t][c], sv[c], acc[t][c]);
     }
   };
 
-  Stage<WR> sa, sbuf;
+  WStage<Fm, WR> sa, sbuf;
   if (n > 0) {
     fetch(sa, 0, 0);
     for (int k = 0; k < n; k += 2) {
@@ -457,7 +625,12 @@ constexpr int kFragGroup = 272;
 constexpr int kFragBytes = 4 * kFragGroup;
 constexpr int kMinFrag = 16;  // fragments 0-7: hi parts of sub-blocks 0-7, 8-15: lo parts,
                               // 16, 17: the min-term hi and lo parts
-constexpr int kTileBytes = 18 * kFragBytes;  // one 16-row m-tile of one super-block
+// one 16-row m-tile of one 256-column step: K-quants 18 fragments, Q8_0 16
+// (no min term)
+template <class Fm>
+constexpr int tile_bytes() {
+  return (Fm::kKind == 0 ? 18 : 16) * kFragBytes;
+}
 
 // fp16 parts of a * s: hi = fp16(a s), lo = fp16(a s - hi), in the low halves.
 __device__ __forceinline__ void split1(float a, float s, uint32_t& hi, uint32_t& lo) {
@@ -472,13 +645,6 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 
-template <int R>
-struct WStage {
-  u32x4 hd[R];
-  u32x2 cw[R][4];
-  u32x2 qh[R];  // Q5_K: the fifth-bit bytes of the lane's 8 code bytes
-};
-
 __device__ __forceinline__ f32x4 buf_f32x4(__amdgpu_buffer_rsrc_t rs, int voff) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
 }
@@ -492,6 +658,7 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
   // hi and lo products in separate accumulators when there are too few
   // independent MFMA chains to cover the dependent-issue latency
   constexpr bool kSplitAcc = R * C < 4;
+  constexpr int kTileBytes = tile_bytes<Fm>();
   constexpr int kStage = C * kTileBytes;
   __shared__ __attribute__((aligned(16))) uint8_t xs[KS][2][kStage];
   __shared__ __attribute__((aligned(16))) float xsv[KS][2][16 * C];
@@ -542,7 +709,7 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
   const int rd_off = q * kFragGroup + i * 16;
 
   f32x4 xr[SX][CW][4];
-  WStage<R> ws[SW];
+  WStage<Fm, R> ws[SW];
 
   // the group's k-th super-block (k past the last re-reads the last; a group
   // with no super-block -- fewer super-blocks than groups -- re-reads
@@ -561,14 +728,7 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
     for (int c = 0; c < CW; ++c)
 #pragma unroll
       for (int v = 0; v < 4; ++v) xr[xslot][c][v] = buf_f32x4(xrs, xv[c] + col[v]);
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-      ws[wslot].hd[t] = buf_b128(wrs, wv[t], sb * Fm::kBytes);
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        ws[wslot].cw[t][g] = buf_b64(wrs, wv[t] + Fm::kCodes + 32 * g + 8 * q, sb * Fm::kBytes);
-      if constexpr (Fm::kQh) ws[wslot].qh[t] = buf_b64(wrs, wv[t] + 16 + 8 * q, sb * Fm::kBytes);
-    }
+    fetch_w<Fm, R>(ws[wslot], wrs, wv, q, sb, a.code_off);
     issue_fence();
   };
 
@@ -610,14 +770,16 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
         split2(x.z, x.w, s, h1, l1);
         *(u32x2*)(tile + 2 * v * kFragBytes + cv_off) = u32x2{h0, h1};
         *(u32x2*)(tile + (8 + 2 * v) * kFragBytes + cv_off) = u32x2{l0, l1};
-        // this lane pair's 8 columns summed, for the min term
-        const float s4 = (x.x + x.y) + (x.z + x.w);
-        const float s8 = s4 + __builtin_bit_cast(float, dpp_u32<0xB1>(__builtin_bit_cast(uint32_t, s4)));
-        if ((cl & 1) == 0) {
-          uint32_t mh, ml;
-          split1(s8, s, mh, ml);
-          *(uint16_t*)(tile + cm_off + 4 * v) = (uint16_t)mh;
-          *(uint16_t*)(tile + cm_off + 4 * v + kFragBytes) = (uint16_t)ml;
+        if constexpr (Fm::kKind == 0) {
+          // this lane pair's 8 columns summed, for the min term
+          const float s4 = (x.x + x.y) + (x.z + x.w);
+          const float s8 = s4 + __builtin_bit_cast(float, dpp_u32<0xB1>(__builtin_bit_cast(uint32_t, s4)));
+          if ((cl & 1) == 0) {
+            uint32_t mh, ml;
+            split1(s8, s, mh, ml);
+            *(uint16_t*)(tile + cm_off + 4 * v) = (uint16_t)mh;
+            *(uint16_t*)(tile + cm_off + 4 * v + kFragBytes) = (uint16_t)ml;
+          }
         }
       }
       if (cl == 0) xsv[wk][buf][16 * ct + ci] = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);
@@ -630,54 +792,103 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
 #pragma unroll
     for (int c = 0; c < C; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int wslot, int buf) {
-    const uint8_t* base = &xs[wk][buf][0];
-    RowHead h[R];
+  // Q8_0: one block per k-slice, each slice's product scaled by its d
+  auto compute_q8 = [&](int wslot, int buf, int sb) {
+    if constexpr (Fm::kKind != 0) {
+      const uint8_t* base = &xs[wk][buf][0];
+      const int real = a.nb - 8 * sb;  // blocks of this step inside the row
+      u32x4 d4[R];
 #pragma unroll
-    for (int t = 0; t < R; ++t) h[t] = decode_head(ws[wslot].hd[t]);
-    f32x4 ph[R][C], pl[R][C];
+      for (int t = 0; t < R; ++t) d4[t] = q8_scales(ws[wslot], t, i);
+      f32x4 pd[R][C];
 #pragma unroll
-    for (int t = 0; t < R; ++t)
+      for (int t = 0; t < R; ++t)
 #pragma unroll
-      for (int c = 0; c < C; ++c) ph[t][c] = pl[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < C; ++c) pd[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      h8 xh[C], xl[C];
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        xh[c] = *(const h8*)(base + c * kTileBytes + j * kFragBytes + rd_off);
-        xl[c] = *(const h8*)(base + c * kTileBytes + (8 + j) * kFragBytes + rd_off);
-      }
-#pragma unroll
-      for (int t = 0; t < R; ++t) {
-        const u32x2 cw = ws[wslot].cw[t][j >> 1];
-        const h2 sc = {h[t].sc[j], h[t].sc[j]}, nsc = {h[t].nsc[j], h[t].nsc[j]};
-        const h8 wop = weight_op_j<Fm>(j, cw, ws[wslot].qh[t], sc, nsc);
+      for (int j = 0; j < 8; ++j) {
+        h8 xh[C], xl[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-          ph[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[c], wop, ph[t][c], 0, 0, 0);
-          if constexpr (kSplitAcc)
-            pl[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[c], wop, pl[t][c], 0, 0, 0);
-          else
-            ph[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[c], wop, ph[t][c], 0, 0, 0);
+          xh[c] = *(const h8*)(base + c * kTileBytes + j * kFragBytes + rd_off);
+          xl[c] = *(const h8*)(base + c * kTileBytes + (8 + j) * kFragBytes + rd_off);
+        }
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+          const u32x2 cw = q8_codes(ws[wslot], t, j);
+          const h8 wop = q8_operand(cw.x, cw.y);
+          const float d = q8_scale(d4[t], j, j < real);
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[c], wop, p, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[c], wop, p, 0, 0, 0);
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) pd[t][c][cc] = __builtin_fmaf(d, p[cc], pd[t][c][cc]);
+          }
         }
       }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const f32x4 sv = *(const f32x4*)&xsv[wk][buf][16 * c + 4 * q];
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) acc[t][c][cc] = __builtin_fmaf(pd[t][c][cc], sv[cc], acc[t][c][cc]);
+      }
     }
+  };
+
+  auto compute = [&](int wslot, int buf) {
+    if constexpr (Fm::kKind == 0) {
+      const uint8_t* base = &xs[wk][buf][0];
+      RowHead h[R];
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const h8 mh = *(const h8*)(base + c * kTileBytes + kMinFrag * kFragBytes + rd_off);
-      const h8 ml = *(const h8*)(base + c * kTileBytes + (kMinFrag + 1) * kFragBytes + rd_off);
-      const f32x4 sv = *(const f32x4*)&xsv[wk][buf][16 * c + 4 * q];
+      for (int t = 0; t < R; ++t) h[t] = decode_head(ws[wslot].hd[t]);
+      f32x4 ph[R][C], pl[R][C];
 #pragma unroll
-      for (int t = 0; t < R; ++t) {
-        f32x4 p2 = {0.f, 0.f, 0.f, 0.f};
-        p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(mh, h[t].mop, p2, 0, 0, 0);
-        p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ml, h[t].mop, p2, 0, 0, 0);
+      for (int t = 0; t < R; ++t)
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const float p1 = kSplitAcc ? ph[t][c][cc] + pl[t][c][cc] : ph[t][c][cc];
-          const float v = __builtin_fmaf(h[t].d, p1, -(h[t].dmin * p2[cc]));
-          acc[t][c][cc] = __builtin_fmaf(v, sv[cc], acc[t][c][cc]);
+        for (int c = 0; c < C; ++c) ph[t][c] = pl[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h8 xh[C], xl[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          xh[c] = *(const h8*)(base + c * kTileBytes + j * kFragBytes + rd_off);
+          xl[c] = *(const h8*)(base + c * kTileBytes + (8 + j) * kFragBytes + rd_off);
+        }
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+          const u32x2 cw = ws[wslot].cw[t][j >> 1];
+          const h2 sc = {h[t].sc[j], h[t].sc[j]}, nsc = {h[t].nsc[j], h[t].nsc[j]};
+          const h8 wop = weight_op_j<Fm>(j, cw, ws[wslot].qh[t], sc, nsc);
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            ph[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[c], wop, ph[t][c], 0, 0, 0);
+            if constexpr (kSplitAcc)
+              pl[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[c], wop, pl[t][c], 0, 0, 0);
+            else
+              ph[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[c], wop, ph[t][c], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const h8 mh = *(const h8*)(base + c * kTileBytes + kMinFrag * kFragBytes + rd_off);
+        const h8 ml = *(const h8*)(base + c * kTileBytes + (kMinFrag + 1) * kFragBytes + rd_off);
+        const f32x4 sv = *(const f32x4*)&xsv[wk][buf][16 * c + 4 * q];
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+          f32x4 p2 = {0.f, 0.f, 0.f, 0.f};
+          p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(mh, h[t].mop, p2, 0, 0, 0);
+          p2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ml, h[t].mop, p2, 0, 0, 0);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const float p1 = kSplitAcc ? ph[t][c][cc] + pl[t][c][cc] : ph[t][c][cc];
+            const float v = __builtin_fmaf(h[t].d, p1, -(h[t].dmin * p2[cc]));
+            acc[t][c][cc] = __builtin_fmaf(v, sv[cc], acc[t][c][cc]);
+          }
         }
       }
     }
@@ -701,7 +912,10 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
       const int k = k0 + u;
       if (k < nsteps) {
         fetch(sb_of(k + D), (u + D) % SX, (u + D) % SW);
-        if (k < nk) compute(u, k & 1);
+        if (k < nk) {
+          if constexpr (Fm::kKind == 0) compute(u, k & 1);
+          else compute_q8(u, k & 1, sb_of(k));
+        }
         if (k + 1 < nk) convert(sb_of(k + 1), (u + 1) % SX, (k + 1) & 1);
         step_barrier();
       }
@@ -813,10 +1027,21 @@ hipError_t launch_gemm_q4k_epi(MmArgs& m, const GemmArgs& a, const int64_t* grou
     if (gy == 0) return hipSuccess;
     return launch(m, gy, s);
   };
-  if (grid(256, 64) >= fill) return run_xs(launch_xs<Fm, 2, 4, 1, 1, 8, EPI>, 64);
-  if (grid(256, 32) >= fill) return run_xs(launch_xs<Fm, 2, 2, 2, 1, 8, EPI>, 32);
-  if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 2, 8, EPI>, 32);
-  if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
+  if constexpr (Fm::kKind == 0) {
+    if (grid(256, 64) >= fill) return run_xs(launch_xs<Fm, 2, 4, 1, 1, 8, EPI>, 64);
+    if (grid(256, 32) >= fill) return run_xs(launch_xs<Fm, 2, 2, 2, 1, 8, EPI>, 32);
+  } else if constexpr (Fm::kKind == 2) {
+    // Q8_0 steps carry twice the weight bytes per lane: 16-row tiles per wave
+    if (grid(128, 64) >= fill) return run_xs(launch_xs<Fm, 1, 4, 1, 1, 8, EPI>, 64);
+  } else {
+    // packed Q8_0 also holds 12 bytes per even block: 8-wave tiles only
+    if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 1, 8, EPI>, 32);
+    if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 2, 4, EPI>, 16);
+  }
+  if constexpr (Fm::kKind != 1) {
+    if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 2, 8, EPI>, 32);
+    if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
+  }
   const int gy = build_groups(m, group_m, group_off, n_groups, group_w_bytes, 16);
   if (gy < 0) return hipErrorInvalidValue;
   if (gy == 0) return hipSuccess;
@@ -850,9 +1075,16 @@ hipError_t launch_gemm_q4k(int fmt, const GemmArgs& a, const int64_t* group_m, c
   m.rows = a.rows;
   m.cols = a.cols;
   m.nsb = (a.cols + 255) / 256;
-  if (fmt == kFmtQ4_K) return launch_gemm_fmt<MmQ4K>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
-  if (fmt == kFmtQ5_K) return launch_gemm_fmt<MmQ5K>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
-  return hipErrorInvalidValue;
+  m.nb = (a.cols + 31) / 32;
+  m.code_off = split_scale_bytes(m.nb);
+  switch (fmt) {
+    case kFmtQ4_K: return launch_gemm_fmt<MmQ4K>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
+    case kFmtQ5_K: return launch_gemm_fmt<MmQ5K>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
+    case kFmtQ8_0: return launch_gemm_fmt<MmQ8P>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
+    case kFmtQ8_0Split:
+      return launch_gemm_fmt<MmQ8S>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace gq

@@ -71,10 +71,11 @@ int check_align(int fmt, const void* W) {
 int finish(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_ERR_DEVICE; }
 
 // Activation rows from which the Q8_0 / Q5_0 / Q5_K / Q6_K products run on
-// the fp32 matrix cores (gemm_f32.hip) instead of the fp32 few-row kernel
-// (measured: K-quants are faster there from M = 2 on; Q8_0 at M = 4 is still
-// faster on the few-row kernel, 21 vs 31 us for 4096 x 4096, and 2.8x slower
-// at M = 16).
+// the matrix cores (gemm_f32.hip; Q8_0 rows the fp16 kernels take go there)
+// instead of the fp32 few-row kernel (measured: K-quants are faster there
+// from M = 2 on; Q8_0 at M = 4 is still faster on the few-row kernel, 21 vs
+// 31 us for 4096 x 4096 on the fp32 matrix cores, 27 vs 37 us for the
+// 14336 x 4096 gate on the fp16 ones, and 2.8x slower at M = 16).
 #ifndef GQ_F32_MIN_M_KQUANT
 #define GQ_F32_MIN_M_KQUANT 2
 #endif
@@ -265,32 +266,47 @@ extern "C" int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, v
 
 namespace {
 
-// Q4_K and Q5_K products run on the fp16 matrix cores when rows are whole
-// groups of four floats, else on the fp32 matrix cores.
-bool q4k_matrix_cores(int fmt, int64_t cols) {
-  return (fmt == GQ_FMT_Q4_K || fmt == GQ_FMT_Q5_K) && cols % 4 == 0;
+// The three output modes of the prefill product.
+enum MatmulMode { kModeStore = 0, kModeAcc = 1, kModeSwiglu = 2 };
+
+// The layouts the fp16 matrix-core kernels take: Q4_K, Q5_K and split Q8_0
+// rows that are whole groups of four floats, and packed Q8_0 ones whose rows
+// are also a whole number of dwords from a dword-aligned W (their loads are
+// dword loads).
+bool f16_layout(int fmt, int64_t cols, int64_t rb, const void* W) {
+  if (cols % 4 != 0) return false;
+  if (fmt == GQ_FMT_Q4_K || fmt == GQ_FMT_Q5_K || fmt == GQ_FMT_Q8_0_SPLIT) return true;
+  return fmt == GQ_FMT_Q8_0 && rb % 4 == 0 && (uintptr_t)W % 4 == 0;
 }
 
 bool batched_matvec(int64_t M, int64_t rows, int64_t cols) {
   return M > 1 && M < 16 && rows * cols <= kBatchMaxWork / M;
 }
 
+// Whether a product of M activation rows past the batched-matvec bound runs
+// on the fp16 matrix cores: every layout above, except that packed Q8_0 with
+// fewer rows than the fp32 kernels' threshold keeps the few-row kernel for
+// the stored form.
+bool f16_route(int fmt, int64_t cols, int64_t rb, const void* W, int64_t M, int epi) {
+  if (!f16_layout(fmt, cols, rb, W)) return false;
+  return fmt != GQ_FMT_Q8_0 || M >= f32_matrix_core_min_m(fmt) || epi != gq::kMmStore;
+}
+
 // Whether the kernel that gq_matmul picks for this shape can address it
 // (its tiles use 31-bit buffer offsets); checked before any HIP call.
-bool matmul_addressable(int fmt, int64_t rows, int64_t cols, int64_t M, int64_t rb) {
-  if (q4k_matrix_cores(fmt, cols) && M > 1 && !batched_matvec(M, rows, cols))
+bool matmul_addressable(int fmt, const void* W, int64_t rows, int64_t cols, int64_t M, int64_t rb,
+                        int mode) {
+  const int epi = mode == kModeStore ? gq::kMmStore : gq::kMmAcc;
+  if (M > 1 && !batched_matvec(M, rows, cols) && f16_route(fmt, cols, rb, W, M, epi))
     return gq::gemm_q4k_fits(rows, cols, rb);
   return true;
 }
-
-// The three output modes of the prefill product.
-enum MatmulMode { kModeStore = 0, kModeAcc = 1, kModeSwiglu = 2 };
 
 // One matrix-core product of the route for (fmt, cols, M) with a GEMM epilogue.
 int matrix_product(int fmt, const uint8_t* W, int64_t rb, int64_t rows, int64_t cols, const float* X,
                    int64_t M, float* Y, hipStream_t s, int cus, int epi) {
   gq::GemmArgs a{W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
-  if (q4k_matrix_cores(fmt, cols)) {
+  if (f16_route(fmt, cols, rb, W, M, epi)) {
     const int64_t off = 0;
     return finish(gq::launch_gemm_q4k(fmt, a, &M, &off, 1, 0, cus, s, epi));
   }
@@ -307,10 +323,10 @@ int matrix_product(int fmt, const uint8_t* W, int64_t rb, int64_t rows, int64_t 
 // cost grows with M * rows * cols: every row repeats the decode; measured
 // faster than the matrix cores up to about 2^28 weight-rows for every
 // format): one batched launch for the stored form, one launch per row for
-// the others. Larger Q4_K products run on the fp16 matrix cores (exact
-// operands), the other formats on the fp32 matrix cores from a per-format M,
-// else on the fp32 few-row kernel. The SwiGLU form on the matrix cores is
-// two launches: Y = W_up X, then Y = silu(W_gate X) * Y.
+// the others. Larger products of the layouts in f16_route run on the fp16
+// matrix cores (exact operands), the others on the fp32 matrix cores from a
+// per-format M, else on the fp32 few-row kernel. The SwiGLU form on the
+// matrix cores is two launches: Y = W_up X, then Y = silu(W_gate X) * Y.
 int matmul_route(int fmt, const void* W, int64_t rb, int64_t rows, int64_t cols, const float* X,
                  int64_t M, float* Y, void* stream, int cus, int mode = kModeStore) {
   const hipStream_t s = (hipStream_t)stream;
@@ -354,7 +370,7 @@ int matmul_entry(int fmt, const void* W, int64_t rows, int64_t cols, const float
   if ((uintptr_t)X % 4 || (uintptr_t)Y % 4) return GQ_ERR_ALIGN;
   if (overlaps(Y, M * rows * 4, W, wbytes) || overlaps(Y, M * rows * 4, X, M * cols * 4))
     return GQ_ERR_OVERLAP;
-  if (!matmul_addressable(fmt, rows, cols, M, rb)) return GQ_ERR_SHAPE;
+  if (!matmul_addressable(fmt, W, rows, cols, M, rb, mode)) return GQ_ERR_SHAPE;
 
   const int cus = current_cus();
   if (cus <= 0) return GQ_ERR_DEVICE;
@@ -405,12 +421,12 @@ extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64
   if ((st = check_align(fmt, W)) != GQ_OK) return st;
   if ((uintptr_t)X % 4 || (uintptr_t)Y % 4) return GQ_ERR_ALIGN;
   if (overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, X, xbytes)) return GQ_ERR_OVERLAP;
-  if (q4k_matrix_cores(fmt, cols) && !gq::gemm_q4k_fits(rows, cols, rb)) return GQ_ERR_SHAPE;
+  if (f16_layout(fmt, cols, rb, W) && !gq::gemm_q4k_fits(rows, cols, rb)) return GQ_ERR_SHAPE;
 
   const int cus = current_cus();
   if (cus <= 0) return GQ_ERR_DEVICE;
   (void)hipGetLastError();
-  if (q4k_matrix_cores(fmt, cols)) {
+  if (f16_layout(fmt, cols, rb, W)) {
     // one grouped launch per 64 experts: group e multiplies expert e by its
     // m_per_expert[e] rows of X (starting after the earlier experts' rows)
     gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0, 0};

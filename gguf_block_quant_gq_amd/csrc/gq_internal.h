@@ -86,8 +86,9 @@ hipError_t launch_gemv(int fmt, GemvArgs a, int cus, hipStream_t s, int epi = kE
 bool gemv_q4k_supports(const GemvArgs& a, int cus, const ExpertArgs* ex);
 hipError_t launch_gemv_q4k(GemvArgs a, int cus, hipStream_t s, int epi, const ExpertArgs* ex);
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
-// The Q4_K / Q5_K product on the fp16 matrix cores (gemm_q4k.hip; fmt is
-// kFmtQ4_K or kFmtQ5_K), one launch for n_groups products that share a
+// The product on the fp16 matrix cores (gemm_q4k.hip; fmt is kFmtQ4_K,
+// kFmtQ5_K, kFmtQ8_0 -- rows a multiple of 4 bytes long, W 4-byte aligned --
+// or kFmtQ8_0Split), one launch for n_groups products that share a
 // shape: group g multiplies the weight tensor at W + g * group_w_bytes by the
 // group_m[g] activation rows starting at row group_off[g] of X, into the
 // same rows of Y (a single product: one group). It takes cols % 4 == 0

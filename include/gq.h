@@ -225,23 +225,28 @@ int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out, v
  * M * rows * cols <= 2^28 the call is gq_matvec_batch, so every row of Y
  * equals gq_matvec of its activation row bit for bit. Otherwise, in one
  * launch:
- *   - Q4_K and Q5_K with cols % 4 == 0 run on the fp16 matrix cores with
- *     exact operands (sc * code, at most 63 * 31, is exact in fp16; each
- *     activation row's 256 values of a super-block are scaled by a power of
- *     two and split into fp16 hi and lo parts). They need 64 * 4 * cols <
- *     2^31 and 256 * gq_row_bytes(fmt, cols) < 2^31 (Q4_K: cols < 2^23),
- *     else GQ_ERR_SHAPE before any launch. Accuracy: the gq_matvec bound, except
+ *   - On the fp16 matrix cores, with exact operands: Q4_K, Q5_K and split
+ *     Q8_0 with cols % 4 == 0, and Q8_0 with cols % 4 == 0, a row length
+ *     gq_row_bytes(GQ_FMT_Q8_0, cols) that is a multiple of 4 (an even
+ *     number of blocks) and W 4-byte aligned, from M = 8. The weight operand
+ *     is sc * code (at most 63 * 31) or the int8 code, exact in fp16, with
+ *     d (and dmin) applied in fp32 per super-block or block; each activation
+ *     row's 256 values of a 256-column step are scaled by a power of two and
+ *     split into fp16 hi and lo parts. They need 64 * 4 * cols < 2^31 and
+ *     256 * gq_row_bytes(fmt, cols) < 2^31 (Q4_K: cols < 2^23), else
+ *     GQ_ERR_SHAPE before any launch. Accuracy: the gq_matvec bound, except
  *     that activations below about 2^-14 of the largest magnitude max_b in
- *     their row's super-block b (256 columns) are carried only to an
- *     absolute 2^-34 max_b: an extra error of at most
- *     2^-33 * max_b * sum_{c in b} (|d sc_j q_c| + |dmin m_j|) per
- *     super-block, none when every activation is 0 or within that range.
- *   - Q4_K and Q5_K with other cols, Q6_K and split Q8_0 with M >= 2, and Q8_0
- *     and Q5_0 with M >= 8, run on the fp32 matrix cores: each k-chunk of W
- *     is dequantised exactly to fp32 and multiplied with the fp32
- *     activations; same accuracy bound as gq_matvec.
+ *     their row's step b (256 columns) are carried only to an absolute
+ *     2^-34 max_b: an extra error of at most 2^-33 * max_b * sum_{c in b}
+ *     |w(r, c)|-terms per step (Q4_K / Q5_K: |d sc_j q_c| + |dmin m_j|;
+ *     Q8_0: |d q_c|), none when every activation is 0 or within that range.
+ *   - The other products with M >= 2 of Q4_K, Q5_K, Q6_K and split Q8_0,
+ *     and with M >= 8 of Q8_0 and Q5_0, run on the fp32 matrix cores: each
+ *     k-chunk of W is dequantised exactly to fp32 and multiplied with the
+ *     fp32 activations; same accuracy bound as gq_matvec.
  *   - Q8_0 and Q5_0 with 2 <= M < 8 stream W once per 15 activation rows on
- *     the fp32 vector units; same accuracy bound as gq_matvec.
+ *     the fp32 vector units; same accuracy bound as gq_matvec. (The
+ *     accumulate and SwiGLU forms run these on the matrix cores above.)
  * Repeated calls give bit-identical results. Asynchronous on `stream`.
  */
 int gq_matmul(int fmt, const void* W, int64_t rows, int64_t cols,
@@ -281,13 +286,14 @@ int gq_matmul_swiglu(int fmt, const void* W, int64_t rows, int64_t cols,
  * order, overwritten:
  *   Y[(o_e + i)*rows + r] = sum_c w_e(r, c) * X[(o_e + i)*cols + c],
  *   o_e = m_0 + ... + m_{e-1}, i < m_e.
- * Q4_K and Q5_K with cols % 4 == 0: one launch per 64 experts on the fp16 matrix
- * cores (every group, whatever its row count, as in gq_matmul's matrix-core
- * case, with the same accuracy bound and shape limits); each block is
- * deterministic but may differ in the last bits from gq_matmul of the same
- * rows, whose tile is chosen for that call alone. Other formats: each
- * expert's block is exactly gq_matmul of that expert's matrix and rows
- * (same kernels, same bits), enqueued in expert order.
+ * The layouts that gq_matmul runs on the fp16 matrix cores (whatever the
+ * row counts here): one launch per 64 experts on the fp16 matrix cores
+ * (every group, whatever its row count, with the accuracy bound and shape
+ * limits of that case); each block is deterministic but may differ in the
+ * last bits from gq_matmul of the same rows, whose tile is chosen for that
+ * call alone. Other layouts: each expert's block is exactly gq_matmul of
+ * that expert's matrix and rows (same kernels, same bits), enqueued in
+ * expert order.
  * Experts with no rows are skipped. All counts are checked (>= 0, at most
  * 2^30 rows in all, as gq_matmul's M) before the first launch; n_expert == 0, rows == 0 or no
  * rows at all is a no-op. Asynchronous on `stream` (the counts are read

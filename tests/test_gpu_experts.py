@@ -109,18 +109,20 @@ def test_invalid_ids_and_empty(gq, oracle):
 GROUPED = [
     (12, 512, 2048, [0, 1, 3, 17, 40, 70, 5, 120]),
     (14, 256, 768, [33, 0, 2, 64]),          # Q6_K: fp32 matrix cores for the large groups
-    (8, 300, 896, [9, 16, 0, 1]),            # Q8_0: few-row kernel / fp32 matrix cores
+    (8, 300, 900, [9, 16, 0, 1]),            # Q8_0, rows of 29 blocks: few-row kernel / fp32 matrix cores
     (12, 64, 300, [0, 0, 7]),                # ragged rows, one expert with all the rows
     (13, 256, 1024, [20, 0, 2, 64]),         # Q5_K: grouped on the fp16 matrix cores
+    (8, 256, 1024, [20, 0, 3, 64]),          # Q8_0 (rows of 1088 bytes): grouped as well
 ]
 
 
 @pytest.mark.parametrize("fmt,rows,cols,counts", GROUPED)
 def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
     """Each expert's block of gq_matmul_experts is within tolerance of the
-    oracle. Q4_K and Q5_K with cols % 4 == 0 run as one grouped launch: a second call
-    gives the same bits. The other formats run gq_matmul per expert: each
-    block equals gq_matmul of that expert's matrix and rows bit for bit."""
+    oracle. Q4_K and Q5_K with cols % 4 == 0, and Q8_0 whose rows are also a
+    whole number of dwords, run as one grouped launch: a second call gives
+    the same bits. The others run gq_matmul per expert: each block equals
+    gq_matmul of that expert's matrix and rows bit for bit."""
     n_expert, total = len(counts), sum(counts)
     rng = synth.rng_for(962, fmt * 1000 + rows)
     W = synth.weights(fmt, n_expert * rows, cols, rng)
@@ -132,7 +134,7 @@ def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
     assert_pad_untouched(Y, total * rows)
     got = to_host(Y)[:total * rows].reshape(total, rows)
     rb = gq.gq_row_bytes(fmt, cols)
-    grouped = fmt in (12, 13) and cols % 4 == 0
+    grouped = cols % 4 == 0 and (fmt in (12, 13) or (fmt == 8 and rb % 4 == 0))
     o = 0
     for e, m in enumerate(counts):
         if m == 0:

@@ -1,7 +1,8 @@
 """gq_matmul_acc and gq_matmul_swiglu on the GPU, one case per route (the
 matvec at M = 1, per-row matvecs in the few-row range, the Q4_K / Q5_K fp16
-matrix cores with each of their tiles, the fp32 matrix cores for the other formats
-and for Q4_K rows that are not a multiple of 4 wide): the accumulating form
+matrix cores with each of their tiles, Q8_0 on the fp16 matrix cores, the
+fp32 matrix cores for the other formats and for rows those kernels do not
+take): the accumulating form
 equals Y0 + gq_matmul bit for bit and the oracle within tolerance; the SwiGLU
 form meets the derived bound against the f64 oracle and equals the host's
 fp32 SwiGLU of the two halves' gq_matmul to a few ulps."""
@@ -17,14 +18,15 @@ U32 = 2.0 ** -24
 
 # (fmt, rows, cols, M): matvec, per-row matvecs, the Q4_K tiles (per-wave,
 # 64x16 split in four, 128x32 split in two, 256x32, 256x64), Q5_K on the
-# per-wave and 128x32 tiles, Q4_K rows of 898 columns and Q8_0 / Q6_K on the
-# fp32 matrix cores (including Q8_0 at M = 4, below the fp32 kernel's usual
-# threshold)
+# per-wave and 128x32 tiles, Q8_0 on the fp16 matrix cores (M = 4, below the
+# stored form's threshold; the per-wave and 128x32 tiles), Q4_K rows of 898
+# columns, Q8_0 rows of 29 blocks and Q6_K on the fp32 matrix cores
 CASES = [
     (12, 300, 896, 1), (12, 300, 896, 5),
     (12, 4096, 14336, 16), (12, 14336, 4096, 16), (12, 14336, 4096, 64), (12, 4096, 4096, 300),
     (12, 14336, 1024, 512), (13, 300, 1024, 20), (13, 14336, 4096, 64),
-    (12, 130, 898, 20), (8, 200, 576, 4), (8, 300, 1024, 40), (14, 256, 768, 33),
+    (12, 130, 898, 20), (8, 200, 576, 4), (8, 300, 1024, 40), (8, 4096, 4096, 160),
+    (8, 300, 900, 40), (14, 256, 768, 33),
 ]
 
 
