@@ -43,7 +43,6 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
-MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 SMALL_M = (2, 4, 8)            # few activation rows (batched matvec or matrix cores)
 
 
@@ -202,7 +201,7 @@ def decode_probe(torch, gq, lib, synth, mats, stream_ptr):
 def prefill_probe(torch, gq, lib, synth, stream_ptr, ms=(512,)):
     """One call of each prefill product per M (after one warm-up call):
     Q4_K gate and down on the fp16 matrix cores and, at M = 512, Q6_K down
-    (fp32 matrix cores) and Q5_K gate (fp16); for rocprofv3 --pmc runs (MFMA
+    and Q5_K gate (fp16 as well); for rocprofv3 --pmc runs (MFMA
     busy cycles, executed matrix ops, waits and cache requests per
     dispatch)."""
     cases = []
@@ -709,8 +708,8 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
         del Wd
     log(f"moe: { {k: v for k, v in out.items() if k.startswith('moe')} }")
 
-    # prefill products of the other formats (the Llama-3-8B Q6_K down shape
-    # on the fp32 matrix cores, the Q5_K gate shape on the fp16 ones)
+    # prefill products of the other formats (the Llama-3-8B Q6_K down and
+    # Q5_K gate shapes, both on the fp16 matrix cores)
     for i in (1, 3):
         name, f, r, c, W, _ = synth.mixed_format_weight_and_x(i)
         Wd = torch.from_numpy(W).cuda()
@@ -726,11 +725,8 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
 
             ms = float(np.median([timer.time(mmf, 10 if M < 512 else 5, warmup=1) for _ in range(3)]))
             tf = 2.0 * M * r * c / (ms * 1e-3) / 1e12
-            if f == 13:
-                pct = dict(pct_mfma_f16_peak=round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2))
-            else:
-                pct = dict(pct_mfma_f32_peak=round(100 * tf / MFMA_F32_PEAK_TFLOPS, 2))
-            out[f"matmul_{name}_M{M}"] = dict(us_per_call=round(ms * 1e3, 1), TFLOPs=round(tf, 2), **pct)
+            out[f"matmul_{name}_M{M}"] = dict(us_per_call=round(ms * 1e3, 1), TFLOPs=round(tf, 2),
+                                              pct_mfma_f16_peak=round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2))
         del Wd
     log(f"mixed-format prefill: { {k: v for k, v in out.items() if k.startswith('matmul_llama3')} }")
 

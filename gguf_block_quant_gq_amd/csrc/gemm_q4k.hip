@@ -1,7 +1,7 @@
-// gemm_q4k.hip -- Y = X W^T for Q4_K (and Q5_K, Q8_0) weights and two or
+// gemm_q4k.hip -- Y = X W^T for Q4_K (and Q5_K, Q6_K, Q8_0) weights and two or
 // more activation rows, on the gfx950 matrix cores
 // (v_mfma_f32_16x16x32_f16). One launch; the kernel uses no memory beyond
-// its arguments. The Q5_K and Q8_0 forms are described with their layout
+// its arguments. The Q5_K, Q6_K and Q8_0 forms are described with their layout
 // traits below; this header describes Q4_K.
 //
 // The prompt-chunk product ("nurllama 0.18.1 API", model.nu section: the
@@ -110,6 +110,20 @@ struct MmQ8P {
 };
 struct MmQ8S {
   static constexpr int kKind = 2, kBytes = 256;
+  static constexpr bool kQh = false;
+};
+// Q6_K (kKind 3): 210-byte super-blocks -- 128 bytes of low nibbles, 64 bytes
+// of 2-bit high parts, 16 int8 sub-block scales, fp16 d -- with
+// w = d * sc_s * (q - 32) over 16-weight sub-blocks s. sc * (q - 32) reaches
+// 13 significant bits, so each k-slice takes two exact operands:
+// 16 sh (q - 32) and sl (q - 32) with sc = 16 sh + sl, 0 <= sl < 16 (at most
+// 4096 with its low 4 bits zero, and 480), four products per slice into one
+// sum; d is applied per super-block. A super-block starts 2 bytes into a
+// dword on odd steps (210 = 2 mod 4): the rows must be a multiple of 4 bytes
+// long and W 4-byte aligned, and every piece is loaded from the dword
+// boundary before it and shifted into place.
+struct MmQ6K {
+  static constexpr int kKind = 3, kBytes = 210;
   static constexpr bool kQh = false;
 };
 
@@ -298,6 +312,17 @@ struct WStage<Fm, R, 2> {
   u32x2 cs[R][8];
   u32x4 dd[R];
 };
+// Q6_K: the lane's 8 bytes of each 32-byte group of low nibbles (group
+// p = 2n + h at 32p + 8q) and of high parts (group n at 128 + 32n + 8q), the
+// 16 scale bytes and the dword holding d, each from 2 bytes early on odd
+// steps.
+template <class Fm, int R>
+struct WStage<Fm, R, 3> {
+  u32x3 ql[R][4];
+  u32x3 qh[R][2];
+  u32x4 sc[R];
+  uint32_t sd[R];
+};
 
 __device__ __forceinline__ u32x3 buf_b96(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
   return __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs, voff, soff, 0));
@@ -330,10 +355,18 @@ __device__ __forceinline__ void fetch_w(WStage<Fm, R>& st, __amdgpu_buffer_rsrc_
       }
       st.dq[t][0] = buf_b32(wrs, wv[t] + 68 * q, sb * Fm::kBytes);
       st.dq[t][1] = buf_b32(wrs, wv[t] + 68 * q + 32, sb * Fm::kBytes);
-    } else {
+    } else if constexpr (Fm::kKind == 2) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) st.cs[t][j] = buf_b64(wrs, wv[t] + code_off + 32 * j + 8 * q, sb * Fm::kBytes);
       st.dd[t] = buf_b128(wrs, wv[t], sb * 16);
+    } else {
+      const int soff = sb * Fm::kBytes - 2 * (sb & 1);  // the dword boundary at or before the step
+#pragma unroll
+      for (int p = 0; p < 4; ++p) st.ql[t][p] = buf_b96(wrs, wv[t] + 32 * p + 8 * q, soff);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) st.qh[t][n] = buf_b96(wrs, wv[t] + 128 + 32 * n + 8 * q, soff);
+      st.sc[t] = buf_b128(wrs, wv[t] + 192, soff);
+      st.sd[t] = buf_b32(wrs, wv[t] + 208, soff);
     }
   }
 }
@@ -341,7 +374,7 @@ __device__ __forceinline__ void fetch_w(WStage<Fm, R>& st, __amdgpu_buffer_rsrc_
 // Vector-memory requests of one fetch_w per row tile.
 template <class Fm>
 constexpr int fetch_w_ops() {
-  return Fm::kKind == 0 ? (Fm::kQh ? 6 : 5) : Fm::kKind == 1 ? 10 : 9;
+  return Fm::kKind == 0 ? (Fm::kQh ? 6 : 5) : Fm::kKind == 1 ? 10 : Fm::kKind == 2 ? 9 : 8;
 }
 
 // Q8_0: the lane's 8 code bytes of block j of row tile t, and the block's d
@@ -380,6 +413,58 @@ __device__ __forceinline__ float q8_scale(u32x4 d4, int j, bool real) {
   return real ? d : 0.f;
 }
 
+// Q6_K, one step of row tile t for lane (i, q): the scales of its 8 slices
+// (slice j uses sub-block 2j + q / 2) as signed bytes, and d.
+struct Q6Head {
+  uint32_t s03, s47;
+  float d;
+};
+
+template <class Fm, int R>
+__device__ __forceinline__ Q6Head q6_head(const WStage<Fm, R>& st, int t, int sh, uint32_t sel) {
+  const u32x4 c = st.sc[t];
+  const uint32_t b0 = __builtin_amdgcn_alignbyte(c.y, c.x, sh), b1 = __builtin_amdgcn_alignbyte(c.z, c.y, sh);
+  const uint32_t b2 = __builtin_amdgcn_alignbyte(c.w, c.z, sh), b3 = __builtin_amdgcn_alignbyte(st.sd[t], c.w, sh);
+  Q6Head h;
+  h.s03 = __builtin_amdgcn_perm(b1, b0, sel);
+  h.s47 = __builtin_amdgcn_perm(b3, b2, sel);
+  h.d = half_bits_to_float((st.sd[t] >> (8 * sh)) & 0xFFFFu);
+  return h;
+}
+
+// The two weight operands of slice j (columns 32j..32j+31 of the step; the
+// lane's 8 of them): 16 sh (q - 32) and sl (q - 32).
+template <class Fm, int R>
+__device__ __forceinline__ void q6_operands(const WStage<Fm, R>& st, int t, int j, int sh, const Q6Head& h,
+                                            h8& ahi, h8& alo) {
+  const int n = j >> 2, k4 = j & 3;
+  const u32x3 lr = st.ql[t][2 * n + (k4 & 1)], hr = st.qh[t][n];
+  uint32_t code[2];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t L = __builtin_amdgcn_alignbyte(w ? lr.z : lr.y, w ? lr.y : lr.x, sh);
+    const uint32_t H = __builtin_amdgcn_alignbyte(w ? hr.z : hr.y, w ? hr.y : hr.x, sh);
+    const uint32_t lo = ((k4 >> 1) ? L >> 4 : L) & 0x0F0F0F0Fu;
+    const uint32_t hi = k4 == 0 ? H << 4 : k4 == 1 ? H << 2 : k4 == 2 ? H : H >> 2;
+    code[w] = lo | (hi & 0x30303030u);
+  }
+  constexpr uint32_t kMagic = 0x64646464u;
+  const int sc = (int)(int8_t)(((j < 4 ? h.s03 : h.s47) >> (8 * (j & 3))) & 0xFFu);
+  const int sl = sc & 15;
+  const _Float16 fh = (_Float16)(sc - sl), fl = (_Float16)sl;
+  const h2 khi = {fh, fh}, klo = {fl, fl}, bias = {(_Float16)-1056.f, (_Float16)-1056.f};
+  uint32_t rh[4], rl[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t pk = __builtin_amdgcn_perm(kMagic, code[k >> 1], (k & 1) ? 0x04030402u : 0x04010400u);
+    const h2 c32 = __builtin_bit_cast(h2, pk) + bias;  // q - 32, exact
+    rh[k] = __builtin_bit_cast(uint32_t, c32 * khi);
+    rl[k] = __builtin_bit_cast(uint32_t, c32 * klo);
+  }
+  ahi = as_h8(rh[0], rh[1], rh[2], rh[3]);
+  alo = as_h8(rl[0], rl[1], rl[2], rl[3]);
+}
+
 // An activation tile (16 rows x the 256 columns of one super-block) in LDS:
 // row r at r * kXRow bytes. The 16-byte pad makes the lane reads of the
 // operand layout (16 rows at the same column) hit 16 different bank groups.
@@ -401,6 +486,8 @@ __global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, q = lane >> 4;
+  // Q6_K: the selector of the lane's scale bytes 2j + q / 2 (q6_head)
+  const uint32_t sel6 = (uint32_t)(q >> 1) * 0x01010101u + 0x06040200u;
 
   // the group of this m-tile (groups are few; a linear scan on scalars)
   int gidx = 0;
@@ -537,6 +624,33 @@ __global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
           acc[t][c] = __builtin_fmaf(v, sv[c], acc[t][c]);
         }
       }
+    } else if constexpr (Fm::kKind == 3) {
+      // Q6_K: two exact weight operands per slice into two sums, d per step
+      const int sh = 2 * (sb & 1);
+      Q6Head hd[WR];
+#pragma unroll
+      for (int t = 0; t < WR; ++t) hd[t] = q6_head(st, t, sh, sel6);
+      f32x4 ph[WR], pl[WR];
+#pragma unroll
+      for (int t = 0; t < WR; ++t) ph[t] = pl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h8 xh, xl;
+        x_operands(j, xh, xl);
+#pragma unroll
+        for (int t = 0; t < WR; ++t) {
+          h8 ahi, alo;
+          q6_operands(st, t, j, sh, hd[t], ahi, alo);
+          ph[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ahi, ph[t], 0, 0, 0);
+          pl[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, alo, pl[t], 0, 0, 0);
+          ph[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, ahi, ph[t], 0, 0, 0);
+          pl[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, alo, pl[t], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < WR; ++t)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[t][c] = __builtin_fmaf(hd[t].d * (ph[t][c] + pl[t][c]), sv[c], acc[t][c]);
     } else {
       // Q8_0: block j's product scaled by its d, per block
       const int real = a.nb - 8 * sb;  // blocks of this step inside the row
@@ -668,6 +782,7 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
   const int wr = wave % RS;  // weight-row group
   const int wk = wave / RS;  // super-block group: super-blocks wk, wk + KS, ...
   const int i = lane & 15, q = lane >> 4;
+  const uint32_t sel6 = (uint32_t)(q >> 1) * 0x01010101u + 0x06040200u;  // Q6_K: q6_head
 
   int gidx = 0;
   for (int g = 1; g < a.n_groups; ++g)
@@ -794,7 +909,7 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
 
   // Q8_0: one block per k-slice, each slice's product scaled by its d
   auto compute_q8 = [&](int wslot, int buf, int sb) {
-    if constexpr (Fm::kKind != 0) {
+    if constexpr (Fm::kKind == 1 || Fm::kKind == 2) {
       const uint8_t* base = &xs[wk][buf][0];
       const int real = a.nb - 8 * sb;  // blocks of this step inside the row
       u32x4 d4[R];
@@ -835,6 +950,52 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
         for (int t = 0; t < R; ++t)
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) acc[t][c][cc] = __builtin_fmaf(pd[t][c][cc], sv[cc], acc[t][c][cc]);
+      }
+    }
+  };
+
+  // Q6_K: two exact weight operands per slice into two sums, d per step
+  auto compute_q6 = [&](int wslot, int buf, int sb) {
+    if constexpr (Fm::kKind == 3) {
+      const uint8_t* base = &xs[wk][buf][0];
+      const int sh = 2 * (sb & 1);
+      Q6Head hd[R];
+#pragma unroll
+      for (int t = 0; t < R; ++t) hd[t] = q6_head(ws[wslot], t, sh, sel6);
+      f32x4 ph[R][C], pl[R][C];
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+#pragma unroll
+        for (int c = 0; c < C; ++c) ph[t][c] = pl[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        h8 xh[C], xl[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          xh[c] = *(const h8*)(base + c * kTileBytes + j * kFragBytes + rd_off);
+          xl[c] = *(const h8*)(base + c * kTileBytes + (8 + j) * kFragBytes + rd_off);
+        }
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+          h8 ahi, alo;
+          q6_operands(ws[wslot], t, j, sh, hd[t], ahi, alo);
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            ph[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[c], ahi, ph[t][c], 0, 0, 0);
+            pl[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[c], alo, pl[t][c], 0, 0, 0);
+            ph[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[c], ahi, ph[t][c], 0, 0, 0);
+            pl[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[c], alo, pl[t][c], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const f32x4 sv = *(const f32x4*)&xsv[wk][buf][16 * c + 4 * q];
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc)
+            acc[t][c][cc] = __builtin_fmaf(hd[t].d * (ph[t][c][cc] + pl[t][c][cc]), sv[cc], acc[t][c][cc]);
       }
     }
   };
@@ -914,6 +1075,7 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
         fetch(sb_of(k + D), (u + D) % SX, (u + D) % SW);
         if (k < nk) {
           if constexpr (Fm::kKind == 0) compute(u, k & 1);
+          else if constexpr (Fm::kKind == 3) compute_q6(u, k & 1, sb_of(k));
           else compute_q8(u, k & 1, sb_of(k));
         }
         if (k + 1 < nk) convert(sb_of(k + 1), (u + 1) % SX, (k + 1) & 1);
@@ -1027,20 +1189,25 @@ hipError_t launch_gemm_q4k_epi(MmArgs& m, const GemmArgs& a, const int64_t* grou
     if (gy == 0) return hipSuccess;
     return launch(m, gy, s);
   };
+  // per layout, the tiles whose registers fit without spilling
   if constexpr (Fm::kKind == 0) {
     if (grid(256, 64) >= fill) return run_xs(launch_xs<Fm, 2, 4, 1, 1, 8, EPI>, 64);
     if (grid(256, 32) >= fill) return run_xs(launch_xs<Fm, 2, 2, 2, 1, 8, EPI>, 32);
+    if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 2, 8, EPI>, 32);
+    if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
   } else if constexpr (Fm::kKind == 2) {
     // Q8_0 steps carry twice the weight bytes per lane: 16-row tiles per wave
     if (grid(128, 64) >= fill) return run_xs(launch_xs<Fm, 1, 4, 1, 1, 8, EPI>, 64);
+    if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 2, 8, EPI>, 32);
+    if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
+  } else if constexpr (Fm::kKind == 3) {
+    if (grid(128, 64) >= fill) return run_xs(launch_xs<Fm, 1, 4, 1, 1, 8, EPI>, 64);
+    if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 1, 8, EPI>, 32);
+    if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
   } else {
     // packed Q8_0 also holds 12 bytes per even block: 8-wave tiles only
     if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 1, 8, EPI>, 32);
     if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 2, 4, EPI>, 16);
-  }
-  if constexpr (Fm::kKind != 1) {
-    if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 2, 8, EPI>, 32);
-    if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
   }
   const int gy = build_groups(m, group_m, group_off, n_groups, group_w_bytes, 16);
   if (gy < 0) return hipErrorInvalidValue;
@@ -1083,6 +1250,7 @@ hipError_t launch_gemm_q4k(int fmt, const GemmArgs& a, const int64_t* group_m, c
     case kFmtQ8_0: return launch_gemm_fmt<MmQ8P>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
     case kFmtQ8_0Split:
       return launch_gemm_fmt<MmQ8S>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
+    case kFmtQ6_K: return launch_gemm_fmt<MmQ6K>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
     default: return hipErrorInvalidValue;
   }
 }

@@ -270,13 +270,13 @@ namespace {
 enum MatmulMode { kModeStore = 0, kModeAcc = 1, kModeSwiglu = 2 };
 
 // The layouts the fp16 matrix-core kernels take: Q4_K, Q5_K and split Q8_0
-// rows that are whole groups of four floats, and packed Q8_0 ones whose rows
-// are also a whole number of dwords from a dword-aligned W (their loads are
-// dword loads).
+// rows that are whole groups of four floats, and packed Q8_0 and Q6_K ones
+// whose rows are also a whole number of dwords from a dword-aligned W (their
+// loads are dword loads).
 bool f16_layout(int fmt, int64_t cols, int64_t rb, const void* W) {
   if (cols % 4 != 0) return false;
   if (fmt == GQ_FMT_Q4_K || fmt == GQ_FMT_Q5_K || fmt == GQ_FMT_Q8_0_SPLIT) return true;
-  return fmt == GQ_FMT_Q8_0 && rb % 4 == 0 && (uintptr_t)W % 4 == 0;
+  return (fmt == GQ_FMT_Q8_0 || fmt == GQ_FMT_Q6_K) && rb % 4 == 0 && (uintptr_t)W % 4 == 0;
 }
 
 bool batched_matvec(int64_t M, int64_t rows, int64_t cols) {

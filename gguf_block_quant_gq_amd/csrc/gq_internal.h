@@ -87,8 +87,8 @@ bool gemv_q4k_supports(const GemvArgs& a, int cus, const ExpertArgs* ex);
 hipError_t launch_gemv_q4k(GemvArgs a, int cus, hipStream_t s, int epi, const ExpertArgs* ex);
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
 // The product on the fp16 matrix cores (gemm_q4k.hip; fmt is kFmtQ4_K,
-// kFmtQ5_K, kFmtQ8_0 -- rows a multiple of 4 bytes long, W 4-byte aligned --
-// or kFmtQ8_0Split), one launch for n_groups products that share a
+// kFmtQ5_K, kFmtQ8_0Split, or kFmtQ8_0 / kFmtQ6_K with rows a multiple of 4
+// bytes long and W 4-byte aligned), one launch for n_groups products that share a
 // shape: group g multiplies the weight tensor at W + g * group_w_bytes by the
 // group_m[g] activation rows starting at row group_off[g] of X, into the
 // same rows of Y (a single product: one group). It takes cols % 4 == 0

@@ -108,7 +108,8 @@ def test_invalid_ids_and_empty(gq, oracle):
 # batched matvec (3, 5), and the matrix cores (17 and up), with empty experts
 GROUPED = [
     (12, 512, 2048, [0, 1, 3, 17, 40, 70, 5, 120]),
-    (14, 256, 768, [33, 0, 2, 64]),          # Q6_K: fp32 matrix cores for the large groups
+    (14, 256, 768, [33, 0, 2, 64]),          # Q6_K, 3 super-blocks a row: fp32 matrix cores
+    (14, 256, 1024, [33, 0, 2, 64]),         # Q6_K, rows of 840 bytes: grouped on the fp16 ones
     (8, 300, 900, [9, 16, 0, 1]),            # Q8_0, rows of 29 blocks: few-row kernel / fp32 matrix cores
     (12, 64, 300, [0, 0, 7]),                # ragged rows, one expert with all the rows
     (13, 256, 1024, [20, 0, 2, 64]),         # Q5_K: grouped on the fp16 matrix cores
@@ -119,8 +120,8 @@ GROUPED = [
 @pytest.mark.parametrize("fmt,rows,cols,counts", GROUPED)
 def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
     """Each expert's block of gq_matmul_experts is within tolerance of the
-    oracle. Q4_K and Q5_K with cols % 4 == 0, and Q8_0 whose rows are also a
-    whole number of dwords, run as one grouped launch: a second call gives
+    oracle. Q4_K and Q5_K with cols % 4 == 0, and Q8_0 and Q6_K whose rows
+    are also a whole number of dwords, run as one grouped launch: a second call gives
     the same bits. The others run gq_matmul per expert: each block equals
     gq_matmul of that expert's matrix and rows bit for bit."""
     n_expert, total = len(counts), sum(counts)
@@ -134,7 +135,7 @@ def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
     assert_pad_untouched(Y, total * rows)
     got = to_host(Y)[:total * rows].reshape(total, rows)
     rb = gq.gq_row_bytes(fmt, cols)
-    grouped = cols % 4 == 0 and (fmt in (12, 13) or (fmt == 8 and rb % 4 == 0))
+    grouped = cols % 4 == 0 and (fmt in (12, 13) or (fmt in (8, 14) and rb % 4 == 0))
     o = 0
     for e, m in enumerate(counts):
         if m == 0:

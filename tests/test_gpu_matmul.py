@@ -96,7 +96,7 @@ def test_few_rows_round_like_matvec(gq, fmt, rows, cols, M):
 @pytest.mark.parametrize("fmt,rows,cols,M", [
     (12, 14336, 4096, 5),     # Q4_K past the batched-matvec bound: fp16 matrix cores
     (8, 151936, 896, 2),      # Q8_0 lm_head, two rows: the fp32 few-row kernel
-    (14, 4096, 14336, 5),     # Q6_K: fp32 matrix cores
+    (14, 4096, 14336, 5),     # Q6_K: fp16 matrix cores
     (13, 14336, 4096, 3),     # Q5_K past the batched-matvec bound: fp16 matrix cores
 ])
 def test_few_rows_large_products(gq, oracle, fmt, rows, cols, M):
