@@ -200,10 +200,11 @@ def decode_probe(torch, gq, lib, synth, mats, stream_ptr):
 
 def prefill_probe(torch, gq, lib, synth, stream_ptr, ms=(512,)):
     """One call of each prefill product per M (after one warm-up call):
-    Q4_K gate and down on the fp16 matrix cores and, at M = 512, Q6_K down
-    and Q5_K gate (fp16 as well); for rocprofv3 --pmc runs (MFMA
-    busy cycles, executed matrix ops, waits and cache requests per
-    dispatch)."""
+    Q4_K gate and down on the fp16 matrix cores and, at M = 512, Q6_K down,
+    Q5_K gate and the Q8_0 gate packed and split (fp16 as well; the split
+    layout made by one gq_q8_0_split_repack launch before its two calls);
+    for rocprofv3 --pmc runs (MFMA busy cycles, executed matrix ops, waits
+    and cache requests per dispatch)."""
     cases = []
     for M in ms:
         for which in ("gate", "down"):
@@ -213,10 +214,16 @@ def prefill_probe(torch, gq, lib, synth, stream_ptr, ms=(512,)):
             for i in (1, 3):
                 name, f, r, c, W, _ = synth.mixed_format_weight_and_x(i)
                 cases.append((name, f, W, synth.activations((M, c), synth.rng_for(911, M)), r, c))
+            W8 = synth.weights(gq.FMT_Q8_0, 14336, 4096, synth.rng_for(6, 0))
+            X8 = synth.activations((M, 4096), synth.rng_for(911, M))
+            cases.append(("q8_0_gate", gq.FMT_Q8_0, W8, X8, 14336, 4096))
+            cases.append(("q8_0_split_gate", gq.FMT_Q8_0_SPLIT, W8, X8, 14336, 4096))
     out = {}
     for name, f, W, X, rows, cols in cases:
         M = X.shape[0]
         Wd, Xd = torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda()
+        if f == gq.FMT_Q8_0_SPLIT:
+            Wd = gq.gq_q8_0_split_repack(Wd, rows, cols)
         Yd = torch.empty((M, rows), dtype=torch.float32, device="cuda")
         for _ in range(2):
             st = lib.gq_matmul(f, Wd.data_ptr(), rows, cols, Xd.data_ptr(), M, Yd.data_ptr(),

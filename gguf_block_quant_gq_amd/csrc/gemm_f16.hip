@@ -1,4 +1,4 @@
-// gemm_q4k.hip -- Y = X W^T for Q4_K (and Q5_K, Q6_K, Q8_0) weights and two or
+// gemm_f16.hip -- Y = X W^T for Q4_K (and Q5_K, Q6_K, Q8_0) weights and two or
 // more activation rows, on the gfx950 matrix cores
 // (v_mfma_f32_16x16x32_f16). One launch; the kernel uses no memory beyond
 // its arguments. The Q5_K, Q6_K and Q8_0 forms are described with their layout
@@ -479,7 +479,7 @@ constexpr int kXTile = 16 * kXRow;
 // stride (cols * 4 bytes, a multiple of 4 KB for 4096 or 14336 columns)
 // maps them all to one L2 channel.
 template <class Fm, int WR, int KW, int EPI>
-__global__ __launch_bounds__(KW * 64) void gemm_q4k_kernel(MmArgs a) {
+__global__ __launch_bounds__(KW * 64) void gemm_f16_kernel(MmArgs a) {
   __shared__ f32x4 red[KW][WR][64];
   __shared__ __attribute__((aligned(16))) uint8_t xbuf[KW][2][kXTile];
 
@@ -764,7 +764,7 @@ __device__ __forceinline__ f32x4 buf_f32x4(__amdgpu_buffer_rsrc_t rs, int voff) 
 }
 
 template <class Fm, int R, int C, int D, int KS, int RS, int EPI>
-__global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
+__global__ __launch_bounds__(64 * RS * KS) void gemm_f16_xs_kernel(MmArgs a) {
   static_assert(RS == 4 || (RS == 8 && C % 2 == 0), "row groups");
   constexpr int CW = C * 4 / RS;          // m-tiles each wave converts
   constexpr int SW = D + 1;               // weight ring slots
@@ -1128,14 +1128,14 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_q4k_xs_kernel(MmArgs a) {
 
 template <class Fm, int WR, int EPI>
 hipError_t launch(const MmArgs& a, int gx, int gy, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_q4k_kernel<Fm, WR, GQ_MM_KW, EPI>), dim3(gx, gy), dim3(GQ_MM_KW * 64), 0, s, a);
+  hipLaunchKernelGGL((gemm_f16_kernel<Fm, WR, GQ_MM_KW, EPI>), dim3(gx, gy), dim3(GQ_MM_KW * 64), 0, s, a);
   return hipGetLastError();
 }
 
 template <class Fm, int R, int C, int D, int KS, int RS, int EPI>
 hipError_t launch_xs(const MmArgs& a, int gy, hipStream_t s) {
   const int gx = (a.rows + 16 * RS * R - 1) / (16 * RS * R);
-  hipLaunchKernelGGL((gemm_q4k_xs_kernel<Fm, R, C, D, KS, RS, EPI>), dim3(gx, gy), dim3(64 * RS * KS), 0, s, a);
+  hipLaunchKernelGGL((gemm_f16_xs_kernel<Fm, R, C, D, KS, RS, EPI>), dim3(gx, gy), dim3(64 * RS * KS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1164,7 +1164,7 @@ int build_groups(MmArgs& m, const int64_t* group_m, const int64_t* group_off, in
 
 }  // namespace
 
-bool gemm_q4k_fits(int64_t rows, int64_t cols, int64_t row_bytes) {
+bool gemm_f16_fits(int64_t rows, int64_t cols, int64_t row_bytes) {
   // 31-bit buffer offsets: 256 weight rows and 64 activation rows of a tile
   return 256 * row_bytes < ((int64_t)1 << 31) && 64 * cols * 4 < ((int64_t)1 << 31) && rows <= INT32_MAX;
 }
@@ -1179,7 +1179,7 @@ bool gemm_q4k_fits(int64_t rows, int64_t cols, int64_t row_bytes) {
 namespace {
 
 template <class Fm, int EPI>
-hipError_t launch_gemm_q4k_epi(MmArgs& m, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
+hipError_t launch_gemm_f16_epi(MmArgs& m, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
                                int n_groups, int64_t group_w_bytes, int cus, hipStream_t s) {
   const int64_t fill = (int64_t)cus * 7 / 8;
   auto grid = [&](int tr, int tm) { return ((a.rows + tr - 1) / tr) * count_mtiles(group_m, n_groups, tm); };
@@ -1221,18 +1221,18 @@ hipError_t launch_gemm_fmt(MmArgs& m, const GemmArgs& a, const int64_t* group_m,
                            int n_groups, int64_t group_w_bytes, int cus, hipStream_t s, int epi) {
   switch (epi) {
     case kMmStore:
-      return launch_gemm_q4k_epi<Fm, kMmStore>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
+      return launch_gemm_f16_epi<Fm, kMmStore>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
     case kMmAcc:
-      return launch_gemm_q4k_epi<Fm, kMmAcc>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
+      return launch_gemm_f16_epi<Fm, kMmAcc>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
     case kMmSiluMul:
-      return launch_gemm_q4k_epi<Fm, kMmSiluMul>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
+      return launch_gemm_f16_epi<Fm, kMmSiluMul>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm_q4k(int fmt, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
+hipError_t launch_gemm_f16(int fmt, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
                            int n_groups, int64_t group_w_bytes, int cus, hipStream_t s, int epi) {
   MmArgs m{};
   m.W = a.W;

@@ -4,7 +4,7 @@
 //
 // These formats scale every 16 or 32 weights, and scale * code needs up to
 // 18 significant bits (Q8_0 d*q), so no exact fp16 operand exists (the Q4_K
-// path in gemm_q4k.hip relies on sc*code <= 945). Here each k-chunk of the
+// path in gemm_f16.hip relies on sc*code <= 945). Here each k-chunk of the
 // weight tile is dequantised exactly to fp32 in LDS (gq_quads.h, the same
 // values gq_dequant writes) and multiplied with fp32 activations by
 // v_mfma_f32_16x16x4f32, accumulating in fp32.

@@ -298,7 +298,7 @@ bool matmul_addressable(int fmt, const void* W, int64_t rows, int64_t cols, int6
                         int mode) {
   const int epi = mode == kModeStore ? gq::kMmStore : gq::kMmAcc;
   if (M > 1 && !batched_matvec(M, rows, cols) && f16_route(fmt, cols, rb, W, M, epi))
-    return gq::gemm_q4k_fits(rows, cols, rb);
+    return gq::gemm_f16_fits(rows, cols, rb);
   return true;
 }
 
@@ -308,7 +308,7 @@ int matrix_product(int fmt, const uint8_t* W, int64_t rb, int64_t rows, int64_t 
   gq::GemmArgs a{W, X, Y, rb, (int)rows, (int)cols, (int)M, 0};
   if (f16_route(fmt, cols, rb, W, M, epi)) {
     const int64_t off = 0;
-    return finish(gq::launch_gemm_q4k(fmt, a, &M, &off, 1, 0, cus, s, epi));
+    return finish(gq::launch_gemm_f16(fmt, a, &M, &off, 1, 0, cus, s, epi));
   }
   // the few-row fp32 kernel stores only: the other modes take the fp32 matrix cores
   if (fmt == GQ_FMT_Q4_K || M >= f32_matrix_core_min_m(fmt) || epi != gq::kMmStore)
@@ -421,7 +421,7 @@ extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64
   if ((st = check_align(fmt, W)) != GQ_OK) return st;
   if ((uintptr_t)X % 4 || (uintptr_t)Y % 4) return GQ_ERR_ALIGN;
   if (overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, X, xbytes)) return GQ_ERR_OVERLAP;
-  if (f16_layout(fmt, cols, rb, W) && !gq::gemm_q4k_fits(rows, cols, rb)) return GQ_ERR_SHAPE;
+  if (f16_layout(fmt, cols, rb, W) && !gq::gemm_f16_fits(rows, cols, rb)) return GQ_ERR_SHAPE;
 
   const int cus = current_cus();
   if (cus <= 0) return GQ_ERR_DEVICE;
@@ -440,7 +440,7 @@ extern "C" int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64
         m0 += m_per_expert[e0 + g];
       }
       a.W = (const uint8_t*)W + e0 * ebytes;
-      st = finish(gq::launch_gemm_q4k(fmt, a, m_per_expert + e0, off, ne, ebytes, cus, (hipStream_t)stream));
+      st = finish(gq::launch_gemm_f16(fmt, a, m_per_expert + e0, off, ne, ebytes, cus, (hipStream_t)stream));
       if (st != GQ_OK) return st;
     }
     return GQ_OK;
