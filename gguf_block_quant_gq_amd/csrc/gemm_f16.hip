@@ -27,7 +27,10 @@
 // the fp16 subnormal range and are represented only to an absolute 2^-34 of
 // that largest magnitude.
 //
-// Decomposition. A workgroup of four waves owns 16 WR weight rows and 16 WM
+// Two kernels. The shared-activation kernel (gemm_f16_xs_kernel, below)
+// converts each activation tile once per workgroup into LDS for every wave;
+// it serves the grids that fill the GPU. The per-wave kernel serves the
+// smaller ones: a workgroup of four waves owns 16 WR weight rows and 16
 // activation rows; its waves take the super-blocks in turn (wave w: w, w + 4,
 // ...) and each builds its own operands in registers:
 //   * the weight rows' bytes arrive by buffer loads -- lane (i, q) reads the
