@@ -127,7 +127,10 @@ def test_graph_replays_of_fused_variants(gq, oracle):
 
 # (fmt, rows, cols, M): the Q4_K matrix-core tiles (64x16 split in four,
 # 128x32 split in two, 256x64), the fp32 matrix cores, the int8 path
-MATMULS = [(12, 14336, 4096, 16), (12, 14336, 4096, 64), (12, 4096, 4096, 512), (14, 1024, 4096, 40)]
+# Q4_K on three fp16 tiles, Q6_K / Q8_0 / Q5_K on the fp16 kernels, Q6_K
+# rows of 3 super-blocks on the fp32 matrix cores
+MATMULS = [(12, 14336, 4096, 16), (12, 14336, 4096, 64), (12, 4096, 4096, 512), (14, 1024, 4096, 40),
+           (8, 4096, 4096, 64), (13, 1024, 4096, 32), (14, 1024, 768, 40)]
 
 
 def test_graph_replays_of_products(gq, oracle):
