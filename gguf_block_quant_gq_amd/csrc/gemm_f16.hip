@@ -350,7 +350,9 @@ __device__ __forceinline__ void fetch_w(WStage<Fm, R>& st, __amdgpu_buffer_rsrc_
       for (int g = 0; g < 4; ++g) st.cw[t][g] = buf_b64(wrs, wv[t] + Fm::kCodes + 32 * g + 8 * q, sb * Fm::kBytes);
       if constexpr (Fm::kQh) st.qh[t] = buf_b64(wrs, wv[t] + 16 + 8 * q, sb * Fm::kBytes);
     } else if constexpr (Fm::kKind == 1) {
-      // block 2h at 68h (codes at 68h + 2 + 8q), block 2h + 1 at 68h + 34
+      // block 2h at 68h (codes at 68h + 2 + 8q), block 2h + 1 at 68h + 34. A
+      // row holds an even number of blocks, so its last block is an odd one,
+      // whose 8-byte loads end inside it.
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         st.ce[t][h] = buf_b96(wrs, wv[t] + 68 * h + 8 * q, sb * Fm::kBytes);
@@ -363,7 +365,11 @@ __device__ __forceinline__ void fetch_w(WStage<Fm, R>& st, __amdgpu_buffer_rsrc_
       for (int j = 0; j < 8; ++j) st.cs[t][j] = buf_b64(wrs, wv[t] + code_off + 32 * j + 8 * q, sb * Fm::kBytes);
       st.dd[t] = buf_b128(wrs, wv[t], sb * 16);
     } else {
-      const int soff = sb * Fm::kBytes - 2 * (sb & 1);  // the dword boundary at or before the step
+      // the dword boundary at or before the step. On even steps the dword of
+      // d also holds the next step's first 2 bytes; a row holds an even number
+      // of super-blocks, so its last step is odd and that dword never crosses
+      // the end of the buffer (whose range check would zero all of it).
+      const int soff = sb * Fm::kBytes - 2 * (sb & 1);
 #pragma unroll
       for (int p = 0; p < 4; ++p) st.ql[t][p] = buf_b96(wrs, wv[t] + 32 * p + 8 * q, soff);
 #pragma unroll
