@@ -152,3 +152,33 @@ def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
         gq.gq_matmul_experts(fmt, Wd, n_expert, rows, cols, Xd, counts, Y=Y2[:total * rows])
         again = to_host(Y2)[:total * rows].reshape(total, rows)
         assert np.array_equal(again.view(np.uint32), got.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [12, 8, 14])
+def test_grouped_prefill_past_64_experts(gq, oracle, fmt):
+    """130 experts (some with no rows): the grouped product runs as three
+    launches of at most 64 experts; every expert's block is within tolerance
+    of the oracle and a second call gives the same bits."""
+    n_expert, rows, cols = 130, 48, 1024
+    rng = synth.rng_for(964, fmt)
+    counts = [int(c) for c in rng.integers(0, 6, n_expert)]
+    counts[0], counts[63], counts[64], counts[129] = 0, 3, 5, 2
+    total = sum(counts)
+    W = synth.weights(fmt, n_expert * rows, cols, rng)
+    X = synth.activations((total, cols), rng)
+    print(f"[grouped] {n_expert} experts fmt={fmt} rows={rows} cols={cols} total={total}", flush=True)
+    Wd, Xd = to_dev(W), to_dev(X)
+    Y = sentinel_buffer(total * rows)
+    gq.gq_matmul_experts(fmt, Wd, n_expert, rows, cols, Xd, counts, Y=Y[:total * rows])
+    assert_pad_untouched(Y, total * rows)
+    got = to_host(Y)[:total * rows].reshape(total, rows)
+    rb = gq.gq_row_bytes(fmt, cols)
+    o = 0
+    for e, m in enumerate(counts):
+        if m:
+            ref, S = oracle.matmul(fmt, W[e * rows * rb:(e + 1) * rows * rb], rows, cols, X[o:o + m])
+            assert_within_tolerance(got[o:o + m], ref, S, f"expert {e}")
+        o += m
+    Y2 = sentinel_buffer(total * rows)
+    gq.gq_matmul_experts(fmt, Wd, n_expert, rows, cols, Xd, counts, Y=Y2[:total * rows])
+    assert np.array_equal(to_host(Y2)[:total * rows].view(np.uint32), got.reshape(-1).view(np.uint32))
