@@ -716,8 +716,9 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
     log(f"moe: { {k: v for k, v in out.items() if k.startswith('moe')} }")
 
     # prefill products of the other formats (the Llama-3-8B Q6_K down and
-    # Q5_K gate shapes, both on the fp16 matrix cores)
-    for i in (1, 3):
+    # Q5_K gate shapes and the Qwen2.5-0.5B Q5_0 4864x896, all on the fp16
+    # matrix cores)
+    for i in (1, 3, 7):
         name, f, r, c, W, _ = synth.mixed_format_weight_and_x(i)
         Wd = torch.from_numpy(W).cuda()
         del W
@@ -735,7 +736,7 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
             out[f"matmul_{name}_M{M}"] = dict(us_per_call=round(ms * 1e3, 1), TFLOPs=round(tf, 2),
                                               pct_mfma_f16_peak=round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2))
         del Wd
-    log(f"mixed-format prefill: { {k: v for k, v in out.items() if k.startswith('matmul_llama3')} }")
+    log(f"mixed-format prefill: { {k: v for k, v in out.items() if k.startswith(('matmul_llama3', 'matmul_qwen'))} }")
 
     # Q8_0 prefill products at the Llama-3-8B gate and down shapes (fp16
     # matrix cores), packed and in the split per-row layout; weights seed 6,

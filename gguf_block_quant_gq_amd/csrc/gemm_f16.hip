@@ -1,8 +1,8 @@
-// gemm_f16.hip -- Y = X W^T for Q4_K (and Q5_K, Q6_K, Q8_0) weights and two or
-// more activation rows, on the gfx950 matrix cores
+// gemm_f16.hip -- Y = X W^T for Q4_K (and Q5_K, Q6_K, Q8_0, Q5_0) weights
+// and two or more activation rows, on the gfx950 matrix cores
 // (v_mfma_f32_16x16x32_f16). One launch; the kernel uses no memory beyond
-// its arguments. The Q5_K, Q6_K and Q8_0 forms are described with their layout
-// traits below; this header describes Q4_K.
+// its arguments. The other layouts are described with their traits below;
+// this header describes Q4_K.
 //
 // The prompt-chunk product ("nurllama 0.18.1 API", model.nu section: the
 // matmuls run over a chunk of positions at once, each weight read once per
@@ -127,6 +127,17 @@ struct MmQ8S {
 // boundary before it and shifted into place.
 struct MmQ6K {
   static constexpr int kKind = 3, kBytes = 210;
+  static constexpr bool kQh = false;
+};
+// Q5_0 (kKind 4): 22-byte blocks -- fp16 d, a 32-bit word qh whose bit k is
+// bit 4 of weight k, 16 bytes of nibbles (weight k < 16: low nibble of byte
+// k, else high nibble of byte k - 16) -- with w = d * (q - 16). Handled as
+// Q8_0: one block per k-slice, the operand q - 16 exact in fp16, d per
+// block. Eight blocks make 176 bytes, so with rows of an even number of
+// blocks and W 4-byte aligned even blocks are dword aligned and odd ones
+// start 2 bytes into a dword.
+struct MmQ50 {
+  static constexpr int kKind = 4, kBytes = 176;
   static constexpr bool kQh = false;
 };
 
@@ -315,6 +326,16 @@ struct WStage<Fm, R, 2> {
   u32x2 cs[R][8];
   u32x4 dd[R];
 };
+// Q5_0: the lane's 8 nibble bytes of each block (bytes 8 (q % 2)..: 12 from
+// 2 bytes early for the even blocks), and the dwords holding d and qh of
+// blocks 2q and 2q + 1 (at 44q, 44q + 4, 44q + 20, 44q + 24), which the
+// row's four lanes share through ds_bpermute.
+template <class Fm, int R>
+struct WStage<Fm, R, 4> {
+  u32x3 qe[R][4];
+  u32x2 qo[R][4];
+  u32x2 dh[R][2];
+};
 // Q6_K: the lane's 8 bytes of each 32-byte group of low nibbles (group
 // p = 2n + h at 32p + 8q) and of high parts (group n at 128 + 32n + 8q), the
 // 16 scale bytes and the dword holding d, each from 2 bytes early on odd
@@ -364,7 +385,7 @@ __device__ __forceinline__ void fetch_w(WStage<Fm, R>& st, __amdgpu_buffer_rsrc_
 #pragma unroll
       for (int j = 0; j < 8; ++j) st.cs[t][j] = buf_b64(wrs, wv[t] + code_off + 32 * j + 8 * q, sb * Fm::kBytes);
       st.dd[t] = buf_b128(wrs, wv[t], sb * 16);
-    } else {
+    } else if constexpr (Fm::kKind == 3) {
       // the dword boundary at or before the step. On even steps the dword of
       // d also holds the next step's first 2 bytes; a row holds an even number
       // of super-blocks, so its last step is odd and that dword never crosses
@@ -376,6 +397,16 @@ __device__ __forceinline__ void fetch_w(WStage<Fm, R>& st, __amdgpu_buffer_rsrc_
       for (int n = 0; n < 2; ++n) st.qh[t][n] = buf_b96(wrs, wv[t] + 128 + 32 * n + 8 * q, soff);
       st.sc[t] = buf_b128(wrs, wv[t] + 192, soff);
       st.sd[t] = buf_b32(wrs, wv[t] + 208, soff);
+    } else {
+      // block 2h at 44h (nibbles from 44h + 6), 2h + 1 at 44h + 22 (from
+      // 44h + 28); the row's last block is an odd one, whose loads end in it
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        st.qe[t][h] = buf_b96(wrs, wv[t] + 44 * h + 4 + 8 * (q & 1), sb * Fm::kBytes);
+        st.qo[t][h] = buf_b64(wrs, wv[t] + 44 * h + 28 + 8 * (q & 1), sb * Fm::kBytes);
+      }
+      st.dh[t][0] = buf_b64(wrs, wv[t] + 44 * q, sb * Fm::kBytes);
+      st.dh[t][1] = buf_b64(wrs, wv[t] + 44 * q + 20, sb * Fm::kBytes);
     }
   }
 }
@@ -383,7 +414,7 @@ __device__ __forceinline__ void fetch_w(WStage<Fm, R>& st, __amdgpu_buffer_rsrc_
 // Vector-memory requests of one fetch_w per row tile.
 template <class Fm>
 constexpr int fetch_w_ops() {
-  return Fm::kKind == 0 ? (Fm::kQh ? 6 : 5) : Fm::kKind == 1 ? 10 : Fm::kKind == 2 ? 9 : 8;
+  return Fm::kKind == 0 ? (Fm::kQh ? 6 : 5) : Fm::kKind == 1 ? 10 : Fm::kKind == 2 ? 9 : Fm::kKind == 3 ? 8 : 10;
 }
 
 // Q8_0: the lane's 8 code bytes of block j of row tile t, and the block's d
@@ -420,6 +451,66 @@ __device__ __forceinline__ float q8_scale(u32x4 d4, int j, bool real) {
   const uint32_t w = d4[j >> 1];
   const float d = half_bits_to_float((j & 1) ? w >> 16 : w & 0xFFFFu);
   return real ? d : 0.f;
+}
+
+// Q5_0: the operand of block j (codes q - 16 of the lane's 8 weights) and
+// its d (zero for a block past the row's last). Lane (i, h) holds the d and
+// qh dwords of blocks 2h and 2h + 1 of row i.
+template <class Fm, int R>
+__device__ __forceinline__ h8 q5_operand(const WStage<Fm, R>& st, int t, int j, int i, int q, bool real, float& d) {
+  const int src = (16 * (j >> 1) + i) << 2;
+  uint32_t d16, qh;
+  u32x2 L;
+  if (j & 1) {
+    const uint32_t b0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)st.dh[t][1].x);
+    qh = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)st.dh[t][1].y);
+    d16 = b0 >> 16;
+    L = st.qo[t][j >> 1];
+  } else {
+    const uint32_t a0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)st.dh[t][0].x);
+    const uint32_t a1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)st.dh[t][0].y);
+    d16 = a0 & 0xFFFFu;
+    qh = __builtin_amdgcn_alignbyte(a1, a0, 2);
+    const u32x3 e = st.qe[t][j >> 1];
+    L = u32x2{__builtin_amdgcn_alignbyte(e.y, e.x, 2), __builtin_amdgcn_alignbyte(e.z, e.y, 2)};
+  }
+  d = real ? half_bits_to_float(d16) : 0.f;
+  // weights 8q..8q+7: nibbles of bytes 8 (q % 2).. (high ones for q >= 2),
+  // fifth bits = byte q of qh, each bit moved to bit 4 of its code byte
+  // ((b * 0x204081) & 0x01010101 puts bit e of a 4-bit b in byte e)
+  const uint32_t nsh = 4u * (uint32_t)(q >> 1);
+  const uint32_t hb = (qh >> (8 * q)) & 0xFFu;
+  const uint32_t c0 = ((L.x >> nsh) & 0x0F0F0F0Fu) | ((((hb & 0xFu) * 0x204081u) & 0x01010101u) << 4);
+  const uint32_t c1 = ((L.y >> nsh) & 0x0F0F0F0Fu) | ((((hb >> 4) * 0x204081u) & 0x01010101u) << 4);
+  constexpr uint32_t kMagic = 0x64646464u;
+  const h2 bias = {(_Float16)-1040.f, (_Float16)-1040.f};
+  uint32_t r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t pk = __builtin_amdgcn_perm(kMagic, k < 2 ? c0 : c1, (k & 1) ? 0x04030402u : 0x04010400u);
+    r[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, pk) + bias);  // q - 16, exact
+  }
+  return as_h8(r[0], r[1], r[2], r[3]);
+}
+
+// Block formats (Q8_0, Q5_0): what a step of row tile t needs for every
+// block (the Q8_0 scales), then each block's operand and d.
+template <class Fm, int R>
+__device__ __forceinline__ u32x4 blk_head(const WStage<Fm, R>& st, int t, int i) {
+  if constexpr (Fm::kKind == 4) return u32x4{0u, 0u, 0u, 0u};
+  else return q8_scales(st, t, i);
+}
+
+template <class Fm, int R>
+__device__ __forceinline__ h8 blk_operand(const WStage<Fm, R>& st, u32x4 head, int t, int j, int i, int q,
+                                          bool real, float& d) {
+  if constexpr (Fm::kKind == 4) {
+    return q5_operand(st, t, j, i, q, real, d);
+  } else {
+    const u32x2 c = q8_codes(st, t, j);
+    d = q8_scale(head, j, real);
+    return q8_operand(c.x, c.y);
+  }
 }
 
 // Q6_K, one step of row tile t for lane (i, q): the scales of its 8 slices
@@ -661,11 +752,11 @@ __global__ __launch_bounds__(KW * 64) void gemm_f16_kernel(MmArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[t][c] = __builtin_fmaf(hd[t].d * (ph[t][c] + pl[t][c]), sv[c], acc[t][c]);
     } else {
-      // Q8_0: block j's product scaled by its d, per block
+      // Q8_0, Q5_0: block j's product scaled by its d, per block
       const int real = a.nb - 8 * sb;  // blocks of this step inside the row
       u32x4 d4[WR];
 #pragma unroll
-      for (int t = 0; t < WR; ++t) d4[t] = q8_scales(st, t, i);
+      for (int t = 0; t < WR; ++t) d4[t] = blk_head(st, t, i);
       f32x4 pd[WR];
 #pragma unroll
       for (int t = 0; t < WR; ++t) pd[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -675,9 +766,8 @@ __global__ __launch_bounds__(KW * 64) void gemm_f16_kernel(MmArgs a) {
         x_operands(j, xh, xl);
 #pragma unroll
         for (int t = 0; t < WR; ++t) {
-          const u32x2 c = q8_codes(st, t, j);
-          const h8 wop = q8_operand(c.x, c.y);
-          const float d = q8_scale(d4[t], j, j < real);
+          float d;
+          const h8 wop = blk_operand(st, d4[t], t, j, i, q, j < real, d);
           f32x4 p = {0.f, 0.f, 0.f, 0.f};
           p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, wop, p, 0, 0, 0);
           p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, wop, p, 0, 0, 0);
@@ -916,14 +1006,14 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_f16_xs_kernel(MmArgs a) {
 #pragma unroll
     for (int c = 0; c < C; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Q8_0: one block per k-slice, each slice's product scaled by its d
+  // Q8_0, Q5_0: one block per k-slice, each slice's product scaled by its d
   auto compute_q8 = [&](int wslot, int buf, int sb) {
-    if constexpr (Fm::kKind == 1 || Fm::kKind == 2) {
+    if constexpr (Fm::kKind == 1 || Fm::kKind == 2 || Fm::kKind == 4) {
       const uint8_t* base = &xs[wk][buf][0];
       const int real = a.nb - 8 * sb;  // blocks of this step inside the row
       u32x4 d4[R];
 #pragma unroll
-      for (int t = 0; t < R; ++t) d4[t] = q8_scales(ws[wslot], t, i);
+      for (int t = 0; t < R; ++t) d4[t] = blk_head(ws[wslot], t, i);
       f32x4 pd[R][C];
 #pragma unroll
       for (int t = 0; t < R; ++t)
@@ -939,9 +1029,8 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_f16_xs_kernel(MmArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < R; ++t) {
-          const u32x2 cw = q8_codes(ws[wslot], t, j);
-          const h8 wop = q8_operand(cw.x, cw.y);
-          const float d = q8_scale(d4[t], j, j < real);
+          float d;
+          const h8 wop = blk_operand(ws[wslot], d4[t], t, j, i, q, j < real, d);
 #pragma unroll
           for (int c = 0; c < C; ++c) {
             f32x4 p = {0.f, 0.f, 0.f, 0.f};
@@ -1182,15 +1271,25 @@ bool gemm_f16_fits(int64_t rows, int64_t cols, int64_t row_bytes) {
 // down): the largest shared-activation tile whose grid still fills about
 // every CU -- 256 x 64 (gate M = 512: 191 us), 256 x 32 (down M = 512:
 // 213 us), 128 x 32 split in two along k (gate M = 64: 38 us), 64 x 16 split
-// in four (gate M = 16: 19 us, down M = 64: 56 us) -- else the per-wave
-// kernel with as many weight-row tiles per workgroup as still fill the GPU
-// (down M = 16: 30 us).
+// in four (gate M = 16: 19 us, down M = 64: 56 us; it also takes grids of
+// 3/4 of the CUs, or a quarter for rows of at most 4 steps) -- else the
+// per-wave kernel with as many weight-row tiles per workgroup as still fill
+// the GPU (down M = 16: 30 us). The other layouts use the tiles their
+// registers allow (below).
 namespace {
 
 template <class Fm, int EPI>
 hipError_t launch_gemm_f16_epi(MmArgs& m, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
                                int n_groups, int64_t group_w_bytes, int cus, hipStream_t s) {
   const int64_t fill = (int64_t)cus * 7 / 8;
+  // the 64 x 16 shared tile from 3/4 of the CUs, and for rows of at most 4
+  // steps from a quarter of them: measured faster than the per-wave kernel
+  // there (8B down at M = 48: 55 against 68 us; 4864 x 896 at M = 32: 8.8
+  // against 16 us), and slower below
+  const bool xs16 = [&] {
+    const int64_t g = ((a.rows + 63) / 64) * count_mtiles(group_m, n_groups, 16);
+    return g >= (int64_t)cus * 3 / 4 || (m.nsb <= 4 && g >= cus / 4);
+  }();
   auto grid = [&](int tr, int tm) { return ((a.rows + tr - 1) / tr) * count_mtiles(group_m, n_groups, tm); };
   auto run_xs = [&](auto launch, int tm) {
     const int gy = build_groups(m, group_m, group_off, n_groups, group_w_bytes, tm);
@@ -1203,20 +1302,20 @@ hipError_t launch_gemm_f16_epi(MmArgs& m, const GemmArgs& a, const int64_t* grou
     if (grid(256, 64) >= fill) return run_xs(launch_xs<Fm, 2, 4, 1, 1, 8, EPI>, 64);
     if (grid(256, 32) >= fill) return run_xs(launch_xs<Fm, 2, 2, 2, 1, 8, EPI>, 32);
     if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 2, 8, EPI>, 32);
-    if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
+    if (xs16) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
   } else if constexpr (Fm::kKind == 2) {
     // Q8_0 steps carry twice the weight bytes per lane: 16-row tiles per wave
     if (grid(128, 64) >= fill) return run_xs(launch_xs<Fm, 1, 4, 1, 1, 8, EPI>, 64);
     if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 2, 8, EPI>, 32);
-    if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
+    if (xs16) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
   } else if constexpr (Fm::kKind == 3) {
     if (grid(128, 64) >= fill) return run_xs(launch_xs<Fm, 1, 4, 1, 1, 8, EPI>, 64);
     if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 1, 8, EPI>, 32);
-    if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
+    if (xs16) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
   } else {
-    // packed Q8_0 also holds 12 bytes per even block: 8-wave tiles only
+    // packed Q8_0 and Q5_0 also hold 12 bytes per even block: 8-wave tiles only
     if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 1, 8, EPI>, 32);
-    if (grid(64, 16) >= fill) return run_xs(launch_xs<Fm, 1, 1, 1, 2, 4, EPI>, 16);
+    if (xs16) return run_xs(launch_xs<Fm, 1, 1, 1, 2, 4, EPI>, 16);
   }
   const int gy = build_groups(m, group_m, group_off, n_groups, group_w_bytes, 16);
   if (gy < 0) return hipErrorInvalidValue;
@@ -1260,6 +1359,7 @@ hipError_t launch_gemm_f16(int fmt, const GemmArgs& a, const int64_t* group_m, c
     case kFmtQ8_0Split:
       return launch_gemm_fmt<MmQ8S>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
     case kFmtQ6_K: return launch_gemm_fmt<MmQ6K>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
+    case kFmtQ5_0: return launch_gemm_fmt<MmQ50>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
     default: return hipErrorInvalidValue;
   }
 }

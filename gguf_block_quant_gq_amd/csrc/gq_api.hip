@@ -270,13 +270,14 @@ namespace {
 enum MatmulMode { kModeStore = 0, kModeAcc = 1, kModeSwiglu = 2 };
 
 // The layouts the fp16 matrix-core kernels take: Q4_K, Q5_K and split Q8_0
-// rows that are whole groups of four floats, and packed Q8_0 and Q6_K ones
+// rows that are whole groups of four floats, and Q8_0, Q5_0 and Q6_K ones
 // whose rows are also a whole number of dwords from a dword-aligned W (their
 // loads are dword loads).
 bool f16_layout(int fmt, int64_t cols, int64_t rb, const void* W) {
   if (cols % 4 != 0) return false;
   if (fmt == GQ_FMT_Q4_K || fmt == GQ_FMT_Q5_K || fmt == GQ_FMT_Q8_0_SPLIT) return true;
-  return (fmt == GQ_FMT_Q8_0 || fmt == GQ_FMT_Q6_K) && rb % 4 == 0 && (uintptr_t)W % 4 == 0;
+  const bool dword_rows = rb % 4 == 0 && (uintptr_t)W % 4 == 0;
+  return (fmt == GQ_FMT_Q8_0 || fmt == GQ_FMT_Q5_0 || fmt == GQ_FMT_Q6_K) && dword_rows;
 }
 
 bool batched_matvec(int64_t M, int64_t rows, int64_t cols) {
@@ -284,12 +285,13 @@ bool batched_matvec(int64_t M, int64_t rows, int64_t cols) {
 }
 
 // Whether a product of M activation rows past the batched-matvec bound runs
-// on the fp16 matrix cores: every layout above, except that packed Q8_0 with
-// fewer rows than the fp32 kernels' threshold keeps the few-row kernel for
-// the stored form.
+// on the fp16 matrix cores: every layout above, except that packed Q8_0 and
+// Q5_0 with fewer rows than the matrix cores' threshold keep the few-row
+// kernel for the stored form.
 bool f16_route(int fmt, int64_t cols, int64_t rb, const void* W, int64_t M, int epi) {
   if (!f16_layout(fmt, cols, rb, W)) return false;
-  return fmt != GQ_FMT_Q8_0 || M >= f32_matrix_core_min_m(fmt) || epi != gq::kMmStore;
+  const bool few_row_kernel = fmt == GQ_FMT_Q8_0 || fmt == GQ_FMT_Q5_0;
+  return !few_row_kernel || M >= f32_matrix_core_min_m(fmt) || epi != gq::kMmStore;
 }
 
 // Whether the kernel that gq_matmul picks for this shape can address it

@@ -87,13 +87,13 @@ bool gemv_q4k_supports(const GemvArgs& a, int cus, const ExpertArgs* ex);
 hipError_t launch_gemv_q4k(GemvArgs a, int cus, hipStream_t s, int epi, const ExpertArgs* ex);
 hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
 // The product on the fp16 matrix cores (gemm_f16.hip; fmt is kFmtQ4_K,
-// kFmtQ5_K, kFmtQ8_0Split, or kFmtQ8_0 / kFmtQ6_K with rows a multiple of 4
-// bytes long and W 4-byte aligned), one launch for n_groups products that share a
-// shape: group g multiplies the weight tensor at W + g * group_w_bytes by the
-// group_m[g] activation rows starting at row group_off[g] of X, into the
-// same rows of Y (a single product: one group). It takes cols % 4 == 0
-// (activations are read four at a time); gemm_f16_fits: whether its 31-bit
-// buffer offsets cover the shape.
+// kFmtQ5_K, kFmtQ8_0Split, or kFmtQ8_0 / kFmtQ5_0 / kFmtQ6_K with rows a
+// multiple of 4 bytes long and W 4-byte aligned), one launch for n_groups
+// products that share a shape: group g multiplies the weight tensor at
+// W + g * group_w_bytes by the group_m[g] activation rows starting at row
+// group_off[g] of X, into the same rows of Y (a single product: one group).
+// It takes cols % 4 == 0 (activations are read four at a time);
+// gemm_f16_fits: whether its 31-bit buffer offsets cover the shape.
 bool gemm_f16_fits(int64_t rows, int64_t cols, int64_t row_bytes);
 hipError_t launch_gemm_f16(int fmt, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
                            int n_groups, int64_t group_w_bytes, int cus, hipStream_t s, int epi = kMmStore);

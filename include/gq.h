@@ -226,12 +226,13 @@ int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out, v
  * equals gq_matvec of its activation row bit for bit. Otherwise, in one
  * launch:
  *   - On the fp16 matrix cores, with exact operands: Q4_K, Q5_K and split
- *     Q8_0 with cols % 4 == 0; Q6_K, and from M = 8 Q8_0, with cols % 4 == 0,
- *     a row length gq_row_bytes(fmt, cols) that is a multiple of 4 (an even
- *     number of super-blocks or blocks) and W 4-byte aligned. The weight
- *     operand is sc * code (at most 63 * 31), the int8 code, or for Q6_K the
- *     pair 16 sh (q - 32), sl (q - 32) with sc = 16 sh + sl, all exact in
- *     fp16, with d (and dmin) applied in fp32 per super-block or block;
+ *     Q8_0 with cols % 4 == 0; Q6_K, and from M = 8 Q8_0 and Q5_0, with
+ *     cols % 4 == 0, a row length gq_row_bytes(fmt, cols) that is a multiple
+ *     of 4 (an even number of super-blocks or blocks) and W 4-byte aligned.
+ *     The weight operand is sc * code (at most 63 * 31), the int8 code, the
+ *     Q5_0 code - 16, or for Q6_K the pair 16 sh (q - 32), sl (q - 32) with
+ *     sc = 16 sh + sl, all exact in fp16, with d (and dmin) applied in fp32
+ *     per super-block or block;
  *     each activation row's 256 values of a 256-column step are scaled by a
  *     power of two and split into fp16 hi and lo parts. They need 64 * 4 * cols < 2^31 and
  *     256 * gq_row_bytes(fmt, cols) < 2^31 (Q4_K: cols < 2^23), else
@@ -240,10 +241,11 @@ int gq_q8_0_split_repack(const void* W, int64_t rows, int64_t cols, void* out, v
  *     their row's step b (256 columns) are carried only to an absolute
  *     2^-34 max_b: an extra error of at most 2^-33 * max_b * sum_{c in b}
  *     |w(r, c)|-terms per step (Q4_K / Q5_K: |d sc_j q_c| + |dmin m_j|;
- *     Q8_0: |d q_c|; Q6_K: |d sc_s (q_c - 32)|), none when every activation
- *     is 0 or within that range.
+ *     Q8_0: |d q_c|; Q5_0: |d (q_c - 16)|; Q6_K: |d sc_s (q_c - 32)|), none
+ *     when every activation is 0 or within that range.
  *   - The other products with M >= 2 of Q4_K, Q5_K, Q6_K and split Q8_0,
- *     and with M >= 8 of Q8_0 and Q5_0, run on the fp32 matrix cores: each
+ *     and with M >= 8 of Q8_0 and Q5_0 (rows those kernels do not take), run
+ *     on the fp32 matrix cores: each
  *     k-chunk of W is dequantised exactly to fp32 and multiplied with the
  *     fp32 activations; same accuracy bound as gq_matvec.
  *   - Q8_0 and Q5_0 with 2 <= M < 8 stream W once per 15 activation rows on

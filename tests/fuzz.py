@@ -61,9 +61,9 @@ def main() -> int:
         base = 8 if fmt == 1008 else fmt
         qk = 256 if base in (12, 13, 14) else 32
         cols = int(rng.integers(1, 70 * qk))
-        if fmt != 6 and rng.random() < 0.5:
-            # the fp16 matrix-core route needs cols % 4 == 0 (and, for Q8_0
-            # and Q6_K, rows of an even number of blocks or super-blocks)
+        if rng.random() < 0.5:
+            # the fp16 matrix-core route needs cols % 4 == 0 (and, for Q8_0,
+            # Q5_0 and Q6_K, rows of an even number of blocks or super-blocks)
             cols = (cols + 3) // 4 * 4
         rows = int(rng.integers(1, 3000))
         M = int(rng.choice(M_CHOICES))

@@ -114,14 +114,15 @@ GROUPED = [
     (12, 64, 300, [0, 0, 7]),                # ragged rows, one expert with all the rows
     (13, 256, 1024, [20, 0, 2, 64]),         # Q5_K: grouped on the fp16 matrix cores
     (8, 256, 1024, [20, 0, 3, 64]),          # Q8_0 (rows of 1088 bytes): grouped as well
+    (6, 256, 896, [20, 0, 3, 64]),           # Q5_0, 28 blocks a row: grouped as well
 ]
 
 
 @pytest.mark.parametrize("fmt,rows,cols,counts", GROUPED)
 def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
     """Each expert's block of gq_matmul_experts is within tolerance of the
-    oracle. Q4_K and Q5_K with cols % 4 == 0, and Q8_0 and Q6_K whose rows
-    are also a whole number of dwords, run as one grouped launch: a second call gives
+    oracle. Q4_K and Q5_K with cols % 4 == 0, and Q8_0, Q5_0 and Q6_K whose
+    rows are also a whole number of dwords, run as one grouped launch: a second call gives
     the same bits. The others run gq_matmul per expert: each block equals
     gq_matmul of that expert's matrix and rows bit for bit."""
     n_expert, total = len(counts), sum(counts)
@@ -135,7 +136,7 @@ def test_grouped_prefill(gq, oracle, fmt, rows, cols, counts):
     assert_pad_untouched(Y, total * rows)
     got = to_host(Y)[:total * rows].reshape(total, rows)
     rb = gq.gq_row_bytes(fmt, cols)
-    grouped = cols % 4 == 0 and (fmt in (12, 13) or (fmt in (8, 14) and rb % 4 == 0))
+    grouped = cols % 4 == 0 and (fmt in (12, 13) or (fmt in (6, 8, 14) and rb % 4 == 0))
     o = 0
     for e, m in enumerate(counts):
         if m == 0:

@@ -266,12 +266,13 @@ def test_prefill_full_size(gq, oracle, i, M):
 
 
 @pytest.mark.parametrize("fmt,rows,cols,M", [(8, 4096, 4096, 64), (8, 65, 1004, 33), (8, 65, 1006, 33),
-                                             (6, 130, 8224, 17), (14, 63, 300, 48), (14, 63, 302, 48),
+                                             (6, 130, 8224, 17), (6, 130, 8192, 17), (14, 63, 300, 48),
+                                             (14, 63, 302, 48),
                                              (13, 200, 1024, 100)])
 def test_matrix_core_edges(gq, oracle, fmt, rows, cols, M):
     """Ragged rows, columns and activation rows on the matrix cores: the fp16
-    kernels for the Q8_0, Q6_K and Q5_K rows they take, the fp32 ones for
-    Q5_0 and for rows whose length is not a multiple of 4 (which take the
+    kernels for the rows they take, the fp32 ones for the others (an odd
+    number of blocks, or a length not a multiple of 4, which takes the
     scalar activation loads)."""
     rng = synth.rng_for(912, fmt * 1000 + rows)
     W = synth.weights(fmt, rows, cols, rng)

@@ -19,15 +19,17 @@ U32 = 2.0 ** -24
 # (fmt, rows, cols, M): matvec, per-row matvecs, the Q4_K tiles (per-wave,
 # 64x16 split in four, 128x32 split in two, 256x32, 256x64), Q5_K on the
 # per-wave and 128x32 tiles, Q8_0 on the fp16 matrix cores (M = 4, below the
-# stored form's threshold; the per-wave and 128x32 tiles), Q6_K on them (the
-# per-wave and 128x32 tiles), Q4_K rows of 898 columns, Q8_0 rows of 29
-# blocks and Q6_K rows of 3 super-blocks on the fp32 matrix cores
+# stored form's threshold; the per-wave and 128x32 tiles), Q6_K and Q5_0 on
+# them (the per-wave and 128x32 tiles), Q4_K rows of 898 columns, Q8_0 rows
+# of 29 blocks, Q6_K rows of 3 super-blocks and Q5_0 rows of 33 blocks on the
+# fp32 matrix cores
 CASES = [
     (12, 300, 896, 1), (12, 300, 896, 5),
     (12, 4096, 14336, 16), (12, 14336, 4096, 16), (12, 14336, 4096, 64), (12, 4096, 4096, 300),
     (12, 14336, 1024, 512), (13, 300, 1024, 20), (13, 14336, 4096, 64),
     (12, 130, 898, 20), (8, 200, 576, 4), (8, 300, 1024, 40), (8, 4096, 4096, 160),
     (8, 300, 900, 40), (14, 256, 768, 33), (14, 300, 1024, 40), (14, 4096, 4096, 160),
+    (6, 300, 896, 40), (6, 4864, 896, 160), (6, 300, 1056, 40),
 ]
 
 

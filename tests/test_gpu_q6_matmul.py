@@ -4,8 +4,8 @@ tile with a partial last super-block (odd steps start 2 bytes into a dword),
 exact integer products at the extreme scales and codes, activations over a
 wide dynamic range, the stated bound for an outlier on a zero sub-block
 scale, and the rows that keep the fp32 matrix cores (an odd number of
-super-blocks, or W not 4-byte aligned). Split Q8_0 and packed Q8_0 get the
-same exact-integer check."""
+super-blocks, or W not 4-byte aligned). Split and packed Q8_0 and Q5_0
+get the same exact-integer check."""
 import numpy as np
 import pytest
 
@@ -15,7 +15,7 @@ from helpers import (assert_pad_untouched, assert_within_tolerance, oracle_threa
 
 pytestmark = pytest.mark.gpu
 
-Q6, Q8, SPLIT = 14, 8, 1008
+Q6, Q8, SPLIT, Q50 = 14, 8, 1008, 6
 SB = 210  # bytes of a Q6_K super-block: ql[128], qh[64], scales[16], d
 
 
@@ -66,6 +66,16 @@ def _q6_unit_d_weights(rng, rows, cols):
     return W.reshape(-1)
 
 
+def _q5_0_unit_d_weights(rng, rows, cols):
+    """Q5_0 rows with d = 1 and random qh and nibbles (codes 0 .. 31)."""
+    nb = cols // 32
+    W = rng.integers(0, 256, size=(rows, nb, 22), dtype=np.uint8)
+    W[:, :, 0:2] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+    W[:, 0, 2:6] = 0xFF            # block 0 of every row: all fifth bits set
+    W[:, 0, 6:22] = 0xFF           # ... and every nibble 15: codes 31
+    return W.reshape(-1)
+
+
 def _q8_unit_d_weights(rng, rows, cols):
     nb = cols // 32
     W = rng.integers(0, 256, size=(rows, nb, 34), dtype=np.uint8)
@@ -74,18 +84,20 @@ def _q8_unit_d_weights(rng, rows, cols):
     return W.reshape(-1)
 
 
-@pytest.mark.parametrize("fmt", [Q6, Q8, SPLIT])
+@pytest.mark.parametrize("fmt", [Q6, Q8, SPLIT, Q50])
 @pytest.mark.parametrize("rows,M", [(64, 32), (4096, 512)])
 def test_fp16_route_exact_integer_products(gq, oracle, fmt, rows, M):
     """d = 1, codes and scales over their whole ranges (Q6_K: int8 scales
     down to -128, so sc (q - 32) spans -4096 .. 4096; Q8_0: codes -128 ..
-    127) and activations in {-1, 0, 1}: every product and partial sum is an
-    integer below 2^24, so Y must equal the exact sum bit for bit -- which
-    holds only if the weight operands are exact."""
+    127; Q5_0: codes 0 .. 31) and activations in {-1, 0, 1}: every product
+    and partial sum is an integer below 2^24, so Y must equal the exact sum
+    bit for bit -- which holds only if the weight operands are exact."""
     cols = 512
     rng = synth.rng_for(631, fmt * 100000 + rows)
-    base = Q6 if fmt == Q6 else Q8
-    W = _q6_unit_d_weights(rng, rows, cols) if fmt == Q6 else _q8_unit_d_weights(rng, rows, cols)
+    base = {Q6: Q6, Q8: Q8, SPLIT: Q8, Q50: Q50}[fmt]
+    make = {Q6: _q6_unit_d_weights, Q8: _q8_unit_d_weights, SPLIT: _q8_unit_d_weights,
+            Q50: _q5_0_unit_d_weights}[fmt]
+    W = make(rng, rows, cols)
     X = rng.integers(-1, 2, size=(M, cols)).astype(np.float32)
     Wd = to_dev(W)
     if fmt == SPLIT:
