@@ -120,8 +120,8 @@ struct MmQ8S {
 // w = d * sc_s * (q - 32) over 16-weight sub-blocks s. sc * (q - 32) reaches
 // 13 significant bits, so each k-slice takes two exact operands:
 // 16 sh (q - 32) and sl (q - 32) with sc = 16 sh + sl, 0 <= sl < 16 (at most
-// 4096 with its low 4 bits zero, and 480), four products per slice into one
-// sum; d is applied per super-block. A super-block starts 2 bytes into a
+// 4096 with its low 4 bits zero, and 480), four products per slice into two
+// fp32 sums added per step; d is applied per super-block. A super-block starts 2 bytes into a
 // dword on odd steps (210 = 2 mod 4): the rows must be a multiple of 4 bytes
 // long and W 4-byte aligned, and every piece is loaded from the dword
 // boundary before it and shifted into place.
@@ -818,17 +818,19 @@ __global__ __launch_bounds__(KW * 64) void gemm_f16_kernel(MmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Shared-activation kernel: a workgroup of four waves owns 64 R weight rows
-// (wave w: rows 16 R w .. 16 R w + 16 R - 1) and 16 C activation rows, over
-// every super-block. Each super-block's activation tile is converted once,
-// by all four waves together, into the fp16 operand fragments in LDS, and
-// every wave multiplies it against its own weight rows; so the conversion is
-// paid once per 64 R weight rows instead of once per 16 WR.
+// Shared-activation kernel: a workgroup of RS x KS waves owns 16 RS R weight
+// rows (wave group row w: rows 16 R w .. 16 R w + 16 R - 1) and 16 C
+// activation rows; wave group k (RS waves) takes the 256-column steps k,
+// k + KS, ... Each step's activation tile is converted once, by the group's
+// waves together, into the fp16 operand fragments in LDS, and every wave
+// multiplies it against its own weight rows; so the conversion is paid once
+// per 16 RS R weight rows instead of once per 16 WR. KS > 1 groups add their
+// sums in LDS in group order at the end.
 //
-// Pipeline, per super-block k: the raw activation rows and the weight bytes
-// of super-block k + D are requested (register rings; D super-blocks in
-// flight), super-block k is multiplied (LDS buffer k % 2), super-block k + 1
-// is converted into the other LDS buffer, and one barrier ends the step.
+// Pipeline, per step k: the raw activation rows and the weight bytes of step
+// k + D are requested (register rings; D steps in flight), step k is
+// multiplied (LDS buffer k % 2), step k + 1 is converted into the other LDS
+// buffer, and one barrier ends the step.
 
 // One operand fragment (64 lanes x 16 bytes): lane L's 16 bytes sit at
 // (L / 16) * 272 + (L % 16) * 16. The 16-byte gap after each group of 16
