@@ -1270,14 +1270,17 @@ bool gemm_f16_fits(int64_t rows, int64_t cols, int64_t row_bytes) {
 }
 
 // Tile choice, measured on MI355X (Q4_K 14336 x 4096 gate / 4096 x 14336
-// down): the largest shared-activation tile whose grid still fills about
-// every CU -- 256 x 64 (gate M = 512: 191 us), 256 x 32 (down M = 512:
-// 213 us), 128 x 32 split in two along k (gate M = 64: 38 us), 64 x 16 split
-// in four (gate M = 16: 19 us, down M = 64: 56 us; it also takes grids of
-// 3/4 of the CUs, or a quarter for rows of at most 4 steps) -- else the
+// down). K-quants: the shared-activation tile with the least time, counted
+// as rounds of one workgroup per CU times a relative workgroup time --
+// 256 x 64 (100; gate M = 512: 189 us), 256 x 32 (70; down M = 512: 211 us),
+// 128 x 32 split in two along k (44; gate M = 64: 39 us), 64 x 16 split in
+// four (21; gate M = 16: 20 us, down M = 64: 54 us); the last only for grids
+// of 3/4 of the CUs, or a quarter for rows of at most 4 steps -- else the
 // per-wave kernel with as many weight-row tiles per workgroup as still fill
-// the GPU (down M = 16: 30 us). The other layouts use the tiles their
-// registers allow (below).
+// the GPU (down M = 16: 31 us). Counting rounds matters between the sizes:
+// at M = 160 the gate takes one round of 256 x 64 (94 us) rather than two of
+// 256 x 32 (124 us). The other layouts take the largest tile their registers
+// allow whose grid fills about every CU (below).
 namespace {
 
 template <class Fm, int EPI>
@@ -1301,10 +1304,20 @@ hipError_t launch_gemm_f16_epi(MmArgs& m, const GemmArgs& a, const int64_t* grou
   };
   // per layout, the tiles whose registers fit without spilling
   if constexpr (Fm::kKind == 0) {
-    if (grid(256, 64) >= fill) return run_xs(launch_xs<Fm, 2, 4, 1, 1, 8, EPI>, 64);
-    if (grid(256, 32) >= fill) return run_xs(launch_xs<Fm, 2, 2, 2, 1, 8, EPI>, 32);
-    if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 2, 8, EPI>, 32);
-    if (xs16) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
+    // the tile with the least time: rounds of one workgroup per CU times the
+    // tile's workgroup time (relative, measured on the Llama gate and down)
+    auto cost = [&](int tr, int tm, int64_t w) { return (grid(tr, tm) + cus - 1) / cus * w; };
+    const int64_t c0 = cost(256, 64, 100), c1 = cost(256, 32, 70), c2 = cost(128, 32, 44), c3 = cost(64, 16, 21);
+    const int64_t best = min(min(c0, c1), min(c2, c3));
+    if (c3 == best) {
+      if (xs16) return run_xs(launch_xs<Fm, 1, 1, 1, 4, 4, EPI>, 16);
+    } else if (c2 == best) {
+      return run_xs(launch_xs<Fm, 1, 2, 1, 2, 8, EPI>, 32);
+    } else if (c1 == best) {
+      return run_xs(launch_xs<Fm, 2, 2, 2, 1, 8, EPI>, 32);
+    } else {
+      return run_xs(launch_xs<Fm, 2, 4, 1, 1, 8, EPI>, 64);
+    }
   } else if constexpr (Fm::kKind == 2) {
     // Q8_0 steps carry twice the weight bytes per lane: 16-row tiles per wave
     if (grid(128, 64) >= fill) return run_xs(launch_xs<Fm, 1, 4, 1, 1, 8, EPI>, 64);
