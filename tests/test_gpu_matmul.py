@@ -116,7 +116,8 @@ def test_few_rows_large_products(gq, oracle, fmt, rows, cols, M):
 @pytest.mark.parametrize("fmt", [12, 13])
 @pytest.mark.parametrize("rows,M", [
     (14336, 512),   # 256 x 64 tiles
-    (14336, 160),   # 256 x 32 tiles
+    (14336, 160),   # 256 x 64 tiles, the last m-tile half full
+    (4096, 512),    # 256 x 32 tiles
     (14336, 64),    # 128 x 32 tiles, k split in two
     (14336, 16),    # 64 x 16 tiles, k split in four
     (300, 20),      # one wave per tile
