@@ -228,6 +228,74 @@ def experts_matvec(fmt: int, W, n_expert: int, rows: int, cols: int, X, xk: int,
     return Y, S
 
 
+def moe_bucket(expid, n_expert: int):
+    """The assignments bucketed by expert (the Loom porting skill, "What the
+    starter generates": the MoE generator buckets the rows by expert before
+    the grouped GEMMs; the order inside a bucket is not printed, the reading
+    taken is the assignments' own order). Returns (counts, order, pos):
+    counts[e] = how many ids equal e; pos[a] = the first slot of bucket e
+    (the counts of the experts before e) plus how many earlier assignments
+    have the same id; order[pos[a]] = a. An id outside [0, n_expert) is
+    dropped: pos -1, counted nowhere, and order's unused tail stays -1."""
+    ids = np.asarray(expid, dtype=np.int64).reshape(-1)
+    counts = np.zeros(n_expert, dtype=np.int64)
+    for e in ids:
+        if 0 <= e < n_expert:
+            counts[e] += 1
+    start = np.zeros(n_expert, dtype=np.int64)
+    running = 0
+    for e in range(n_expert):
+        start[e] = running
+        running += counts[e]
+    pos = np.full(ids.size, -1, dtype=np.int32)
+    order = np.full(ids.size, -1, dtype=np.int32)
+    nxt = start.copy()
+    for a, e in enumerate(ids):
+        if 0 <= e < n_expert:
+            pos[a] = nxt[e]
+            order[nxt[e]] = a
+            nxt[e] += 1
+    return counts, order, pos
+
+
+def moe_gather(X, k: int, pos, cols: int) -> np.ndarray:
+    """Each placed assignment's activation row in its bucket slot:
+    Xb[pos[a]] = X[a // k] (a = position * k + slot). Slots no assignment
+    fills are NaN here (the GPU leaves them as they were)."""
+    X = np.ascontiguousarray(X, dtype=np.float32).reshape(-1, cols)
+    pos = np.asarray(pos, dtype=np.int64).reshape(-1)
+    n = pos.size
+    Xb = np.full((n, cols), np.nan, dtype=np.float32)
+    for a in range(n):
+        if 0 <= pos[a] < n:
+            Xb[pos[a]] = X[a // k]
+    return Xb
+
+
+def moe_scatter(out, Yb, pos, w, k: int) -> np.ndarray:
+    """The scatter that ends an MoE layer ("nurllama 0.18.1 API", kernels.nu
+    section: for each position, the weighted sum over its k selected experts'
+    rows is added onto the output). Here the experts' rows sit in bucket
+    order, so slot j of position t reads row pos[t k + j]. In fp32 as the
+    pages' buffers are, summed in slot order starting from 0, every product
+    and sum rounded on its own, then added onto out; a dropped slot (pos
+    outside [0, n)) adds nothing. Returns the new out."""
+    pos = np.asarray(pos, dtype=np.int64).reshape(-1)
+    n = pos.size
+    Yb = np.ascontiguousarray(Yb, dtype=np.float32).reshape(n, -1)
+    w = np.asarray(w, dtype=np.float32).reshape(-1)
+    res = np.array(out, dtype=np.float32).reshape(n // k, -1).copy()
+    for t in range(n // k):
+        acc = np.zeros(res.shape[1], dtype=np.float32)
+        for j in range(k):
+            a = t * k + j
+            if 0 <= pos[a] < n:
+                prod = np.multiply(w[a], Yb[pos[a]], dtype=np.float32)
+                acc = np.add(acc, prod, dtype=np.float32)
+        res[t] = np.add(res[t], acc, dtype=np.float32)
+    return res
+
+
 def q8_0_split_repack(W, rows: int, cols: int) -> np.ndarray:
     """Q8_0 rows repacked into the split per-row layout (scales first, padded
     to 16 bytes, then the codes): the oracle's reading of the q8_0 repack of
