@@ -17,6 +17,9 @@ is no CPU fallback: if the library is not built, loading raises.
     gq_matmul_swiglu(fmt, W, rows, cols, X, Y=None)    -> Y = silu(W_gate X) * (W_up X)
     gq_quantize_q8_1(X, n, cols, out=None)             -> Q8_1 activation blocks
     gq_matvec_q8_1(fmt, W, rows, cols, xq, y=None)     -> y = W x^ (int8 activations)
+    gq_moe_bucket(expid, n_expert)                     -> (counts, order, pos) by expert
+    gq_moe_gather(X, k, pos, Xb=None)                  -> Xb[pos[a]] = X[a // k]
+    gq_moe_scatter(Yb, pos, w, k, out)                 -> out[t] += sum_j w Yb[pos[t k + j]]
 
 W is a uint8 CUDA tensor holding rows * gq_row_bytes(fmt, cols) bytes of
 GGUF blocks; fmt is FMT_Q8_0 (8), FMT_Q4_K (12), FMT_Q5_0 (6), FMT_Q5_K (13)
@@ -51,7 +54,7 @@ GQ_ERR_OVERLAP = 6
 EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matvec_acc",
            "gq_matvec_swiglu", "gq_matvec_experts", "gq_matvec_batch", "gq_q8_0_split_repack",
            "gq_matmul", "gq_matmul_experts", "gq_quantize_q8_1", "gq_matvec_q8_1",
-           "gq_matmul_acc", "gq_matmul_swiglu")
+           "gq_matmul_acc", "gq_matmul_swiglu", "gq_moe_bucket", "gq_moe_gather", "gq_moe_scatter")
 
 _lib = None
 
@@ -94,6 +97,12 @@ def load_library():
     lib.gq_quantize_q8_1.restype = i32
     lib.gq_matvec_q8_1.argtypes = [i32, vp, i64, i64, vp, vp, vp]
     lib.gq_matvec_q8_1.restype = i32
+    lib.gq_moe_bucket.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    lib.gq_moe_bucket.restype = i32
+    lib.gq_moe_gather.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+    lib.gq_moe_gather.restype = i32
+    lib.gq_moe_scatter.argtypes = [vp, i64, vp, vp, i64, i64, vp, vp]
+    lib.gq_moe_scatter.restype = i32
     _lib = lib
     return lib
 
@@ -345,3 +354,74 @@ def gq_matmul_experts(fmt: int, W, n_expert: int, rows: int, cols: int, X, m_per
     if st != GQ_OK:
         raise GQError(st, "gq_matmul_experts")
     return Y
+
+
+def gq_moe_bucket(expid, n_expert: int, counts=None, order=None, pos=None, stream=None):
+    """Stable bucketing of the assignments by expert id (expid: int32 GPU
+    tensor of n_assign ids): returns (counts int64 [n_expert], order int32
+    [n_assign], pos int32 [n_assign]); order is written for the placed
+    assignments only. Asynchronous."""
+    torch = _torch()
+    _check_dev(expid, "expid", torch.int32)
+    n_assign = expid.numel()
+    dev = expid.device
+    if counts is None:
+        counts = torch.empty(max(0, int(n_expert)), dtype=torch.int64, device=dev)
+    if order is None:
+        order = torch.full((n_assign,), -1, dtype=torch.int32, device=dev)
+    if pos is None:
+        pos = torch.empty(n_assign, dtype=torch.int32, device=dev)
+    _check_dev(counts, "counts", torch.int64)
+    _check_dev(order, "order", torch.int32)
+    _check_dev(pos, "pos", torch.int32)
+    if counts.numel() < n_expert or order.numel() < n_assign or pos.numel() < n_assign:
+        raise ValueError("an output is too small")
+    st = load_library().gq_moe_bucket(_ptr(expid), int(n_assign), int(n_expert), _ptr(counts),
+                                      _ptr(order), _ptr(pos), _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_moe_bucket")
+    return counts, order, pos
+
+
+def gq_moe_gather(X, k: int, pos, Xb=None, stream=None):
+    """Xb[pos[a]] = X[a // k] for the placed assignments (X: fp32 [ceil(n_assign
+    / k), cols] GPU tensor, pos from gq_moe_bucket). Asynchronous."""
+    torch = _torch()
+    _check_dev(X, "X", torch.float32)
+    _check_dev(pos, "pos", torch.int32)
+    n_assign = pos.numel()
+    cols = X.shape[-1] if X.dim() > 1 else X.numel()
+    if X.numel() < -(-n_assign // max(1, k)) * cols:
+        raise ValueError("X is too small")
+    if Xb is None:
+        Xb = torch.empty((n_assign, cols), dtype=torch.float32, device=X.device)
+    _check_dev(Xb, "Xb", torch.float32)
+    if Xb.numel() < n_assign * cols:
+        raise ValueError("Xb is too small")
+    st = load_library().gq_moe_gather(_ptr(X), int(cols), int(k), _ptr(pos), int(n_assign), _ptr(Xb),
+                                      _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_moe_gather")
+    return Xb
+
+
+def gq_moe_scatter(Yb, pos, w, k: int, out, stream=None):
+    """out[t] += sum_j w[t k + j] * Yb[pos[t k + j]] over the placed slots, in
+    slot order, each product and sum rounded in fp32 (Yb: [n_assign, rows],
+    w: fp32 [n_assign], out: [n_assign / k, rows]). Asynchronous."""
+    torch = _torch()
+    _check_dev(Yb, "Yb", torch.float32)
+    _check_dev(pos, "pos", torch.int32)
+    _check_dev(w, "w", torch.float32)
+    _check_dev(out, "out", torch.float32)
+    n_assign = pos.numel()
+    rows = Yb.shape[-1] if Yb.dim() > 1 else Yb.numel()
+    if w.numel() < n_assign or Yb.numel() < n_assign * rows:
+        raise ValueError("w or Yb is too small")
+    if k > 0 and out.numel() < (n_assign // k) * rows:
+        raise ValueError("out is too small")
+    st = load_library().gq_moe_scatter(_ptr(Yb), int(rows), _ptr(pos), _ptr(w), int(n_assign), int(k),
+                                       _ptr(out), _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_moe_scatter")
+    return out

@@ -492,3 +492,57 @@ extern "C" int gq_matvec_q8_1(int fmt, const void* W, int64_t rows, int64_t cols
   return finish(gq::launch_gemv_q8a(fmt, (const uint8_t*)W, rb, (int)rows, (int)cols, (const uint8_t*)xq, y, cus,
                                     (hipStream_t)stream));
 }
+
+extern "C" int gq_moe_bucket(const int32_t* expid, int64_t n_assign, int64_t n_expert, int64_t* counts,
+                             int32_t* order, int32_t* pos, void* stream) {
+  if (n_expert < 1 || n_expert > gq::kMaxBucketExperts || n_assign < 0 || n_assign > kMaxDim)
+    return GQ_ERR_SHAPE;
+  if (!counts || (n_assign > 0 && (!expid || !order || !pos))) return GQ_ERR_NULL;
+  if ((uintptr_t)counts % 8 || (uintptr_t)expid % 4 || (uintptr_t)order % 4 || (uintptr_t)pos % 4)
+    return GQ_ERR_ALIGN;
+  const int64_t ib = n_assign * 4, cb = n_expert * 8;
+  if (overlaps(counts, cb, expid, ib) || overlaps(counts, cb, order, ib) || overlaps(counts, cb, pos, ib) ||
+      overlaps(order, ib, expid, ib) || overlaps(pos, ib, expid, ib) || overlaps(order, ib, pos, ib))
+    return GQ_ERR_OVERLAP;
+  if (current_cus() <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  return finish(gq::launch_moe_bucket(expid, (int)n_assign, (int)n_expert, counts, order, pos,
+                                      (hipStream_t)stream));
+}
+
+extern "C" int gq_moe_gather(const float* X, int64_t cols, int64_t k, const int32_t* pos, int64_t n_assign,
+                             float* Xb, void* stream) {
+  if (cols < 1 || cols > kMaxDim || k < 1 || k > kMaxDim || n_assign < 0 || n_assign > kMaxDim)
+    return GQ_ERR_SHAPE;
+  if (n_assign == 0) return GQ_OK;
+  const int64_t xrows = (n_assign + k - 1) / k;
+  if (cols > INT64_MAX / 4 / n_assign) return GQ_ERR_SHAPE;
+  if (!X || !pos || !Xb) return GQ_ERR_NULL;
+  if ((uintptr_t)X % 4 || (uintptr_t)pos % 4 || (uintptr_t)Xb % 4) return GQ_ERR_ALIGN;
+  const int64_t xbb = n_assign * cols * 4;
+  if (overlaps(Xb, xbb, X, xrows * cols * 4) || overlaps(Xb, xbb, pos, n_assign * 4)) return GQ_ERR_OVERLAP;
+  const int cus = current_cus();
+  if (cus <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  return finish(gq::launch_moe_gather(X, (int)cols, (int)k, pos, (int)n_assign, Xb, cus, (hipStream_t)stream));
+}
+
+extern "C" int gq_moe_scatter(const float* Yb, int64_t rows, const int32_t* pos, const float* w,
+                              int64_t n_assign, int64_t k, float* out, void* stream) {
+  if (rows < 0 || rows > kMaxDim || k < 1 || k > kMaxDim || n_assign < 0 || n_assign > kMaxDim ||
+      n_assign % k != 0)
+    return GQ_ERR_SHAPE;
+  if (rows == 0 || n_assign == 0) return GQ_OK;
+  if (rows > INT64_MAX / 4 / n_assign) return GQ_ERR_SHAPE;
+  if (!Yb || !pos || !w || !out) return GQ_ERR_NULL;
+  if ((uintptr_t)Yb % 4 || (uintptr_t)pos % 4 || (uintptr_t)w % 4 || (uintptr_t)out % 4) return GQ_ERR_ALIGN;
+  const int64_t n_tok = n_assign / k, ob = n_tok * rows * 4;
+  if (overlaps(out, ob, Yb, n_assign * rows * 4) || overlaps(out, ob, pos, n_assign * 4) ||
+      overlaps(out, ob, w, n_assign * 4))
+    return GQ_ERR_OVERLAP;
+  const int cus = current_cus();
+  if (cus <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  return finish(gq::launch_moe_scatter(Yb, (int)rows, pos, w, (int)n_tok, (int)k, out, cus,
+                                       (hipStream_t)stream));
+}

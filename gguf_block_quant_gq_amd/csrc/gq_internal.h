@@ -107,4 +107,14 @@ hipError_t launch_gemv_q8a(int fmt, const uint8_t* W, int64_t row_bytes, int row
 // Q6_K, and Q4_K rows whose length is not a multiple of 4.
 hipError_t launch_gemm_f32(int fmt, GemmArgs a, int cus, hipStream_t s, int epi = kMmStore);
 
+// MoE bucketing, gather and scatter (moe.hip); arguments checked by the
+// caller. The bucketing runs in one workgroup with an LDS count per expert.
+constexpr int kMaxBucketExperts = 1024;
+hipError_t launch_moe_bucket(const int32_t* expid, int n_assign, int n_expert, int64_t* counts,
+                             int32_t* order, int32_t* pos, hipStream_t s);
+hipError_t launch_moe_gather(const float* X, int cols, int k, const int32_t* pos, int n_assign, float* Xb,
+                             int cus, hipStream_t s);
+hipError_t launch_moe_scatter(const float* Yb, int rows, const int32_t* pos, const float* wts, int n_tok,
+                              int k, float* out, int cus, hipStream_t s);
+
 }  // namespace gq

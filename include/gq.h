@@ -309,6 +309,56 @@ int gq_matmul_experts(int fmt, const void* W, int64_t n_expert, int64_t rows, in
                       const float* X, const int64_t* m_per_expert, float* Y, void* stream);
 
 /*
+ * The steps around gq_matmul_experts for a mixture-of-experts prefill, all
+ * on the device: bucketing of the assignments by expert (the Loom porting
+ * skill, "What the starter generates": the MoE generator buckets the rows
+ * before the grouped GEMMs), the gather of the activation rows into bucket
+ * order, and the weighted scatter back to the positions ("nurllama 0.18.1
+ * API", kernels.nu section: the assignment table holds an expert id and a
+ * weight per (position, selected expert) pair, and the scatter adds, for each
+ * position, the sum over its k experts of weight times the expert's output
+ * row onto the output). An assignment a = t * k + j is slot j of position t.
+ *
+ * gq_moe_bucket: expid is a device array of n_assign int32 expert ids. A
+ * stable counting sort by expert: counts[e] (device, n_expert int64) = the
+ * assignments with id e; the bucket of expert e starts at o_e = counts[0] +
+ * ... + counts[e-1]; assignment a with id e goes to position pos[a] = o_e +
+ * (the assignments a' < a with id e), and order[pos[a]] = a. An id outside
+ * [0, n_expert) is dropped: pos[a] = -1, counted nowhere (order then has
+ * fewer than n_assign entries written; the rest are left as they were). The
+ * same placement on every call (no atomics). One workgroup (1024 threads,
+ * an LDS count per expert and wave): n_expert at most 1024, n_assign at most
+ * 2^30 (GQ_ERR_SHAPE beyond); sized for the assignments of a prompt chunk,
+ * its time grows with n_assign / 1024. n_assign == 0 writes zero counts.
+ * counts 8-byte aligned, the int32 arrays 4-byte aligned, no two of the four
+ * arrays overlapping. The counts stay on the device: copying them to the
+ * host gives gq_matmul_experts its m_per_expert.
+ *
+ * gq_moe_gather: Xb[pos[a]*cols + c] = X[(a / k)*cols + c] for every a <
+ * n_assign with 0 <= pos[a] < n_assign (other rows of Xb are left as they
+ * were). X: [ceil(n_assign / k), cols] fp32; Xb: [n_assign, cols] fp32, must
+ * not overlap X or pos. A plain copy, bit for bit.
+ *
+ * gq_moe_scatter: for t < n_assign / k (n_assign a multiple of k), r < rows:
+ *   s = 0; for j = 0 .. k-1, a = t*k + j, if 0 <= pos[a] < n_assign:
+ *     s = s + w[a] * Yb[pos[a]*rows + r];
+ *   out[t*rows + r] = out[t*rows + r] + s,
+ * in fp32 with every product and sum rounded on its own (no fused
+ * multiply-add), in slot order j. Yb: [n_assign, rows] (gq_matmul_experts
+ * on the gathered rows); w: n_assign fp32 weights; out: [n_assign / k, rows],
+ * must not overlap Yb, pos or w.
+ *
+ * All three: asynchronous on `stream`; arguments checked on the host
+ * (GQ_ERR_SHAPE / NULL / ALIGN / OVERLAP) before any launch.
+ */
+int gq_moe_bucket(const int32_t* expid, int64_t n_assign, int64_t n_expert, int64_t* counts,
+                  int32_t* order, int32_t* pos, void* stream);
+int gq_moe_gather(const float* X, int64_t cols, int64_t k, const int32_t* pos, int64_t n_assign,
+                  float* Xb, void* stream);
+int gq_moe_scatter(const float* Yb, int64_t rows, const int32_t* pos, const float* w,
+                   int64_t n_assign, int64_t k, float* out, void* stream);
+
+/*
  * The int8-activation decode path (the Loom porting skill, "What the starter
  * generates": decode-shaped linears with activations in llama.cpp's Q8_1
  * numerics and 4-way integer dot products, an fp32-activation switch kept

@@ -261,6 +261,56 @@ def test_validation_experts(lib):
     assert _mx(lib, Y=W_OK + 4 * 4 * 144 - 4) == gq.GQ_ERR_OVERLAP
 
 
+def _bk(lib, expid=0x40000, n_assign=8, n_expert=4, counts=0x50000, order=0x60000, pos=0x70000):
+    return lib.gq_moe_bucket(expid, n_assign, n_expert, counts, order, pos, None)
+
+
+def _ga(lib, X=X_OK, cols=64, k=2, pos=0x70000, n_assign=8, Xb=0x80000):
+    return lib.gq_moe_gather(X, cols, k, pos, n_assign, Xb, None)
+
+
+def _sc(lib, Yb=0x80000, rows=64, pos=0x70000, w=0x60000, n_assign=8, k=2, out=Y_OK):
+    return lib.gq_moe_scatter(Yb, rows, pos, w, n_assign, k, out, None)
+
+
+def test_validation_moe_bucket_gather_scatter(lib):
+    assert _bk(lib, n_expert=0) == gq.GQ_ERR_SHAPE
+    assert _bk(lib, n_expert=1025) == gq.GQ_ERR_SHAPE
+    assert _bk(lib, n_assign=-1) == gq.GQ_ERR_SHAPE
+    assert _bk(lib, n_assign=2 ** 30 + 1) == gq.GQ_ERR_SHAPE
+    assert _bk(lib, counts=None) == gq.GQ_ERR_NULL
+    assert _bk(lib, expid=None) == gq.GQ_ERR_NULL
+    assert _bk(lib, order=None) == gq.GQ_ERR_NULL
+    assert _bk(lib, pos=None) == gq.GQ_ERR_NULL
+    assert _bk(lib, counts=0x50004) == gq.GQ_ERR_ALIGN
+    assert _bk(lib, pos=0x70002) == gq.GQ_ERR_ALIGN
+    assert _bk(lib, order=0x70000 + 16) == gq.GQ_ERR_OVERLAP
+    assert _bk(lib, counts=0x40000 + 8) == gq.GQ_ERR_OVERLAP
+
+    assert _ga(lib, cols=0) == gq.GQ_ERR_SHAPE
+    assert _ga(lib, k=0) == gq.GQ_ERR_SHAPE
+    assert _ga(lib, n_assign=-1) == gq.GQ_ERR_SHAPE
+    assert _ga(lib, cols=2 ** 30 + 1) == gq.GQ_ERR_SHAPE
+    assert _ga(lib, n_assign=0, X=None, pos=None, Xb=None) == gq.GQ_OK
+    assert _ga(lib, X=None) == gq.GQ_ERR_NULL
+    assert _ga(lib, Xb=None) == gq.GQ_ERR_NULL
+    assert _ga(lib, X=X_OK + 2) == gq.GQ_ERR_ALIGN
+    assert _ga(lib, Xb=X_OK + 64) == gq.GQ_ERR_OVERLAP      # Xb over X
+    assert _ga(lib, Xb=0x70000 - 64) == gq.GQ_ERR_OVERLAP   # Xb over pos
+
+    assert _sc(lib, rows=-1) == gq.GQ_ERR_SHAPE
+    assert _sc(lib, k=0) == gq.GQ_ERR_SHAPE
+    assert _sc(lib, n_assign=7) == gq.GQ_ERR_SHAPE           # not a multiple of k
+    assert _sc(lib, rows=2 ** 30 + 1) == gq.GQ_ERR_SHAPE
+    assert _sc(lib, rows=0, Yb=None) == gq.GQ_OK
+    assert _sc(lib, n_assign=0, Yb=None, pos=None, w=None, out=None) == gq.GQ_OK
+    assert _sc(lib, w=None) == gq.GQ_ERR_NULL
+    assert _sc(lib, out=None) == gq.GQ_ERR_NULL
+    assert _sc(lib, w=0x60002) == gq.GQ_ERR_ALIGN
+    assert _sc(lib, out=0x80000 + 4) == gq.GQ_ERR_OVERLAP    # out over Yb
+    assert _sc(lib, out=0x60000 - 16) == gq.GQ_ERR_OVERLAP   # out over w
+
+
 def test_split_layout_row_bytes_and_repack_validation(lib, oracle):
     for cols in (1, 31, 32, 33, 896, 4096, 14336):
         assert gq.gq_row_bytes(1008, cols) == oracle.row_bytes(1008, cols)
