@@ -711,7 +711,58 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
             out["moe_prefill_512x2_of_8_14336x4096_q4_k"] = dict(
                 rows_per_expert=counts, us_per_call=round(ms * 1e3, 1), TFLOPs=round(tf, 2),
                 pct_mfma_f16_peak=round(100 * tf / MFMA_F16_PEAK_TFLOPS, 2))
-            del Xg, Yg
+            # the device-side steps around it: bucketing of the 1024
+            # assignments (ids giving the same split, in shuffled order), the
+            # gather of the 512 activation rows into bucket order, the
+            # weighted scatter of the 1024 expert rows back onto 512 outputs,
+            # and the whole chain with the counts copied to the host
+            n_tok, k = 512, 2
+            idv = rng.permutation(np.repeat(np.arange(n_expert, dtype=np.int32), counts)).astype(np.int32)
+            idd = torch.from_numpy(idv).cuda()
+            cnt = torch.empty(n_expert, dtype=torch.int64, device="cuda")
+            ordr = torch.empty(n_tok * k, dtype=torch.int32, device="cuda")
+            posd = torch.empty(n_tok * k, dtype=torch.int32, device="cuda")
+            Xt = torch.from_numpy(synth.activations((n_tok, c), rng)).cuda()
+            wts = torch.rand(n_tok * k, dtype=torch.float32, device="cuda")
+            outd = torch.zeros((n_tok, r), dtype=torch.float32, device="cuda")
+
+            def bucket():
+                assert lib.gq_moe_bucket(idd.data_ptr(), n_tok * k, n_expert, cnt.data_ptr(), ordr.data_ptr(),
+                                         posd.data_ptr(), stream_ptr()) == 0
+
+            def gather():
+                assert lib.gq_moe_gather(Xt.data_ptr(), c, k, posd.data_ptr(), n_tok * k, Xg.data_ptr(),
+                                         stream_ptr()) == 0
+
+            def scatter():
+                assert lib.gq_moe_scatter(Yg.data_ptr(), r, posd.data_ptr(), wts.data_ptr(), n_tok * k, k,
+                                          outd.data_ptr(), stream_ptr()) == 0
+
+            def chain():
+                bucket()
+                gather()
+                m = cnt.cpu().tolist()
+                ca = (ctypes.c_int64 * n_expert)(*m)
+                assert lib.gq_matmul_experts(f, Wd.data_ptr(), n_expert, r, c, Xg.data_ptr(), ca,
+                                             Yg.data_ptr(), stream_ptr()) == 0
+                scatter()
+
+            bucket()
+            torch.cuda.synchronize()
+            assert cnt.cpu().tolist() == counts
+            ms_b = timer.time(bucket, 20, warmup=2)
+            ms_g = timer.time(gather, 20, warmup=2)
+            ms_s = timer.time(scatter, 20, warmup=2)
+            ms_c = timer.time(chain, 5, warmup=1)
+            gb_g = (n_tok * c * 4 + n_tok * k * c * 4) / 1e9
+            gb_s = (n_tok * k * r * 4 + 2 * n_tok * r * 4) / 1e9
+            out["moe_prefill_device_steps_512x2_of_8"] = dict(
+                bucket_us=round(ms_b * 1e3, 2), gather_us=round(ms_g * 1e3, 2),
+                gather_GBps=round(gb_g / (ms_g * 1e-3), 1), scatter_us=round(ms_s * 1e3, 2),
+                scatter_GBps=round(gb_s / (ms_s * 1e-3), 1),
+                chain_us=round(ms_c * 1e3, 1),
+                chain="bucket + gather + counts to the host + gq_matmul_experts + scatter")
+            del Xg, Yg, Xt, outd
         del Wd
     log(f"moe: { {k: v for k, v in out.items() if k.startswith('moe')} }")
 

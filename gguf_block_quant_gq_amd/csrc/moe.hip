@@ -132,20 +132,28 @@ __global__ __launch_bounds__(256) void moe_gather_kernel(const float* __restrict
 }
 
 // out[t] += sum_j w[t k + j] * Yb[pos[t k + j]], in slot order, every
-// product and sum rounded on its own (no fused multiply-add)
+// product and sum rounded on its own (no fused multiply-add); four columns
+// per thread when the rows allow 16-byte accesses
+template <bool kVec4>
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const float* __restrict__ Yb, int rows,
                                                           const int32_t* __restrict__ pos,
                                                           const float* __restrict__ wts, int n_tok, int k,
                                                           int n_assign, float* __restrict__ out) {
 #pragma clang fp contract(off)  // a product and the sum it enters round separately
+  constexpr int V = kVec4 ? 4 : 1;
+  typedef float vec __attribute__((ext_vector_type(V)));
+  const int nv = rows / V;
   for (int t = blockIdx.x; t < n_tok; t += gridDim.x) {
-    float* o = out + (int64_t)t * rows;
-    for (int r = threadIdx.x; r < rows; r += blockDim.x) {
-      float s = 0.f;
+    vec* o = reinterpret_cast<vec*>(out + (int64_t)t * rows);
+    for (int r = threadIdx.x; r < nv; r += blockDim.x) {
+      vec s = {};
       for (int j = 0; j < k; ++j) {
         const int a = t * k + j;
         const int p = pos[a];
-        if (p >= 0 && p < n_assign) s = s + wts[a] * Yb[(int64_t)p * rows + r];
+        if (p >= 0 && p < n_assign) {
+          const vec y = reinterpret_cast<const vec*>(Yb + (int64_t)p * rows)[r];
+          s = s + wts[a] * y;
+        }
       }
       o[r] = o[r] + s;
     }
@@ -172,8 +180,13 @@ hipError_t launch_moe_gather(const float* X, int cols, int k, const int32_t* pos
 hipError_t launch_moe_scatter(const float* Yb, int rows, const int32_t* pos, const float* wts, int n_tok,
                               int k, float* out, int cus, hipStream_t s) {
   const int blocks = (int)std::min<int64_t>(n_tok, (int64_t)cus * 8);
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3(blocks), dim3(256), 0, s, Yb, rows, pos, wts, n_tok, k,
-                     n_tok * k, out);
+  const bool vec4 = rows % 4 == 0 && (uintptr_t)Yb % 16 == 0 && (uintptr_t)out % 16 == 0;
+  if (vec4)
+    hipLaunchKernelGGL(moe_scatter_kernel<true>, dim3(blocks), dim3(256), 0, s, Yb, rows, pos, wts, n_tok, k,
+                       n_tok * k, out);
+  else
+    hipLaunchKernelGGL(moe_scatter_kernel<false>, dim3(blocks), dim3(256), 0, s, Yb, rows, pos, wts, n_tok, k,
+                       n_tok * k, out);
   return hipGetLastError();
 }
 
