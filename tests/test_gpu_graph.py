@@ -200,3 +200,56 @@ def test_graph_replays_of_products(gq, oracle):
     fmt, r, c, m = MATMULS[0]
     ref, S = oracle.matmul(fmt, to_host(Ws[0]), r, c, to_host(Xs[0]), nthreads=oracle_threads())
     assert_within_tolerance(got[0], ref, S, "graph product")
+
+
+def test_graph_moe_steps(gq, oracle):
+    """The MoE bucketing, gather and scatter captured in one graph, replayed
+    with new expert ids, activations, expert rows and outputs written eagerly
+    between replays: every replay bit-equal to the oracle."""
+    import torch
+    n_tok, k, n_expert, cols, rows = 200, 2, 8, 96, 64
+    n = n_tok * k
+    ids = torch.zeros(n, dtype=torch.int32, device="cuda")
+    X = torch.zeros((n_tok, cols), dtype=torch.float32, device="cuda")
+    Yb = torch.zeros((n, rows), dtype=torch.float32, device="cuda")
+    w = torch.zeros(n, dtype=torch.float32, device="cuda")
+    out = torch.zeros((n_tok, rows), dtype=torch.float32, device="cuda")
+    counts = torch.empty(n_expert, dtype=torch.int64, device="cuda")
+    order = torch.empty(n, dtype=torch.int32, device="cuda")
+    pos = torch.empty(n, dtype=torch.int32, device="cuda")
+    Xb = torch.empty((n, cols), dtype=torch.float32, device="cuda")
+
+    def step():
+        gq.gq_moe_bucket(ids, n_expert, counts, order, pos)
+        gq.gq_moe_gather(X, k, pos, Xb)
+        gq.gq_moe_scatter(Yb, pos, w, k, out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+
+    for rep in range(3):
+        rng = synth.rng_for(805, rep)
+        hid = rng.integers(0, n_expert, size=n).astype(np.int32)
+        hX = synth.activations((n_tok, cols), rng)
+        hY = synth.activations((n, rows), rng)
+        hw = rng.random(n).astype(np.float32)
+        ho = synth.activations((n_tok, rows), rng)
+        for t, h in ((ids, hid), (X, hX), (Yb, hY), (w, hw), (out, ho)):
+            t.copy_(torch.from_numpy(h))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] moe replay {rep}", flush=True)
+        wc, wo, wp = oracle.moe_bucket(hid, n_expert)
+        assert np.array_equal(to_host(counts), wc) and np.array_equal(to_host(pos), wp)
+        assert np.array_equal(to_host(order), wo)
+        assert np.array_equal(to_host(Xb).view(np.uint32), oracle.moe_gather(hX, k, wp, cols).view(np.uint32))
+        want = oracle.moe_scatter(ho, hY, wp, hw, k)
+        assert np.array_equal(to_host(out).view(np.uint32), want.view(np.uint32))
