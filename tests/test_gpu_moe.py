@@ -25,6 +25,7 @@ def _ids(rng, n, n_expert, invalid=0.0):
 @pytest.mark.parametrize("n,n_expert,invalid", [
     (1, 1, 0.0), (8, 4, 0.0), (1000, 8, 0.05), (1024, 8, 0.0), (1025, 8, 0.0),
     (32768, 128, 0.01), (5000, 1024, 0.02), (3000, 3, 0.5), (64, 16, 1.0),
+    (1 << 20, 64, 0.01),   # 1024 tiles of the one-workgroup walk
 ])
 def test_bucket_matches_oracle(gq, oracle, n, n_expert, invalid):
     import torch
