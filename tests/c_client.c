@@ -11,7 +11,8 @@
  *
  * It runs gq_row_bytes, gq_matvec (default stream and a created stream),
  * gq_matmul with M = 2 and M = 20 (few-row and matrix-core routes),
- * gq_dequant, and a few calls the host checks reject. Prints "c client ok"
+ * gq_dequant, gq_moe_bucket and gq_moe_scatter on a hand-worked case, and a
+ * few calls the host checks reject. Prints "c client ok"
  * and exits 0 on success; any mismatch prints the case and exits 1.
  *
  * Built by __graft_entry__.build() (gcc, linked against libgq.so and
@@ -146,6 +147,61 @@ int main(void) {
             failures++;
             break;
         }
+    }
+
+    /* gq_moe_bucket / gq_moe_scatter on 4 positions x 2 slots, 4 experts:
+     * ids 2 0 | 2 1 | 0 0 | 3 2 give counts 3 1 3 1 and positions
+     * 4 0 5 3 1 2 7 6 (a stable sort by id); the scatter then adds to each
+     * position w0 * row(pos[2t]) + w1 * row(pos[2t + 1]), exact in small
+     * integers */
+    {
+        const int32_t ids[8] = {2, 0, 2, 1, 0, 0, 3, 2};
+        const int32_t want_pos[8] = {4, 0, 5, 3, 1, 2, 7, 6};
+        const int64_t want_counts[4] = {3, 1, 3, 1};
+        const int R = 3;
+        float yb[8 * 3], w[8], out[4 * 3];
+        for (int p = 0; p < 8; p++)
+            for (int r = 0; r < R; r++) yb[p * R + r] = (float)(10 * p + r);
+        for (int a = 0; a < 8; a++) w[a] = (float)(a % 3 + 1);
+        for (int i = 0; i < 4 * R; i++) out[i] = 1.0f;
+        void *dids = NULL, *dcnt = NULL, *dord = NULL, *dpos = NULL, *dyb = NULL, *dw = NULL, *dout = NULL;
+        if (!hip_ok(hipMalloc(&dids, sizeof(ids)), "hipMalloc ids") ||
+            !hip_ok(hipMalloc(&dcnt, sizeof(want_counts)), "hipMalloc counts") ||
+            !hip_ok(hipMalloc(&dord, sizeof(ids)), "hipMalloc order") ||
+            !hip_ok(hipMalloc(&dpos, sizeof(ids)), "hipMalloc pos") ||
+            !hip_ok(hipMalloc(&dyb, sizeof(yb)), "hipMalloc yb") ||
+            !hip_ok(hipMalloc(&dw, sizeof(w)), "hipMalloc w") ||
+            !hip_ok(hipMalloc(&dout, sizeof(out)), "hipMalloc out"))
+            return 2;
+        if (!hip_ok(hipMemcpy(dids, ids, sizeof(ids), hipMemcpyHostToDevice), "copy ids") ||
+            !hip_ok(hipMemcpy(dyb, yb, sizeof(yb), hipMemcpyHostToDevice), "copy yb") ||
+            !hip_ok(hipMemcpy(dw, w, sizeof(w), hipMemcpyHostToDevice), "copy w") ||
+            !hip_ok(hipMemcpy(dout, out, sizeof(out), hipMemcpyHostToDevice), "copy out"))
+            return 2;
+        check(gq_moe_bucket((const int32_t*)dids, 8, 4, (int64_t*)dcnt, (int32_t*)dord, (int32_t*)dpos,
+                            (void*)s) == GQ_OK, "gq_moe_bucket status");
+        check(gq_moe_scatter((const float*)dyb, R, (const int32_t*)dpos, (const float*)dw, 8, 2,
+                             (float*)dout, (void*)s) == GQ_OK, "gq_moe_scatter status");
+        if (!hip_ok(hipStreamSynchronize(s), "sync moe")) return 2;
+        int32_t pos[8];
+        int64_t counts[4];
+        float got[4 * 3];
+        if (!hip_ok(hipMemcpy(pos, dpos, sizeof(pos), hipMemcpyDeviceToHost), "copy pos") ||
+            !hip_ok(hipMemcpy(counts, dcnt, sizeof(counts), hipMemcpyDeviceToHost), "copy counts") ||
+            !hip_ok(hipMemcpy(got, dout, sizeof(got), hipMemcpyDeviceToHost), "copy out"))
+            return 2;
+        check(memcmp(pos, want_pos, sizeof(pos)) == 0, "gq_moe_bucket positions");
+        check(memcmp(counts, want_counts, sizeof(counts)) == 0, "gq_moe_bucket counts");
+        for (int t = 0; t < 4; t++)
+            for (int r = 0; r < R; r++) {
+                float want = 1.0f;
+                for (int j = 0; j < 2; j++) want += w[2 * t + j] * yb[want_pos[2 * t + j] * R + r];
+                if (got[t * R + r] != want) {
+                    fprintf(stderr, "c client: scatter position %d col %d: %g != %g\n", t, r, got[t * R + r], want);
+                    failures++;
+                }
+            }
+        hipFree(dids); hipFree(dcnt); hipFree(dord); hipFree(dpos); hipFree(dyb); hipFree(dw); hipFree(dout);
     }
 
     /* calls the host checks reject (nothing is launched) */
