@@ -20,6 +20,8 @@ is no CPU fallback: if the library is not built, loading raises.
     gq_moe_bucket(expid, n_expert)                     -> (counts, order, pos) by expert
     gq_moe_gather(X, k, pos, Xb=None)                  -> Xb[pos[a]] = X[a // k]
     gq_moe_scatter(Yb, pos, w, k, out)                 -> out[t] += sum_j w Yb[pos[t k + j]]
+    gq_matmul_experts_dev(fmt, W, n_expert, rows, cols, X, counts, Y=None)
+                                                       -> gq_matmul_experts, counts on the device
 
 W is a uint8 CUDA tensor holding rows * gq_row_bytes(fmt, cols) bytes of
 GGUF blocks; fmt is FMT_Q8_0 (8), FMT_Q4_K (12), FMT_Q5_0 (6), FMT_Q5_K (13)
@@ -54,7 +56,8 @@ GQ_ERR_OVERLAP = 6
 EXPORTS = ("gq_row_bytes", "gq_status_str", "gq_dequant", "gq_matvec", "gq_matvec_acc",
            "gq_matvec_swiglu", "gq_matvec_experts", "gq_matvec_batch", "gq_q8_0_split_repack",
            "gq_matmul", "gq_matmul_experts", "gq_quantize_q8_1", "gq_matvec_q8_1",
-           "gq_matmul_acc", "gq_matmul_swiglu", "gq_moe_bucket", "gq_moe_gather", "gq_moe_scatter")
+           "gq_matmul_acc", "gq_matmul_swiglu", "gq_moe_bucket", "gq_moe_gather", "gq_moe_scatter",
+           "gq_matmul_experts_dev")
 
 _lib = None
 
@@ -103,6 +106,8 @@ def load_library():
     lib.gq_moe_gather.restype = i32
     lib.gq_moe_scatter.argtypes = [vp, i64, vp, vp, i64, i64, vp, vp]
     lib.gq_moe_scatter.restype = i32
+    lib.gq_matmul_experts_dev.argtypes = [i32, vp, i64, i64, i64, vp, vp, i64, vp, vp]
+    lib.gq_matmul_experts_dev.restype = i32
     _lib = lib
     return lib
 
@@ -425,3 +430,27 @@ def gq_moe_scatter(Yb, pos, w, k: int, out, stream=None):
     if st != GQ_OK:
         raise GQError(st, "gq_moe_scatter")
     return out
+
+
+def gq_matmul_experts_dev(fmt: int, W, n_expert: int, rows: int, cols: int, X, counts, Y=None,
+                          stream=None):
+    """gq_matmul_experts with the per-expert row counts in an int64 GPU
+    tensor (gq_moe_bucket's counts): X [total, cols] bucketed by expert, Y
+    [total, rows]; no host synchronisation. Asynchronous."""
+    torch = _torch()
+    _check_w(fmt, W, n_expert * rows, cols)
+    _check_dev(X, "X", torch.float32)
+    _check_dev(counts, "counts", torch.int64)
+    if counts.numel() < n_expert:
+        raise ValueError("counts must hold n_expert values")
+    total = X.numel() // cols
+    if Y is None:
+        Y = torch.empty((total, rows), dtype=torch.float32, device=W.device)
+    _check_dev(Y, "Y", torch.float32)
+    if Y.numel() < total * rows:
+        raise ValueError("Y is too small")
+    st = load_library().gq_matmul_experts_dev(int(fmt), _ptr(W), int(n_expert), int(rows), int(cols), _ptr(X),
+                                              _ptr(counts), int(total), _ptr(Y), _stream_handle(stream))
+    if st != GQ_OK:
+        raise GQError(st, "gq_matmul_experts_dev")
+    return Y

@@ -298,7 +298,42 @@ struct MmArgs {
   int code_off;  // split Q8_0: bytes of a row's scale region
   int n_groups;
   MmTile g[kMaxGroups];
+  // groups whose row counts live on the device (gq_matmul_experts_dev):
+  // n_groups counts at dev_m, expert e's weights at W + e * dev_w_bytes, and
+  // dev_total activation rows in X and Y; null for the table g above
+  const int64_t* dev_m;
+  int64_t dev_w_bytes;
+  int dev_total;
 };
+
+// This workgroup's group: the table entry whose m-tiles hold blockIdx.y, or,
+// with device counts, the group found by walking the counts (each clamped to
+// the rows left of dev_total, so that no group reaches past X or Y). False
+// when blockIdx.y lies past the last m-tile (the grid is sized for the most
+// m-tiles the total can need).
+__device__ __forceinline__ bool find_group(const MmArgs& a, int tm, MmTile& grp) {
+  const int y = (int)blockIdx.y;
+  if (a.dev_m == nullptr) {
+    int gidx = 0;
+    for (int g = 1; g < a.n_groups; ++g)
+      if (y >= a.g[g].mtile0) gidx = g;
+    grp = a.g[gidx];
+    return true;
+  }
+  int tiles = 0, rows = 0;
+  for (int e = 0; e < a.n_groups; ++e) {
+    const int64_t c = a.dev_m[e];
+    const int m = c < 0 ? 0 : (int)min(c, (int64_t)(a.dev_total - rows));
+    const int t = (m + tm - 1) / tm;
+    if (y < tiles + t) {
+      grp = MmTile{a.dev_w_bytes * e, rows, m, tiles};
+      return true;
+    }
+    tiles += t;
+    rows += m;
+  }
+  return false;
+}
 
 // The weight bytes lane (i, q) needs for one 256-column step of R row tiles
 // (row i of each): K-quants -- the super-block header and the lane's 8 code
@@ -590,10 +625,8 @@ __global__ __launch_bounds__(KW * 64) void gemm_f16_kernel(MmArgs a) {
   const uint32_t sel6 = (uint32_t)(q >> 1) * 0x01010101u + 0x06040200u;
 
   // the group of this m-tile (groups are few; a linear scan on scalars)
-  int gidx = 0;
-  for (int g = 1; g < a.n_groups; ++g)
-    if ((int)blockIdx.y >= a.g[g].mtile0) gidx = g;
-  const MmTile grp = a.g[gidx];
+  MmTile grp;
+  if (!find_group(a, 16, grp)) return;
   const int m0 = grp.m_begin + ((int)blockIdx.y - grp.mtile0) * 16;  // first activation row
   const int m_end = grp.m_begin + grp.m_count;
   const int r0 = blockIdx.x * 16 * WR;
@@ -885,10 +918,8 @@ __global__ __launch_bounds__(64 * RS * KS) void gemm_f16_xs_kernel(MmArgs a) {
   const int i = lane & 15, q = lane >> 4;
   const uint32_t sel6 = (uint32_t)(q >> 1) * 0x01010101u + 0x06040200u;  // Q6_K: q6_head
 
-  int gidx = 0;
-  for (int g = 1; g < a.n_groups; ++g)
-    if ((int)blockIdx.y >= a.g[g].mtile0) gidx = g;
-  const MmTile grp = a.g[gidx];
+  MmTile grp;
+  if (!find_group(a, 16 * C, grp)) return;
   const int m0 = grp.m_begin + ((int)blockIdx.y - grp.mtile0) * 16 * C;
   const int m_end = grp.m_begin + grp.m_count;
   const int r0 = blockIdx.x * 16 * RS * R;
@@ -1296,8 +1327,14 @@ hipError_t launch_gemm_f16_epi(MmArgs& m, const GemmArgs& a, const int64_t* grou
     return g >= (int64_t)cus * 3 / 4 || (m.nsb <= 4 && g >= cus / 4);
   }();
   auto grid = [&](int tr, int tm) { return ((a.rows + tr - 1) / tr) * count_mtiles(group_m, n_groups, tm); };
+  // the grid's y: the m-tiles of the host table, or with device counts the
+  // most the total can need (each non-empty group wastes under one m-tile)
+  auto grid_y = [&](int tm) {
+    if (m.dev_m) return (int)((m.dev_total + tm - 1) / tm + m.n_groups);
+    return build_groups(m, group_m, group_off, n_groups, group_w_bytes, tm);
+  };
   auto run_xs = [&](auto launch, int tm) {
-    const int gy = build_groups(m, group_m, group_off, n_groups, group_w_bytes, tm);
+    const int gy = grid_y(tm);
     if (gy < 0) return hipErrorInvalidValue;
     if (gy == 0) return hipSuccess;
     return launch(m, gy, s);
@@ -1332,7 +1369,7 @@ hipError_t launch_gemm_f16_epi(MmArgs& m, const GemmArgs& a, const int64_t* grou
     if (grid(128, 32) >= fill) return run_xs(launch_xs<Fm, 1, 2, 1, 1, 8, EPI>, 32);
     if (xs16) return run_xs(launch_xs<Fm, 1, 1, 1, 2, 4, EPI>, 16);
   }
-  const int gy = build_groups(m, group_m, group_off, n_groups, group_w_bytes, 16);
+  const int gy = grid_y(16);
   if (gy < 0) return hipErrorInvalidValue;
   if (gy == 0) return hipSuccess;
   if (grid(32, 16) >= fill) return launch<Fm, 2, EPI>(m, (a.rows + 31) / 32, gy, s);
@@ -1375,6 +1412,35 @@ hipError_t launch_gemm_f16(int fmt, const GemmArgs& a, const int64_t* group_m, c
       return launch_gemm_fmt<MmQ8S>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
     case kFmtQ6_K: return launch_gemm_fmt<MmQ6K>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
     case kFmtQ5_0: return launch_gemm_fmt<MmQ50>(m, a, group_m, group_off, n_groups, group_w_bytes, cus, s, epi);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_f16_dev(int fmt, const GemmArgs& a, const int64_t* dev_m, int n_expert, int total,
+                               int64_t group_w_bytes, int cus, hipStream_t s) {
+  MmArgs m{};
+  m.W = a.W;
+  m.X = a.X;
+  m.Y = a.Y;
+  m.row_bytes = a.row_bytes;
+  m.rows = a.rows;
+  m.cols = a.cols;
+  m.nsb = (a.cols + 255) / 256;
+  m.nb = (a.cols + 31) / 32;
+  m.code_off = split_scale_bytes(m.nb);
+  m.n_groups = n_expert;
+  m.dev_m = dev_m;
+  m.dev_w_bytes = group_w_bytes;
+  m.dev_total = total;
+  // the tile is chosen as for one group of all the rows
+  const int64_t tm = total, off = 0;
+  switch (fmt) {
+    case kFmtQ4_K: return launch_gemm_fmt<MmQ4K>(m, a, &tm, &off, 1, group_w_bytes, cus, s, kMmStore);
+    case kFmtQ5_K: return launch_gemm_fmt<MmQ5K>(m, a, &tm, &off, 1, group_w_bytes, cus, s, kMmStore);
+    case kFmtQ8_0: return launch_gemm_fmt<MmQ8P>(m, a, &tm, &off, 1, group_w_bytes, cus, s, kMmStore);
+    case kFmtQ8_0Split: return launch_gemm_fmt<MmQ8S>(m, a, &tm, &off, 1, group_w_bytes, cus, s, kMmStore);
+    case kFmtQ6_K: return launch_gemm_fmt<MmQ6K>(m, a, &tm, &off, 1, group_w_bytes, cus, s, kMmStore);
+    case kFmtQ5_0: return launch_gemm_fmt<MmQ50>(m, a, &tm, &off, 1, group_w_bytes, cus, s, kMmStore);
     default: return hipErrorInvalidValue;
   }
 }

@@ -546,3 +546,32 @@ extern "C" int gq_moe_scatter(const float* Yb, int64_t rows, const int32_t* pos,
   return finish(gq::launch_moe_scatter(Yb, (int)rows, pos, w, (int)n_tok, (int)k, out, cus,
                                        (hipStream_t)stream));
 }
+
+extern "C" int gq_matmul_experts_dev(int fmt, const void* W, int64_t n_expert, int64_t rows, int64_t cols,
+                                     const float* X, const int64_t* m_dev, int64_t total, float* Y,
+                                     void* stream) {
+  int64_t rb = 0, ebytes = 0;
+  int st = check_shape(fmt, rows, cols, 1, &rb, &ebytes);
+  if (st != GQ_OK) return st;
+  if (n_expert < 1 || n_expert > gq::kMaxBucketExperts || total < 0 || total > kMaxDim) return GQ_ERR_SHAPE;
+  // the fp16 matrix-core layouts only (rows of whole dwords where the format needs it)
+  const bool dword_format = fmt == GQ_FMT_Q8_0 || fmt == GQ_FMT_Q5_0 || fmt == GQ_FMT_Q6_K;
+  if (cols % 4 != 0 || (dword_format && rb % 4 != 0)) return GQ_ERR_SHAPE;
+  if (rows == 0 || total == 0) return GQ_OK;
+  if (ebytes > INT64_MAX / n_expert) return GQ_ERR_SHAPE;
+  if (rows > INT64_MAX / 4 / total || cols > INT64_MAX / 4 / total) return GQ_ERR_SHAPE;
+  if (!gq::gemm_f16_fits(rows, cols, rb)) return GQ_ERR_SHAPE;
+  const int64_t wbytes = ebytes * n_expert, xbytes = total * cols * 4, ybytes = total * rows * 4;
+  if (!W || !X || !Y || !m_dev) return GQ_ERR_NULL;
+  if ((st = check_align(fmt, W)) != GQ_OK) return st;
+  if ((dword_format && (uintptr_t)W % 4) || (uintptr_t)X % 4 || (uintptr_t)Y % 4 || (uintptr_t)m_dev % 8)
+    return GQ_ERR_ALIGN;
+  if (overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, X, xbytes) || overlaps(Y, ybytes, m_dev, n_expert * 8))
+    return GQ_ERR_OVERLAP;
+  const int cus = current_cus();
+  if (cus <= 0) return GQ_ERR_DEVICE;
+  (void)hipGetLastError();
+  gq::GemmArgs a{(const uint8_t*)W, X, Y, rb, (int)rows, (int)cols, 0, 0};
+  return finish(gq::launch_gemm_f16_dev(fmt, a, m_dev, (int)n_expert, (int)total, ebytes, cus,
+                                        (hipStream_t)stream));
+}

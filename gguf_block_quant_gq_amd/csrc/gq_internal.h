@@ -97,6 +97,10 @@ hipError_t launch_gemm_small(int fmt, GemmArgs a, int cus, hipStream_t s);
 bool gemm_f16_fits(int64_t rows, int64_t cols, int64_t row_bytes);
 hipError_t launch_gemm_f16(int fmt, const GemmArgs& a, const int64_t* group_m, const int64_t* group_off,
                            int n_groups, int64_t group_w_bytes, int cus, hipStream_t s, int epi = kMmStore);
+// The grouped product with the per-group row counts on the device (n_expert
+// int64 counts at dev_m, total rows of X and Y); the fp16 layouts only.
+hipError_t launch_gemm_f16_dev(int fmt, const GemmArgs& a, const int64_t* dev_m, int n_expert, int total,
+                               int64_t group_w_bytes, int cus, hipStream_t s);
 // The int8-activation path (gemv_q8a.hip): Q8_1 quantisation of n rows of
 // activations, and y = W x^ for Q8_0 / Q4_K weights with integer dots.
 hipError_t launch_quantize_q8_1(const float* x, int64_t n, int cols, uint8_t* out, hipStream_t s);

@@ -359,6 +359,29 @@ int gq_moe_scatter(const float* Yb, int64_t rows, const int32_t* pos, const floa
                    int64_t n_assign, int64_t k, float* out, void* stream);
 
 /*
+ * gq_matmul_experts with the row counts on the device, so that a whole MoE
+ * prefill (gq_moe_bucket, gq_moe_gather, this product, gq_moe_scatter) runs
+ * without a host synchronisation and can be captured in a HIP graph. m_dev:
+ * n_expert int64 counts in device memory (8-byte aligned), such as
+ * gq_moe_bucket's; X: [total, cols] and Y: [total, rows] fp32 with expert
+ * 0's rows first, then expert 1's, ... as in gq_matmul_experts. The counts
+ * are read by the kernels: a negative count counts as 0, and the groups are
+ * cut at `total` rows (a count past what is left is clamped), so no group
+ * reads or writes past X or Y; rows of Y past the sum of the counts are left
+ * as they were. The layouts of the fp16 matrix cores only: cols a multiple
+ * of 4, and for Q8_0, Q5_0 and Q6_K rows of whole dwords and a 4-byte
+ * aligned W (GQ_ERR_SHAPE / GQ_ERR_ALIGN otherwise). One launch; its grid is
+ * sized for the most m-tiles `total` rows can need, the tile is chosen as
+ * for one group of `total` rows, and each workgroup finds its group by
+ * walking the counts (linear in n_expert, at most 1024). The results obey
+ * gq_matmul's accuracy bound per expert; a group's bits may differ from
+ * gq_matmul_experts of the same rows, whose tile follows the counts.
+ * Asynchronous on `stream`.
+ */
+int gq_matmul_experts_dev(int fmt, const void* W, int64_t n_expert, int64_t rows, int64_t cols,
+                          const float* X, const int64_t* m_dev, int64_t total, float* Y, void* stream);
+
+/*
  * The int8-activation decode path (the Loom porting skill, "What the starter
  * generates": decode-shaped linears with activations in llama.cpp's Q8_1
  * numerics and 4-way integer dot products, an fp32-activation switch kept

@@ -311,6 +311,29 @@ def test_validation_moe_bucket_gather_scatter(lib):
     assert _sc(lib, out=0x60000 - 16) == gq.GQ_ERR_OVERLAP   # out over w
 
 
+def _gd(lib, fmt=12, W=W_OK, n_expert=4, rows=4, cols=256, X=X_OK, m=0x90000, total=8, Y=Y_OK):
+    return lib.gq_matmul_experts_dev(fmt, W, n_expert, rows, cols, X, m, total, Y, None)
+
+
+def test_validation_grouped_device_counts(lib):
+    assert _gd(lib, fmt=7) == gq.GQ_ERR_FMT
+    assert _gd(lib, n_expert=0) == gq.GQ_ERR_SHAPE
+    assert _gd(lib, n_expert=1025) == gq.GQ_ERR_SHAPE
+    assert _gd(lib, total=-1) == gq.GQ_ERR_SHAPE
+    assert _gd(lib, total=2 ** 30 + 1) == gq.GQ_ERR_SHAPE
+    assert _gd(lib, cols=258) == gq.GQ_ERR_SHAPE            # not a multiple of 4
+    assert _gd(lib, fmt=8, cols=96) == gq.GQ_ERR_SHAPE      # Q8_0 rows of 3 blocks: not whole dwords
+    assert _gd(lib, fmt=14, cols=768) == gq.GQ_ERR_SHAPE    # Q6_K rows of 3 super-blocks
+    assert _gd(lib, total=0, W=None, X=None, m=None, Y=None) == gq.GQ_OK
+    assert _gd(lib, rows=0, W=None) == gq.GQ_OK
+    assert _gd(lib, m=None) == gq.GQ_ERR_NULL
+    assert _gd(lib, W=None) == gq.GQ_ERR_NULL
+    assert _gd(lib, m=0x90004) == gq.GQ_ERR_ALIGN
+    assert _gd(lib, fmt=8, cols=128, W=W_OK + 2) == gq.GQ_ERR_ALIGN   # dword rows need a 4-byte W
+    assert _gd(lib, Y=X_OK + 64) == gq.GQ_ERR_OVERLAP
+    assert _gd(lib, m=Y_OK + 8) == gq.GQ_ERR_OVERLAP
+
+
 def test_split_layout_row_bytes_and_repack_validation(lib, oracle):
     for cols in (1, 31, 32, 33, 896, 4096, 14336):
         assert gq.gq_row_bytes(1008, cols) == oracle.row_bytes(1008, cols)

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import oracle_threads, to_dev, to_host
+from helpers import assert_within_tolerance, oracle_threads, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +127,117 @@ def test_prefill_chain_against_expert_matvecs(gq, oracle, fmt):
         mag[a // k] += float(w[a]) * np.abs(Ye[a])
     bound += (2 * k + 2) * 2.0 ** -24 * mag
     assert (np.abs(got - ref) <= bound).all()
+
+
+@pytest.mark.parametrize("fmt", [12, 13, 8, 1008, 14, 6])
+def test_grouped_product_with_device_counts(gq, oracle, fmt):
+    """gq_matmul_experts_dev against the oracle per expert (counts skewed,
+    one expert empty), Y rows past the counts left alone, and the same bits
+    on a second call."""
+    import torch
+    n_expert, rows, cols = 6, 320, 512
+    counts = [150, 0, 70, 33, 1, 90]
+    total = sum(counts) + 17   # rows past the counts stay untouched
+    rng = synth.rng_for(914, fmt)
+    base = 8 if fmt == 1008 else fmt
+    W = np.concatenate([synth.weights(base, rows, cols, rng) for _ in range(n_expert)])
+    X = synth.activations((total, cols), rng)
+    Wd = to_dev(W)
+    if fmt == 1008:
+        Wd = gq.gq_q8_0_split_repack(Wd, n_expert * rows, cols)
+    cd = to_dev(np.array(counts, np.int64))
+    Y = torch.full((total, rows), float("nan"), dtype=torch.float32, device="cuda")
+    print(f"[moe] grouped product, device counts fmt={fmt}", flush=True)
+    gq.gq_matmul_experts_dev(fmt, Wd, n_expert, rows, cols, to_dev(X), cd, Y=Y)
+    got = to_host(Y).copy()
+    eb = rows * gq.gq_row_bytes(base, cols)
+    m0 = 0
+    for e, m in enumerate(counts):
+        if m:
+            ref, S = oracle.matmul(base, W[e * eb:(e + 1) * eb], rows, cols, X[m0:m0 + m],
+                                   nthreads=oracle_threads())
+            assert_within_tolerance(got[m0:m0 + m], ref, S, f"expert {e} fmt={fmt}")
+        m0 += m
+    assert np.isnan(got[m0:]).all()
+    gq.gq_matmul_experts_dev(fmt, Wd, n_expert, rows, cols, to_dev(X), cd, Y=Y)
+    assert np.array_equal(to_host(Y).view(np.uint32), got.view(np.uint32))
+
+
+def test_grouped_product_device_counts_clamped(gq, oracle):
+    """Counts that add up past the rows given (and a negative one): the
+    groups are cut at the total, every row computed is its expert's product."""
+    import torch
+    n_expert, rows, cols, total = 4, 64, 256, 100
+    counts = [60, -5, 70, 40]        # 60 rows, none, the last 40 rows, nothing left
+    rng = synth.rng_for(915, 0)
+    W = np.concatenate([synth.weights(12, rows, cols, rng) for _ in range(n_expert)])
+    X = synth.activations((total, cols), rng)
+    Y = torch.full((total, rows), float("nan"), dtype=torch.float32, device="cuda")
+    print("[moe] grouped product, clamped device counts", flush=True)
+    gq.gq_matmul_experts_dev(12, to_dev(W), n_expert, rows, cols, to_dev(X),
+                             to_dev(np.array(counts, np.int64)), Y=Y)
+    got = to_host(Y)
+    eb = rows * gq.gq_row_bytes(12, cols)
+    for e, lo, hi in ((0, 0, 60), (2, 60, 100)):
+        ref, S = oracle.matmul(12, W[e * eb:(e + 1) * eb], rows, cols, X[lo:hi])
+        assert_within_tolerance(got[lo:hi], ref, S, f"clamped expert {e}")
+
+
+def test_moe_prefill_chain_in_one_graph(gq, oracle):
+    """Bucket, gather, the grouped product with device counts and the
+    scatter captured in one HIP graph and replayed with new ids and data:
+    every replay within the chain's bound against the f64 expert matvecs."""
+    import torch
+    n_tok, k, n_expert, rows, cols = 64, 2, 8, 256, 512
+    n = n_tok * k
+    rng = synth.rng_for(916, 0)
+    W = np.concatenate([synth.weights(12, rows, cols, rng) for _ in range(n_expert)])
+    Wd = to_dev(W)
+    ids = torch.zeros(n, dtype=torch.int32, device="cuda")
+    X = torch.zeros((n_tok, cols), dtype=torch.float32, device="cuda")
+    w = torch.zeros(n, dtype=torch.float32, device="cuda")
+    out = torch.zeros((n_tok, rows), dtype=torch.float32, device="cuda")
+    counts = torch.empty(n_expert, dtype=torch.int64, device="cuda")
+    order = torch.empty(n, dtype=torch.int32, device="cuda")
+    pos = torch.empty(n, dtype=torch.int32, device="cuda")
+    Xb = torch.empty((n, cols), dtype=torch.float32, device="cuda")
+    Yb = torch.empty((n, rows), dtype=torch.float32, device="cuda")
+
+    def step():
+        gq.gq_moe_bucket(ids, n_expert, counts, order, pos)
+        gq.gq_moe_gather(X, k, pos, Xb)
+        gq.gq_matmul_experts_dev(12, Wd, n_expert, rows, cols, Xb, counts, Y=Yb)
+        gq.gq_moe_scatter(Yb, pos, w, k, out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        r2 = synth.rng_for(917, rep)
+        hid = _ids(r2, n, n_expert)
+        hX = synth.activations((n_tok, cols), r2)
+        hw = r2.random(n).astype(np.float32)
+        ho = synth.activations((n_tok, rows), r2)
+        for t, h in ((ids, hid), (X, hX), (w, hw), (out, ho)):
+            t.copy_(torch.from_numpy(h))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[moe] graph replay {rep}", flush=True)
+        got = to_host(out).astype(np.float64)
+        Ye, Se = oracle.experts_matvec(12, W, n_expert, rows, cols, hX, k, hid, nthreads=oracle_threads())
+        ref = ho.astype(np.float64).copy()
+        bound = np.zeros_like(ref)
+        mag = np.abs(ho).astype(np.float64)
+        for a in range(n):
+            ref[a // k] += float(hw[a]) * Ye[a]
+            bound[a // k] += float(hw[a]) * 2e-4 * Se[a]
+            mag[a // k] += float(hw[a]) * np.abs(Ye[a])
+        bound += (2 * k + 2) * 2.0 ** -24 * mag
+        assert (np.abs(got - ref) <= bound).all()
