@@ -747,9 +747,19 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
                                              Yg.data_ptr(), stream_ptr()) == 0
                 scatter()
 
+            def chain_dev():
+                bucket()
+                gather()
+                assert lib.gq_matmul_experts_dev(f, Wd.data_ptr(), n_expert, r, c, Xg.data_ptr(), cnt.data_ptr(),
+                                                 n_tok * k, Yg.data_ptr(), stream_ptr()) == 0
+                scatter()
+
             bucket()
             torch.cuda.synchronize()
             assert cnt.cpu().tolist() == counts
+            gchain = capture(torch, chain_dev)
+            ms_gc = timer.time(gchain.replay, 5, warmup=1)
+            del gchain
             ms_b = timer.time(bucket, 20, warmup=2)
             ms_g = timer.time(gather, 20, warmup=2)
             ms_s = timer.time(scatter, 20, warmup=2)
@@ -761,7 +771,8 @@ def run_extras(torch, gq, lib, synth, timer, stream_ptr, args):
                 gather_GBps=round(gb_g / (ms_g * 1e-3), 1), scatter_us=round(ms_s * 1e3, 2),
                 scatter_GBps=round(gb_s / (ms_s * 1e-3), 1),
                 chain_us=round(ms_c * 1e3, 1),
-                chain="bucket + gather + counts to the host + gq_matmul_experts + scatter")
+                chain="bucket + gather + counts to the host + gq_matmul_experts + scatter",
+                chain_device_counts_graph_us=round(ms_gc * 1e3, 1))
             del Xg, Yg, Xt, outd
         del Wd
     log(f"moe: { {k: v for k, v in out.items() if k.startswith('moe')} }")
